@@ -1,0 +1,260 @@
+/*
+ * oracle.cpp - float64 reference for the NVFP4 MoE decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg, never by the GPU library. Every step is its
+ * plain definition evaluated in double, in the order the definition states.
+ * See oracle.h for the layouts and for what each function follows.
+ */
+#include "oracle.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <limits>
+#include <vector>
+
+/* ---- NVFP4 element and scale decoding ------------------------------------- */
+
+/* E2M1 (OCP MX FP4): bit 3 sign, bits 2..1 exponent with bias 1, bit 0
+ * mantissa. Exponent field 0 is subnormal: 0.5 * m. Otherwise
+ * (1 + m/2) * 2^(e-1). The values are 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+ * negatives (code 8 is -0). */
+double oracle_e2m1(uint32_t code) {
+  code &= 15u;
+  const int sign = (code >> 3) & 1;
+  const int e = (code >> 1) & 3;
+  const int m = code & 1;
+  double mag;
+  if (e == 0)
+    mag = 0.5 * m;
+  else
+    mag = (1.0 + 0.5 * m) * std::ldexp(1.0, e - 1);
+  return sign ? -mag : mag;
+}
+
+/* E4M3 (OCP 8-bit floating point, the "FN" variant used for NVFP4 block
+ * scales): bit 7 sign, bits 6..3 exponent with bias 7, bits 2..0 mantissa.
+ * Exponent 15 with mantissa 7 is NaN (no infinities). Exponent 0 is
+ * subnormal: (m/8) * 2^-6. Otherwise (1 + m/8) * 2^(e-7). */
+double oracle_e4m3(uint32_t byte) {
+  byte &= 255u;
+  const int sign = (byte >> 7) & 1;
+  const int e = (byte >> 3) & 15;
+  const int m = byte & 7;
+  double mag;
+  if (e == 15 && m == 7)
+    mag = std::numeric_limits<double>::quiet_NaN();
+  else if (e == 0)
+    mag = (m / 8.0) * std::ldexp(1.0, -6);
+  else
+    mag = (1.0 + m / 8.0) * std::ldexp(1.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* BF16 is the upper half of an IEEE binary32. */
+double oracle_bf16(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Element (n, k) of matrix g in the canonical layout. */
+static inline uint32_t code_at(const uint8_t* codes, int64_t N, int64_t K, int64_t gi, int64_t n,
+                               int64_t k) {
+  const uint8_t b = codes[(gi * N + n) * (K / 2) + k / 2];
+  return (k & 1) ? (b >> 4) : (b & 15u);
+}
+
+static inline uint32_t scale_at(const uint8_t* scales, int64_t N, int64_t K, int64_t gi,
+                                int64_t n, int64_t k) {
+  return scales[(gi * N + n) * (K / 16) + k / 16];
+}
+
+/* W[n][k] = e2m1(code) * e4m3(scale of the 16-block holding k) * g. */
+void oracle_dequant(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t G,
+                    int64_t N, int64_t K, double* out) {
+  for (int64_t gi = 0; gi < G; ++gi)
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t k = 0; k < K; ++k)
+        out[(gi * N + n) * K + k] = oracle_e2m1(code_at(codes, N, K, gi, n, k)) *
+                                    oracle_e4m3(scale_at(scales, N, K, gi, n, k)) *
+                                    (double)g[gi];
+}
+
+void oracle_dequant_f32(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t G,
+                        int64_t N, int64_t K, float* out) {
+  for (int64_t gi = 0; gi < G; ++gi)
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t k = 0; k < K; ++k) {
+        const float vs = (float)(oracle_e2m1(code_at(codes, N, K, gi, n, k)) *
+                                 oracle_e4m3(scale_at(scales, N, K, gi, n, k)));
+        out[(gi * N + n) * K + k] = vs * g[gi];
+      }
+}
+
+/* ---- skinny product --------------------------------------------------------- */
+
+/* y[m][n] = sum over k ascending of x[m][k] * W[n][k], in double. */
+void oracle_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes,
+                 const uint8_t* scales, float g, int64_t N, double* y) {
+  std::vector<double> W((size_t)(N * K));
+  oracle_dequant(codes, scales, &g, 1, N, K, W.data());
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) acc += oracle_bf16(x[m * K + k]) * W[(size_t)(n * K + k)];
+      y[m * N + n] = acc;
+    }
+}
+
+/* ---- routing ----------------------------------------------------------------- */
+
+/* Does expert a come before expert b? Larger l' first, NaN after everything,
+ * equal values (including +0 / -0, and two NaNs) by lower index. */
+static bool route_before(const std::vector<float>& lp, int a, int b) {
+  const float la = lp[(size_t)a], lb = lp[(size_t)b];
+  const bool na = std::isnan(la), nb = std::isnan(lb);
+  if (na != nb) return nb;
+  if (!na && la != lb) return la > lb;
+  return a < b;
+}
+
+int oracle_route_topk(const float* logits, const float* bias, int64_t M, int64_t E, int64_t k,
+                      int32_t* ids, double* w) {
+  if (k < 1 || k > E) return -1;
+  std::vector<float> lp((size_t)E);
+  std::vector<int> order((size_t)E);
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t e = 0; e < E; ++e) {
+      const float l = logits[m * E + e];
+      lp[(size_t)e] = bias ? (float)(l + bias[e]) : l; /* one FP32 add */
+    }
+    for (int64_t e = 0; e < E; ++e) order[(size_t)e] = (int)e;
+    std::sort(order.begin(), order.end(), [&](int a, int b) { return route_before(lp, a, b); });
+    for (int64_t j = 0; j < k; ++j) ids[m * k + j] = order[(size_t)j];
+    /* softmax restricted to the selected experts, renormalised to sum 1 */
+    const double top = (double)lp[(size_t)order[0]];
+    double z = 0.0;
+    for (int64_t j = 0; j < k; ++j) z += std::exp((double)lp[(size_t)order[(size_t)j]] - top);
+    for (int64_t j = 0; j < k; ++j)
+      w[m * k + j] = std::exp((double)lp[(size_t)order[(size_t)j]] - top) / z;
+  }
+  return 0;
+}
+
+void oracle_group_by_expert(const int32_t* ids, int64_t M, int64_t E, int64_t k, int32_t* counts,
+                            int32_t* offsets, int32_t* pairs, int32_t* active,
+                            int32_t* n_active) {
+  const int64_t P = M * k;
+  for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t p = 0; p < P; ++p) counts[ids[p]] += 1;
+  offsets[0] = 0;
+  for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int64_t pos = 0;
+  for (int64_t e = 0; e < E; ++e)
+    for (int64_t p = 0; p < P; ++p)
+      if (ids[p] == e) pairs[pos++] = (int32_t)p;
+  int32_t na = 0;
+  for (int64_t e = 0; e < E; ++e)
+    if (counts[e] > 0) active[na++] = (int32_t)e;
+  for (int64_t s = na; s < E; ++s) active[s] = -1;
+  *n_active = na;
+}
+
+/* ---- expert feed-forward -------------------------------------------------------- */
+
+static double silu(double a) { return a / (1.0 + std::exp(-a)); }
+
+/* u = W_gu x (2I outputs); h[i] = silu(u[i]) * u[I + i]; y = W_dn h. Gate is
+ * rows 0..I-1 of the fused gate_up matrix, up is rows I..2I-1. */
+static void ffn_dequantized(const double* x, int64_t H, int64_t I, const double* Wgu,
+                            const double* Wdn, double* y) {
+  std::vector<double> u((size_t)(2 * I)), h((size_t)I);
+  for (int64_t n = 0; n < 2 * I; ++n) {
+    double acc = 0.0;
+    for (int64_t kk = 0; kk < H; ++kk) acc += x[kk] * Wgu[(size_t)(n * H + kk)];
+    u[(size_t)n] = acc;
+  }
+  for (int64_t i = 0; i < I; ++i) h[(size_t)i] = silu(u[(size_t)i]) * u[(size_t)(I + i)];
+  for (int64_t n = 0; n < H; ++n) {
+    double acc = 0.0;
+    for (int64_t i = 0; i < I; ++i) acc += h[(size_t)i] * Wdn[(size_t)(n * I + i)];
+    y[n] = acc;
+  }
+}
+
+void oracle_expert_ffn(const uint16_t* x, int64_t H, int64_t I, const uint8_t* gu_codes,
+                       const uint8_t* gu_scales, float gu_g, const uint8_t* dn_codes,
+                       const uint8_t* dn_scales, float dn_g, double* y) {
+  std::vector<double> Wgu((size_t)(2 * I * H)), Wdn((size_t)(H * I)), xd((size_t)H);
+  oracle_dequant(gu_codes, gu_scales, &gu_g, 1, 2 * I, H, Wgu.data());
+  oracle_dequant(dn_codes, dn_scales, &dn_g, 1, H, I, Wdn.data());
+  for (int64_t kk = 0; kk < H; ++kk) xd[(size_t)kk] = oracle_bf16(x[kk]);
+  ffn_dequantized(xd.data(), H, I, Wgu.data(), Wdn.data(), y);
+}
+
+/* ---- MoE block ------------------------------------------------------------------- */
+
+void oracle_moe_block(const uint16_t* x, int64_t M, int64_t H, int64_t I, int64_t E, int64_t k,
+                      const int32_t* ids, const double* w, const uint8_t* gu_codes,
+                      const uint8_t* gu_scales, const float* gu_g, const uint8_t* dn_codes,
+                      const uint8_t* dn_scales, const float* dn_g, const uint8_t* sgu_codes,
+                      const uint8_t* sgu_scales, const float* sgu_g, const uint8_t* sdn_codes,
+                      const uint8_t* sdn_scales, const float* sdn_g, const uint16_t* residual,
+                      double* out) {
+  const int64_t P = M * k;
+  std::vector<double> xd((size_t)(M * H));
+  for (int64_t i = 0; i < M * H; ++i) xd[(size_t)i] = oracle_bf16(x[i]);
+  /* y_p for every (row, slot) pair p = m*k + j, through expert ids[p]. Each
+   * expert is dequantized once and applied to all of its pairs. */
+  std::vector<double> Y((size_t)(P * H));
+  std::vector<double> Wgu((size_t)(2 * I * H)), Wdn((size_t)(H * I));
+  for (int64_t e = 0; e < E; ++e) {
+    bool used = false;
+    for (int64_t p = 0; p < P && !used; ++p) used = (ids[p] == e);
+    if (!used) continue;
+    oracle_dequant(gu_codes + e * (2 * I * H / 2), gu_scales + e * (2 * I * H / 16), gu_g + e, 1,
+                   2 * I, H, Wgu.data());
+    oracle_dequant(dn_codes + e * (H * I / 2), dn_scales + e * (H * I / 16), dn_g + e, 1, H, I,
+                   Wdn.data());
+    for (int64_t p = 0; p < P; ++p)
+      if (ids[p] == e)
+        ffn_dequantized(&xd[(size_t)((p / k) * H)], H, I, Wgu.data(), Wdn.data(),
+                        &Y[(size_t)(p * H)]);
+  }
+  std::vector<double> S;
+  if (sgu_codes) {
+    S.resize((size_t)(M * H));
+    oracle_dequant(sgu_codes, sgu_scales, sgu_g, 1, 2 * I, H, Wgu.data());
+    oracle_dequant(sdn_codes, sdn_scales, sdn_g, 1, H, I, Wdn.data());
+    for (int64_t m = 0; m < M; ++m)
+      ffn_dequantized(&xd[(size_t)(m * H)], H, I, Wgu.data(), Wdn.data(), &S[(size_t)(m * H)]);
+  }
+  /* combine: routing-weighted sum over the k slots in slot order, then the
+   * shared expert with weight 1, then the residual */
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < H; ++n) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < k; ++j)
+        acc += w[m * k + j] * Y[(size_t)((m * k + j) * H + n)];
+      if (sgu_codes) acc += S[(size_t)(m * H + n)];
+      if (residual) acc += oracle_bf16(residual[m * H + n]);
+      out[m * H + n] = acc;
+    }
+}
+
+int oracle_moe_decode(const uint16_t* x, const float* logits, const float* bias, int64_t M,
+                      int64_t H, int64_t I, int64_t E, int64_t k, const uint8_t* gu_codes,
+                      const uint8_t* gu_scales, const float* gu_g, const uint8_t* dn_codes,
+                      const uint8_t* dn_scales, const float* dn_g, const uint8_t* sgu_codes,
+                      const uint8_t* sgu_scales, const float* sgu_g, const uint8_t* sdn_codes,
+                      const uint8_t* sdn_scales, const float* sdn_g, const uint16_t* residual,
+                      int32_t* ids, double* w, double* out) {
+  if (oracle_route_topk(logits, bias, M, E, k, ids, w) != 0) return -1;
+  oracle_moe_block(x, M, H, I, E, k, ids, w, gu_codes, gu_scales, gu_g, dn_codes, dn_scales,
+                   dn_g, sgu_codes, sgu_scales, sgu_g, sdn_codes, sdn_scales, sdn_g, residual,
+                   out);
+  return 0;
+}

@@ -1,0 +1,424 @@
+"""Pins of the float64 oracle against what the formats and mathematics fix.
+
+Each test pins the oracle to something other than itself: published value
+tables (tests/golden), torch's independent float8_e4m3fn decoder, exact
+rational arithmetic, closed forms of constructed special cases, high-precision
+decimal brute force, and invariants. CPU only.
+"""
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.workloads import NVFP4, MoELayer, moe_layer
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            a, b = line.split()
+            rows.append((int(a, 0), float(b)))
+    return rows
+
+
+# ---- independent decoders used by the pins ------------------------------------
+
+E2M1_TABLE = {c: v for c, v in _golden("e2m1_values.txt")}
+
+
+def torch_e4m3(codes: np.ndarray) -> np.ndarray:
+    """torch's own float8_e4m3fn decode: a library routine independent of the oracle."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def unpack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """[.., K/2] bytes -> [.., K] codes, element 2b = low nibble of byte b."""
+    lo = codes & 15
+    hi = codes >> 4
+    return np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
+
+
+def table_e2m1(c: np.ndarray) -> np.ndarray:
+    lut = np.array([E2M1_TABLE[i] for i in range(16)], dtype=np.float64)
+    lut[8] = -0.0
+    return lut[c]
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+FINITE_E4M3 = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+# ---- format decode ---------------------------------------------------------------
+
+def test_e2m1_all_codes_match_published_table():
+    for c in range(16):
+        v = oracle.e2m1(c)
+        assert v == E2M1_TABLE[c], c
+    assert math.copysign(1.0, oracle.e2m1(8)) == -1.0  # code 8 is -0
+    assert math.copysign(1.0, oracle.e2m1(0)) == 1.0
+
+
+def test_e4m3_all_codes_match_torch_and_anchors():
+    ref = torch_e4m3(np.arange(256, dtype=np.uint8))
+    for b in range(256):
+        v = oracle.e4m3(b)
+        if np.isnan(ref[b]):
+            assert math.isnan(v), hex(b)
+        else:
+            assert v == ref[b] and math.copysign(1, v) == math.copysign(1, ref[b]), hex(b)
+    for b, val in _golden("e4m3_anchors.txt"):
+        v = oracle.e4m3(b)
+        if math.isnan(val):
+            assert math.isnan(v)
+        else:
+            assert v == val and math.copysign(1, v) == math.copysign(1, val), hex(b)
+    finite = [b for b in range(256) if not math.isnan(oracle.e4m3(b))]
+    assert len(finite) == 254
+    # strictly increasing over the non-negative codes, symmetric in the sign bit
+    pos = [oracle.e4m3(b) for b in range(0x7F)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))
+    assert all(oracle.e4m3(b | 0x80) == -oracle.e4m3(b) for b in range(1, 0x7F))
+
+
+def test_code_times_scale_is_exact_in_fp32_and_bf16():
+    """Every E2M1 x finite-E4M3 product has at most 6 significant bits, so it is
+    exact in FP32 and in BF16: decoding to either loses nothing."""
+    v = table_e2m1(np.arange(16))
+    s = torch_e4m3(FINITE_E4M3)
+    prod = np.outer(v, s)
+    assert (prod.astype(np.float32).astype(np.float64) == prod).all()
+    bf = torch.from_numpy(prod).to(torch.bfloat16).to(torch.float64).numpy()
+    assert (bf == prod).all()
+    for i in range(16):
+        for j, b in enumerate(FINITE_E4M3):
+            assert oracle.e2m1(i) * oracle.e4m3(int(b)) == prod[i, j]
+
+
+def test_bf16_widening_matches_torch():
+    bits = np.arange(0, 65536, 7, dtype=np.uint32).astype(np.uint16)
+    ref = bf16_to_f64(bits)
+    got = np.array([oracle.bf16(int(b)) for b in bits])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+@pytest.mark.parametrize("g", [1.0, 0.37, 2.0 ** -9])
+def test_dequant_matches_independent_decode(g):
+    """Dequant (float64 and FP32) against nibble unpacking + published E2M1 table
+    + torch's E4M3 decoder; every finite scale code and every element code
+    appears."""
+    G, N, K = 3, 16, 128
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    scales = rng.choice(FINITE_E4M3, (G, N, K // 16)).astype(np.uint8)
+    scales.reshape(-1)[: len(FINITE_E4M3)] = FINITE_E4M3
+    gv = np.array([g, g * 2, g / 4], dtype=np.float32)
+    v = table_e2m1(unpack_nibbles(codes))
+    s = np.repeat(torch_e4m3(scales), 16, axis=-1)
+    ref64 = v * s * gv.astype(np.float64)[:, None, None]
+    assert (oracle.dequant(codes, scales, gv) == ref64).all()
+    ref32 = ((v * s).astype(np.float32) * gv[:, None, None]).astype(np.float32)
+    got32 = oracle.dequant_f32(codes, scales, gv)
+    assert (got32.view(np.uint32) == ref32.view(np.uint32)).all()
+
+
+# ---- skinny product: exact rational brute force -------------------------------------
+
+def _bf16_bits_in_range(rng, shape):
+    """BF16 values with |x| in [2^-8, 2^8) or 0: x * 2^15 is an integer < 2^24."""
+    e = rng.integers(-8, 8, shape)
+    m = rng.integers(0, 128, shape)
+    sign = rng.integers(0, 2, shape)
+    bits = (sign << 15) | ((e + 127) << 7) | m
+    bits = np.where(rng.random(shape) < 0.1, 0, bits)
+    return bits.astype(np.uint16)
+
+
+@pytest.mark.parametrize("M,K,N,gexp", [(1, 16, 1, 0), (2, 32, 5, -9), (3, 64, 8, 3),
+                                        (3, 64, 7, -8)])
+def test_gemm_equals_exact_rational_sum(M, K, N, gexp):
+    """Inside this range every product and partial sum is a dyadic rational
+    that float64 holds exactly, so the oracle must equal the exact sum bit for
+    bit (codes from all 16, scales from all 254 finite codes incl. subnormal
+    and negative)."""
+    rng = np.random.default_rng(M * 1000 + K + N)
+    x = _bf16_bits_in_range(rng, (M, K))
+    codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = rng.choice(FINITE_E4M3, (N, K // 16)).astype(np.uint8)
+    g = 2.0 ** gexp
+    xf = [[Fraction(float(v)) for v in row] for row in bf16_to_f64(x)]
+    cu = unpack_nibbles(codes)
+    sv = torch_e4m3(scales)
+    got = oracle.gemm(x, codes, scales, g)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(xf[m][k] * Fraction(E2M1_TABLE[int(cu[n, k])]) *
+                        Fraction(float(sv[n, k // 16])) for k in range(K)) * Fraction(g)
+            assert got[m, n] == float(exact) and Fraction(got[m, n]) == exact, (m, n)
+
+
+def test_gemm_special_cases():
+    rng = np.random.default_rng(11)
+    M, K, N = 2, 64, 4
+    x = synth.normal_bf16(synth.key(1), (M, K))
+    xd = bf16_to_f64(x)
+    # one non-zero weight: y = x_k * w
+    codes = np.zeros((N, K // 2), np.uint8)
+    scales = np.full((N, K // 16), 0x38, np.uint8)
+    codes[1, 37 // 2] = 5 << 4          # element 37 (odd -> high nibble) = 3.0
+    scales[1, 37 // 16] = 0x2B          # 2^-2 * 1.375
+    y = oracle.gemm(x, codes, scales, 0.5)
+    assert (y[:, [0, 2, 3]] == 0).all()
+    assert (y[:, 1] == xd[:, 37] * 3.0 * 0.34375 * 0.5).all()
+    # all codes c, all scales 1.0: y = e2m1(c) * g * sum(x)
+    for c in range(16):
+        codes = np.full((N, K // 2), c | (c << 4), np.uint8)
+        scales = np.full((N, K // 16), 0x38, np.uint8)
+        y = oracle.gemm(x, codes, scales, 0.25)
+        ref = E2M1_TABLE[c] * 0.25 * np.array([math.fsum(r) for r in xd])
+        assert np.allclose(y, ref[:, None], rtol=1e-15, atol=1e-15)
+    # doubling g doubles y exactly
+    codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = rng.choice(FINITE_E4M3, (N, K // 16)).astype(np.uint8)
+    assert (oracle.gemm(x, codes, scales, 0.75) * 2 == oracle.gemm(x, codes, scales, 1.5)).all()
+
+
+# ---- routing -------------------------------------------------------------------------
+
+def _brute_route(logits, k, bias=None):
+    M, E = logits.shape
+    ids, ws = [], []
+    for m in range(M):
+        lp = logits[m] if bias is None else (logits[m] + bias).astype(np.float32)
+        key = lambda e: (1 if math.isnan(lp[e]) else 0, 0.0 if math.isnan(lp[e]) else -float(lp[e]), e)
+        order = sorted(range(E), key=key)[:k]
+        ids.append(order)
+    return np.array(ids, dtype=np.int32)
+
+
+@pytest.mark.parametrize("M,E,k,seed,bias", [(1, 256, 8, 0, False), (4, 256, 8, 1, False),
+                                             (16, 256, 8, 2, True), (5, 64, 2, 3, False),
+                                             (3, 256, 1, 4, True), (7, 8, 8, 5, False)])
+def test_route_matches_brute_force_sort(M, E, k, seed, bias):
+    logits = synth.normal_f32(synth.key(seed, 9), (M, E))
+    b = synth.normal_f32(synth.key(seed, 10), (E,), 0.0, 0.5) if bias else None
+    ids, w = oracle.route_topk(logits, k, b)
+    assert (ids == _brute_route(logits, k, b)).all()
+    for m in range(M):
+        assert len(set(ids[m])) == k
+        assert abs(math.fsum(w[m]) - 1.0) <= 1e-12
+        assert all(w[m][j] >= w[m][j + 1] for j in range(k - 1))
+        lp = logits[m] if b is None else (logits[m] + b).astype(np.float32)
+        for j in range(1, k):   # closed-form ratio of softmax weights
+            r = math.exp(float(lp[ids[m][j]]) - float(lp[ids[m][0]]))
+            assert abs(w[m][j] / w[m][0] - r) <= 1e-12 * max(1.0, r)
+
+
+def test_route_ties_zeros_and_nan():
+    E, k = 16, 4
+    rows = np.array([
+        [1.0] * E,                                            # all equal -> 0..3
+        [0.0, -0.0, 0.0, -0.0] + [-1.0] * 12,                 # +/-0 tie -> index order
+        [np.nan, 2.0, np.nan, 2.0, 1.0, -np.inf] + [-3.0] * 10,
+        [-np.inf] * 2 + [5.0, 5.0, 5.0] + [-np.inf] * 11,
+    ], dtype=np.float32)
+    ids, w = oracle.route_topk(rows, k)
+    assert ids[0].tolist() == [0, 1, 2, 3]
+    assert ids[1].tolist() == [0, 1, 2, 3]
+    assert ids[2].tolist() == [1, 3, 4, 6]
+    assert ids[3].tolist() == [2, 3, 4, 0]
+    assert np.allclose(w[0], 0.25, rtol=0, atol=1e-15)
+    assert np.allclose(w[3], [1 / 3, 1 / 3, 1 / 3, 0.0], rtol=0, atol=1e-15)
+    assert (ids == _brute_route(rows, k)).all()
+    # fp32 bias add decides ties that exact arithmetic would not
+    # exactly, 1 + 0.75 ulp < 1 + 1 ulp puts expert 1 first; in FP32 the sum
+    # rounds up to 1 + 1 ulp, the two tie, and the lower index wins
+    lg = np.array([[1.0, 1.0 + 2 ** -23, 0.0, 0.0]], np.float32)
+    b = np.array([3 * 2 ** -25, 0.0, 0.0, 0.0], np.float32)
+    ids, _ = oracle.route_topk(lg, 1, b)
+    assert ids[0, 0] == 0
+    with pytest.raises(ValueError):
+        oracle.route_topk(rows, 17)
+
+
+def test_group_by_expert_matches_brute_counting_sort():
+    for seed, (M, E, k) in enumerate([(4, 256, 8), (16, 256, 8), (256, 256, 8), (3, 5, 2)]):
+        logits = synth.normal_f32(synth.key(seed, 12), (M, E))
+        ids, _ = oracle.route_topk(logits, k)
+        counts, offsets, pairs, active, na = oracle.group_by_expert(ids, E)
+        flat = ids.reshape(-1)
+        assert (counts == np.bincount(flat, minlength=E)).all()
+        assert offsets[0] == 0 and (np.diff(offsets) == counts).all()
+        assert counts.sum() == M * k and offsets[-1] == M * k
+        assert sorted(pairs.tolist()) == list(range(M * k))
+        brute = [p for e in range(E) for p in range(M * k) if flat[p] == e]
+        assert pairs.tolist() == brute
+        for e in range(E):
+            grp = pairs[offsets[e]:offsets[e + 1]]
+            assert (flat[grp] == e).all() and (np.diff(grp) > 0).all()
+        assert na == int((counts > 0).sum())
+        assert active[:na].tolist() == [e for e in range(E) if counts[e] > 0]
+        assert (active[na:] == -1).all()
+
+
+# ---- expert FFN and MoE block ----------------------------------------------------------
+
+def _onehot_layer(H, I, E, x, a, b, c, vcode, scode, g_gu, g_dn):
+    """Expert e's gate row i reads x[a[e][i]], up row i reads x[b[e][i]], down
+    row n reads h[c[e][n]]; the single non-zero weight is e2m1(vcode) *
+    e4m3(scode) * g."""
+    gu_c = np.zeros((E, 2 * I, H // 2), np.uint8)
+    gu_s = np.full((E, 2 * I, H // 16), 0x38, np.uint8)
+    dn_c = np.zeros((E, H, I // 2), np.uint8)
+    dn_s = np.full((E, H, I // 16), 0x38, np.uint8)
+
+    def put(cd, sc, e, row, col):
+        cd[e, row, col // 2] |= (vcode << 4) if col & 1 else vcode
+        sc[e, row, col // 16] = scode
+
+    for e in range(E):
+        for i in range(I):
+            put(gu_c, gu_s, e, i, a[e][i])
+            put(gu_c, gu_s, e, I + i, b[e][i])
+        for n in range(H):
+            put(dn_c, dn_s, e, n, c[e][n])
+    gu = NVFP4(gu_c, gu_s, np.full(E, g_gu, np.float32))
+    dn = NVFP4(dn_c, dn_s, np.full(E, g_dn, np.float32))
+    return gu, dn
+
+
+def test_moe_block_closed_form_onehot():
+    """Closed form of a constructed block: y_e[n] = wv*g_dn * silu(wv*g_gu*x[a]) *
+    (wv*g_gu*x[b]) with a = a_e[c_e[n]], b = b_e[c_e[n]]; out = sum_j w_j y + residual.
+    Pins the gate/up split, nibble and scale-block positions, the combine and
+    the residual."""
+    H, I, E, M, k = 64, 16, 3, 2, 2
+    rng = np.random.default_rng(3)
+    x = synth.normal_bf16(synth.key(3, 1), (M, H))
+    res = synth.normal_bf16(synth.key(3, 2), (M, H))
+    a = [rng.integers(0, H, I) for _ in range(E)]
+    b = [rng.integers(0, H, I) for _ in range(E)]
+    c = [rng.integers(0, I, H) for _ in range(E)]
+    vcode, scode = 13, 0x31  # -3.0, 0.5625
+    wv = -3.0 * 0.5625
+    gu, dn = _onehot_layer(H, I, E, x, a, b, c, vcode, scode, 0.5, 0.25)
+    ids = np.array([[2, 0], [1, 2]], np.int32)
+    w = np.array([[0.7, 0.3], [0.25, 0.75]])
+    out = oracle.moe_block(x, ids, w, gu, dn, residual=res)
+    xd, rd = bf16_to_f64(x), bf16_to_f64(res)
+    silu = lambda t: t / (1.0 + math.exp(-t))
+    for m in range(M):
+        for n in range(H):
+            terms = []
+            for j in range(k):
+                e = ids[m, j]
+                i = c[e][n]
+                ug = wv * 0.5 * xd[m, a[e][i]]
+                uu = wv * 0.5 * xd[m, b[e][i]]
+                terms.append(w[m, j] * wv * 0.25 * silu(ug) * uu)
+            ref = terms[0] + terms[1] + rd[m, n]
+            assert abs(out[m, n] - ref) <= 1e-14 * max(1.0, abs(ref)), (m, n)
+
+
+def _decimal_block(layer: MoELayer, ids, w, prec=40):
+    """Brute force of the block in 40-digit decimal arithmetic on the dequantized
+    weights from the independent decoders."""
+    getcontext().prec = prec
+    M, H, I = layer.M, layer.H, layer.I
+    xd = bf16_to_f64(layer.x)
+
+    def deq(t: NVFP4, e):
+        v = table_e2m1(unpack_nibbles(t.codes[e]))
+        s = np.repeat(torch_e4m3(t.scales[e]), 16, axis=-1)
+        return v * s * float(t.g[e])  # exact in double (dyadic, few bits)
+
+    def ffn(xrow, Wgu, Wdn):
+        u = [sum(Decimal(float(xrow[kk])) * Decimal(float(Wgu[n, kk])) for kk in range(H))
+             for n in range(2 * I)]
+        h = [u[i] / (1 + (-u[i]).exp()) * u[I + i] for i in range(I)]
+        return [sum(h[i] * Decimal(float(Wdn[n, i])) for i in range(I)) for n in range(H)]
+
+    out = [[Decimal(0)] * H for _ in range(M)]
+    for m in range(M):
+        for j in range(ids.shape[1]):
+            e = int(ids[m, j])
+            y = ffn(xd[m], deq(layer.gate_up, e), deq(layer.down, e))
+            for n in range(H):
+                out[m][n] += Decimal(float(w[m, j])) * y[n]
+        if layer.shared_gate_up is not None:
+            y = ffn(xd[m], deq(layer.shared_gate_up, 0), deq(layer.shared_down, 0))
+            for n in range(H):
+                out[m][n] += y[n]
+    return np.array([[float(v) for v in row] for row in out])
+
+
+def test_moe_block_decimal_brute_force():
+    lay = moe_layer(seed=7, wl=90, M=2, E_=6, H_=32, I_=16, k=2, shared=True)
+    ids, w = oracle.route_topk(lay.logits, lay.k)
+    out = oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down, lay.shared_gate_up,
+                           lay.shared_down)
+    ref = _decimal_block(lay, ids, w)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-13)
+    # and through the whole step from logits
+    ids2, w2, out2 = oracle.moe_decode(lay.x, lay.logits, lay.k, lay.gate_up, lay.down,
+                                       shared_gate_up=lay.shared_gate_up,
+                                       shared_down=lay.shared_down)
+    assert (ids2 == ids).all() and (w2 == w).all() and (out2 == out).all()
+
+
+def test_moe_block_invariants():
+    lay = moe_layer(seed=8, wl=91, M=3, E_=8, H_=64, I_=32, k=2)
+    ids, w = oracle.route_topk(lay.logits, lay.k)
+    base = oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down)
+    # rows are independent
+    for m in range(lay.M):
+        one = oracle.moe_block(lay.x[m:m + 1], ids[m:m + 1], w[m:m + 1], lay.gate_up, lay.down)
+        assert (one[0] == base[m]).all()
+    # down is linear: doubling its tensor scale doubles the output exactly,
+    # flipping every down sign bit negates it exactly
+    dn2 = NVFP4(lay.down.codes, lay.down.scales, lay.down.g * 2)
+    assert (oracle.moe_block(lay.x, ids, w, lay.gate_up, dn2) == 2 * base).all()
+    dneg = NVFP4(lay.down.codes ^ np.uint8(0x88), lay.down.scales, lay.down.g)
+    assert (oracle.moe_block(lay.x, ids, w, lay.gate_up, dneg) == -base).all()
+    # k = 1, weight 1 is one expert FFN
+    e = int(ids[0, 0])
+    one = oracle.moe_block(lay.x[:1], np.array([[e]], np.int32), np.ones((1, 1)), lay.gate_up,
+                           lay.down)
+    y = oracle.expert_ffn(lay.x[0], lay.gate_up.select([e]), lay.down.select([e]))
+    assert (one[0] == y).all()
+    # gate rows at zero switch the expert off: silu(0) * up = 0
+    gz = lay.gate_up.codes.copy()
+    gz[:, :lay.I, :] = 0
+    gu0 = NVFP4(gz, lay.gate_up.scales, lay.gate_up.g)
+    assert (oracle.moe_block(lay.x, ids, w, gu0, lay.down) == 0).all()
+    # a zero shared expert adds exactly nothing
+    zgu = NVFP4(np.zeros((1, 2 * lay.I, lay.H // 2), np.uint8),
+                np.full((1, 2 * lay.I, lay.H // 16), 0x38, np.uint8), np.ones(1, np.float32))
+    zdn = NVFP4(np.zeros((1, lay.H, lay.I // 2), np.uint8),
+                np.full((1, lay.H, lay.I // 16), 0x38, np.uint8), np.ones(1, np.float32))
+    assert (oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down, zgu, zdn) == base).all()
+
+
+def test_moe_block_touched_subset_equals_full():
+    lay = moe_layer(seed=9, wl=92, M=4, E_=32, H_=64, I_=32, k=4)
+    ids, w = oracle.route_topk(lay.logits, lay.k)
+    full = oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down)
+    sub = oracle.moe_block_touched(lay, ids, w)
+    assert (full == sub).all()
+    rows = oracle.moe_block_touched(lay, ids, w, rows=[1, 3])
+    assert (rows == full[[1, 3]]).all()
