@@ -1,0 +1,164 @@
+/*
+ * nvfp4moe.h - C ABI of libnvfp4moe.so: the decode-time mixture-of-experts
+ * contraction on 4-bit NVFP4 weights, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation. In decode, most products are skinny: a handful of BF16
+ * activation rows times a large 4-bit weight matrix (Elsa RTX 5090 page,
+ * "Making decode faster", skinny matrix multiplies; there the 4-bit weights
+ * are used with 16-bit activations). A few token rows are routed top-k to
+ * experts stored in NVFP4 (same page, "The card and the model"), pushed
+ * through gate_up -> SiLU*up -> down and combined with the routing weights
+ * (the "finalize" step of the same page's "One environment variable"). An
+ * always-on shared expert is a separate weight-1 term ("What didn't work":
+ * fusing it into the routed MoE gave wrong output). Each step reads every
+ * touched expert weight once, so it is bounded by memory bandwidth (the
+ * decode roofline of the "One config is the weakest card's config" page,
+ * "The numbers").
+ *
+ * NVFP4, canonical form (what callers hold):
+ *   codes  uint8 [G][N][K/2]  E2M1 element codes (OCP MX FP4); element 2b of a
+ *                             row is the low nibble of byte b, 2b+1 the high
+ *   scales uint8 [G][N][K/16] E4M3 scale (OCP FP8 E4M3, no infinities) per 16
+ *                             consecutive elements along K
+ *   g      float [G]          FP32 tensor scale per matrix
+ *   weight W[n][k] = e2m1(code) * e4m3(scale[n][k/16]) * g; a matrix is
+ *   [N][K] (out x in) and is applied as y = x W^T.
+ *
+ * Conventions for every call:
+ *   - Status: 0 = NVFP4MOE_OK, negative = error (codes below). On error
+ *     nothing is launched; nvfp4moe_last_error_detail() says why.
+ *   - All array pointers are DEVICE pointers unless stated otherwise. The
+ *     caller owns all memory. The library never allocates, frees,
+ *     synchronises or copies to the host, so every call is stream-ordered on
+ *     the given hipStream_t (NULL = default stream) and may be captured in a
+ *     HIP graph.
+ *   - Arguments are validated on the host before launch. Faults inside a
+ *     kernel (for example from a bad device pointer) surface at the caller's
+ *     next synchronisation.
+ *   - Shapes are int64_t. Support set: K is 32 * 2^j with K <= 2048; N >= 1;
+ *     1 <= k <= 8; 1 <= E <= 256. Anything else returns
+ *     NVFP4MOE_ERR_UNSUPPORTED; no shape ever falls back to another path.
+ *   - Stateless and thread-safe.
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4MOE_OK 0
+#define NVFP4MOE_ERR_NULL_ARG (-1)
+#define NVFP4MOE_ERR_BAD_SHAPE (-2)
+#define NVFP4MOE_ERR_UNSUPPORTED (-3)
+#define NVFP4MOE_ERR_WORKSPACE (-4)
+#define NVFP4MOE_ERR_HIP (-5)
+
+/* Name of a status code; never NULL. */
+const char* nvfp4moe_strerror(int32_t status);
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* nvfp4moe_last_error_detail(void);
+/* Library version string. */
+const char* nvfp4moe_version(void);
+
+/* ---- weight layout ------------------------------------------------------------
+ *
+ * The library streams weights in its own packed layout: a lossless byte
+ * permutation of the canonical form that puts each wavefront's codes and
+ * scales in 1 KB contiguous runs. The packed layout is opaque: to take a
+ * slice of a matrix, slice the canonical form and pack again (slicing a
+ * repacked 4-bit head silently produced garbage on the Elsa page, "FR-Spec,
+ * and a silent bug").
+ */
+
+/* Bytes of packed storage for G matrices of N x K. Returns < 0 (an error
+ * code) for an unsupported K or a non-positive size. */
+int64_t nvfp4_packed_bytes(int64_t G, int64_t N, int64_t K);
+
+/* Canonical -> packed. codes [G][N][K/2], scales [G][N][K/16], g [G] (all
+ * device memory); packed receives nvfp4_packed_bytes(G, N, K) bytes. Rows
+ * beyond N inside the last tile are zero-filled. */
+int32_t nvfp4_pack(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t G,
+                   int64_t N, int64_t K, void* packed, hipStream_t stream);
+
+/* Decodes a packed tensor back to FP32 with the same device decode routines
+ * the products use: out[G][N][K] = fl32(fl32(e2m1 * e4m3) * g) (apply_g != 0)
+ * or e2m1 * e4m3 (apply_g == 0; exact). path selects the element decoder:
+ * 0 = the BF16 pair decoder of the activation-row products, 1 = the FP32
+ * pair decoder of the FP32-row products. Test hook for bit-exact decode. */
+int32_t nvfp4_dequant_f32(const void* packed, int64_t G, int64_t N, int64_t K, int32_t apply_g,
+                          int32_t path, float* out, hipStream_t stream);
+
+/* ---- dense skinny product ----------------------------------------------------------
+ *
+ * y[M][N] = bf16_rne( sum_k x[m][k] * W[n][k] ), one packed matrix (G = 1),
+ * FP32 accumulation, BF16 activations x [M][K] and output y [M][N] (raw BF16
+ * bits). M >= 1 (rows beyond 8 are taken in batches of 8 over the same
+ * weight registers).
+ */
+int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w_packed,
+                          int64_t N, uint16_t* y, hipStream_t stream);
+
+/* ---- routing -------------------------------------------------------------------------
+ *
+ * Per row m: l'[e] = fl32(logits[m][e] + bias[e]) (bias may be NULL: l' =
+ * logits); experts ordered by l' descending, ties to the lower expert index,
+ * +0 == -0, NaN after -inf; ids[m][0..k) = the first k in that order;
+ * w[m][j] = exp(l'_j - l'_0) / sum_i exp(l'_i - l'_0) over the selected
+ * (FP32, sums to 1). Then the (row, slot) pairs p = m*k + j are grouped by
+ * expert:
+ *   counts[E]      pairs per expert
+ *   offsets[E+1]   exclusive prefix sum of counts
+ *   pairs[M*k]     for experts in ascending order, their p ascending
+ *   active[E]      experts with counts > 0 in ascending order, then -1
+ *   n_active[1]    number of such experts
+ * All outputs are device memory and are never read back, so the call can be
+ * captured. logits [M][E] FP32, bias [E] FP32. */
+int32_t moe_route_topk(const float* logits, const float* bias, int64_t M, int64_t E, int64_t k,
+                       int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* pairs,
+                       int32_t* active, int32_t* n_active, hipStream_t stream);
+
+/* ---- MoE block -------------------------------------------------------------------------- */
+
+typedef struct moe_nvfp4_args {
+  const uint16_t* x;          /* [M][H] BF16 activation rows */
+  const int32_t* ids;         /* [M][k]   from moe_route_topk */
+  const float* w;             /* [M][k]   from moe_route_topk */
+  const int32_t* offsets;     /* [E+1]    from moe_route_topk */
+  const int32_t* pairs;       /* [M*k]    from moe_route_topk */
+  const int32_t* active;      /* [E]      from moe_route_topk */
+  const int32_t* n_active;    /* [1]      from moe_route_topk */
+  const void* w_gate_up;      /* packed G = E, N = 2I, K = H; rows 0..I-1 gate, I..2I-1 up */
+  const void* w_down;         /* packed G = E, N = H, K = I */
+  const void* shared_gate_up; /* packed G = 1, N = 2I, K = H, or NULL (no shared expert) */
+  const void* shared_down;    /* packed G = 1, N = H, K = I, or NULL */
+  const uint16_t* residual;   /* [M][H] BF16 added before rounding, or NULL */
+  uint16_t* out;              /* [M][H] BF16 */
+  void* workspace;            /* device scratch, >= moe_nvfp4_workspace_bytes(...) */
+  int64_t workspace_bytes;
+  int64_t M, E, k, H, I;
+} moe_nvfp4_args;
+
+/* Workspace bytes for moe_nvfp4_decode: FP32 h rows [M*k (+M)][I], FP32
+ * expert outputs [M*k (+M)][H] and per-tile counters. Its contents need no
+ * initialisation and are overwritten by every call. */
+int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, int64_t I,
+                                  int32_t has_shared);
+
+/* out[m] = bf16_rne( sum_j w[m][j] * y_{ids[m][j]}(x[m]) + y_shared(x[m]) + residual[m] ),
+ * y_e(x) = W_dn,e ( silu(u[0:I]) * u[I:2I] ),  u = W_gu,e x,  silu(a) = a / (1 + e^-a),
+ * with FP32 accumulation and FP32 h. The slot sum runs in j order, then the
+ * shared term, then the residual. Extra support-set conditions: H and I are
+ * each 32 * 2^j <= 2048, and I is a multiple of 16384 / H (gate and up
+ * halves start on a tile boundary). Returns NVFP4MOE_ERR_WORKSPACE if the
+ * workspace is too small. */
+int32_t moe_nvfp4_decode(const moe_nvfp4_args* args, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,246 @@
+"""nvfp4_moe_skinny_amd: Python binding of libnvfp4moe.so.
+
+Argument marshalling only. Every computation runs in the library's HIP
+kernels on the GPU; PyTorch supplies device memory and the current stream.
+There is no CPU fallback: if the library is missing, importing the binding
+raises.
+
+The functions carry the C names (see include/nvfp4moe.h for the contract)
+and take torch tensors on the GPU in the documented dtypes and layouts.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4moe.so")
+
+NVFP4MOE_OK = 0
+NVFP4MOE_ERR_NULL_ARG = -1
+NVFP4MOE_ERR_BAD_SHAPE = -2
+NVFP4MOE_ERR_UNSUPPORTED = -3
+NVFP4MOE_ERR_WORKSPACE = -4
+NVFP4MOE_ERR_HIP = -5
+
+_vp, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+
+
+class NVFP4MoEError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {strerror(status)} ({detail})")
+        self.status = status
+
+
+class MoeArgs(ctypes.Structure):
+    """Mirror of struct moe_nvfp4_args."""
+    _fields_ = [
+        ("x", _vp), ("ids", _vp), ("w", _vp), ("offsets", _vp), ("pairs", _vp),
+        ("active", _vp), ("n_active", _vp), ("w_gate_up", _vp), ("w_down", _vp),
+        ("shared_gate_up", _vp), ("shared_down", _vp), ("residual", _vp), ("out", _vp),
+        ("workspace", _vp), ("workspace_bytes", _i64),
+        ("M", _i64), ("E", _i64), ("k", _i64), ("H", _i64), ("I", _i64),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python nvfp4_moe_skinny_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    L.nvfp4moe_strerror.restype = ctypes.c_char_p
+    L.nvfp4moe_strerror.argtypes = [_i32]
+    L.nvfp4moe_last_error_detail.restype = ctypes.c_char_p
+    L.nvfp4moe_last_error_detail.argtypes = []
+    L.nvfp4moe_version.restype = ctypes.c_char_p
+    L.nvfp4moe_version.argtypes = []
+    L.nvfp4_packed_bytes.restype = _i64
+    L.nvfp4_packed_bytes.argtypes = [_i64, _i64, _i64]
+    L.nvfp4_pack.restype = _i32
+    L.nvfp4_pack.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]
+    L.nvfp4_dequant_f32.restype = _i32
+    L.nvfp4_dequant_f32.argtypes = [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp]
+    L.nvfp4_skinny_gemm.restype = _i32
+    L.nvfp4_skinny_gemm.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _vp]
+    L.moe_route_topk.restype = _i32
+    L.moe_route_topk.argtypes = [_vp, _vp, _i64, _i64, _i64] + [_vp] * 8
+    L.moe_nvfp4_workspace_bytes.restype = _i64
+    L.moe_nvfp4_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32]
+    L.moe_nvfp4_decode.restype = _i32
+    L.moe_nvfp4_decode.argtypes = [ctypes.POINTER(MoeArgs), _vp]
+    return L
+
+
+lib = _load()
+
+EXPORTS = ["nvfp4moe_strerror", "nvfp4moe_last_error_detail", "nvfp4moe_version",
+           "nvfp4_packed_bytes", "nvfp4_pack", "nvfp4_dequant_f32", "nvfp4_skinny_gemm",
+           "moe_route_topk", "moe_nvfp4_workspace_bytes", "moe_nvfp4_decode"]
+
+
+def strerror(status: int) -> str:
+    return lib.nvfp4moe_strerror(status).decode()
+
+
+def last_error_detail() -> str:
+    return lib.nvfp4moe_last_error_detail().decode()
+
+
+def version() -> str:
+    return lib.nvfp4moe_version().decode()
+
+
+def _check(status: int, where: str):
+    if status != NVFP4MOE_OK:
+        raise NVFP4MoEError(status, where, last_error_detail())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+# ---- weights ------------------------------------------------------------------------
+
+@dataclass
+class PackedNVFP4:
+    """G packed matrices of N x K in the library layout (device bytes)."""
+    data: torch.Tensor  # uint8, nvfp4_packed_bytes(G, N, K)
+    G: int
+    N: int
+    K: int
+
+
+def nvfp4_packed_bytes(G: int, N: int, K: int) -> int:
+    n = lib.nvfp4_packed_bytes(G, N, K)
+    if n < 0:
+        raise NVFP4MoEError(int(n), "nvfp4_packed_bytes", last_error_detail())
+    return int(n)
+
+
+def nvfp4_pack(codes: torch.Tensor, scales: torch.Tensor, g: torch.Tensor, stream=None,
+               out: Optional[torch.Tensor] = None) -> PackedNVFP4:
+    """codes uint8 [G][N][K/2], scales uint8 [G][N][K/16], g float32 [G] (GPU)."""
+    G, N, kh = codes.shape
+    K = kh * 2
+    if tuple(scales.shape) != (G, N, K // 16) or tuple(g.shape) != (G,):
+        raise ValueError("scales must be [G][N][K/16] and g [G]")
+    nbytes = nvfp4_packed_bytes(G, N, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    _check(lib.nvfp4_pack(_ptr(codes), _ptr(scales), _ptr(g), G, N, K, _ptr(out),
+                          _stream(stream)), "nvfp4_pack")
+    return PackedNVFP4(out, G, N, K)
+
+
+def nvfp4_dequant_f32(w: PackedNVFP4, apply_g: bool = True, path: int = 0,
+                      stream=None) -> torch.Tensor:
+    out = torch.empty((w.G, w.N, w.K), dtype=torch.float32, device=w.data.device)
+    _check(lib.nvfp4_dequant_f32(_ptr(w.data), w.G, w.N, w.K, int(apply_g), int(path),
+                                 _ptr(out), _stream(stream)), "nvfp4_dequant_f32")
+    return out
+
+
+def nvfp4_skinny_gemm(x: torch.Tensor, w: PackedNVFP4, stream=None,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x bfloat16 [M][K] -> bfloat16 [M][N] = x W^T."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    M, K = x.shape
+    if K != w.K or w.G != 1:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device)
+    _check(lib.nvfp4_skinny_gemm(_ptr(x), M, K, _ptr(w.data), w.N, _ptr(out), _stream(stream)),
+           "nvfp4_skinny_gemm")
+    return out
+
+
+# ---- routing -------------------------------------------------------------------------
+
+@dataclass
+class Routing:
+    ids: torch.Tensor       # int32 [M][k]
+    w: torch.Tensor         # float32 [M][k]
+    counts: torch.Tensor    # int32 [E]
+    offsets: torch.Tensor   # int32 [E+1]
+    pairs: torch.Tensor     # int32 [M*k]
+    active: torch.Tensor    # int32 [E]
+    n_active: torch.Tensor  # int32 [1]
+
+
+def routing_buffers(M: int, E: int, k: int, device) -> Routing:
+    i32 = dict(dtype=torch.int32, device=device)
+    return Routing(torch.empty((M, k), **i32), torch.empty((M, k), dtype=torch.float32,
+                                                           device=device),
+                   torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(M * k, **i32),
+                   torch.empty(E, **i32), torch.empty(1, **i32))
+
+
+def moe_route_topk(logits: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None,
+                   stream=None, out: Optional[Routing] = None) -> Routing:
+    """logits float32 [M][E] (+ bias float32 [E])."""
+    if logits.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
+        raise ValueError("logits and bias must be float32")
+    M, E = logits.shape
+    r = routing_buffers(M, E, k, logits.device) if out is None else out
+    _check(lib.moe_route_topk(_ptr(logits), _ptr(bias), M, E, k, _ptr(r.ids), _ptr(r.w),
+                              _ptr(r.counts), _ptr(r.offsets), _ptr(r.pairs), _ptr(r.active),
+                              _ptr(r.n_active), _stream(stream)), "moe_route_topk")
+    return r
+
+
+# ---- MoE block ---------------------------------------------------------------------------
+
+def moe_nvfp4_workspace_bytes(M: int, E: int, k: int, H: int, I: int, has_shared: bool) -> int:
+    n = lib.moe_nvfp4_workspace_bytes(M, E, k, H, I, int(has_shared))
+    if n < 0:
+        raise NVFP4MoEError(int(n), "moe_nvfp4_workspace_bytes", last_error_detail())
+    return int(n)
+
+
+def moe_nvfp4_decode(x: torch.Tensor, routing: Routing, w_gate_up: PackedNVFP4,
+                     w_down: PackedNVFP4, shared_gate_up: Optional[PackedNVFP4] = None,
+                     shared_down: Optional[PackedNVFP4] = None,
+                     residual: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x bfloat16 [M][H] -> bfloat16 [M][H] (routed experts + shared + residual)."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    M, H = x.shape
+    E, I = w_gate_up.G, w_down.K
+    k = routing.ids.shape[1]
+    if w_gate_up.N != 2 * I or w_gate_up.K != H or w_down.N != H or w_down.G != E:
+        raise ValueError("expert weight shapes do not match x")
+    has_shared = shared_gate_up is not None
+    if workspace is None:
+        workspace = torch.empty(moe_nvfp4_workspace_bytes(M, E, k, H, I, has_shared),
+                                dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    a = MoeArgs()
+    a.x, a.ids, a.w = _ptr(x), _ptr(routing.ids), _ptr(routing.w)
+    a.offsets, a.pairs = _ptr(routing.offsets), _ptr(routing.pairs)
+    a.active, a.n_active = _ptr(routing.active), _ptr(routing.n_active)
+    a.w_gate_up, a.w_down = _ptr(w_gate_up.data), _ptr(w_down.data)
+    a.shared_gate_up = _ptr(shared_gate_up.data) if has_shared else None
+    a.shared_down = _ptr(shared_down.data) if has_shared else None
+    a.residual = _ptr(residual)
+    a.out = _ptr(out)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    a.M, a.E, a.k, a.H, a.I = M, E, k, H, I
+    _check(lib.moe_nvfp4_decode(ctypes.byref(a), _stream(stream)), "moe_nvfp4_decode")
+    return out

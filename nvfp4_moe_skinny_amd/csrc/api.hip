@@ -1,0 +1,285 @@
+// api.hip - the extern "C" entry points of libnvfp4moe.so (see include/nvfp4moe.h).
+//
+// Every call validates on the host, launches on the caller's stream and
+// returns; nothing is allocated, synchronised or read back.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "nvfp4moe.h"
+
+#include "gemm.hpp"
+#include "moe.hpp"
+#include "pack.hpp"
+#include "route.hpp"
+
+using namespace nvfp4moe;
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int32_t ok() {
+  g_detail[0] = '\0';
+  return NVFP4MOE_OK;
+}
+
+int32_t launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(NVFP4MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool valid_k(int64_t K) {
+  if (K < 32 || K > 2048) return false;
+  return ((K / 32) & (K / 32 - 1)) == 0 && K % 32 == 0;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int grid_for(int64_t items, int64_t per_block, int64_t cap) {
+  int64_t g = (items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (int)g;
+}
+
+template <template <int> class Launcher, typename... Args>
+int32_t dispatch_l(int64_t L, Args&&... args) {
+  switch (L) {
+    case 1: return Launcher<1>::run(args...);
+    case 2: return Launcher<2>::run(args...);
+    case 4: return Launcher<4>::run(args...);
+    case 8: return Launcher<8>::run(args...);
+    case 16: return Launcher<16>::run(args...);
+    case 32: return Launcher<32>::run(args...);
+    case 64: return Launcher<64>::run(args...);
+    default: return fail(NVFP4MOE_ERR_UNSUPPORTED, "K/32 = %lld", (long long)L);
+  }
+}
+
+template <int L>
+struct GemmLaunch {
+  static int32_t run(const uint16_t* x, int64_t M, const uint8_t* w, int64_t N, uint16_t* y,
+                     hipStream_t s) {
+    const int64_t tiles = tiles_per_matrix(N, L * 32);
+    hipLaunchKernelGGL(skinny_gemm_kernel<L>, dim3(grid_for(tiles, 4, 1 << 30)), dim3(256), 0, s,
+                       x, M, w, N, y);
+    return launched("nvfp4_skinny_gemm");
+  }
+};
+
+template <int L>
+struct GateUpLaunch {
+  static int32_t run(const MoeParams& p, int blocks, hipStream_t s) {
+    hipLaunchKernelGGL(moe_gate_up_kernel<L>, dim3(blocks), dim3(256), 0, s, p);
+    return launched("moe_nvfp4_decode gate_up");
+  }
+};
+
+template <int L>
+struct DownLaunch {
+  static int32_t run(const MoeParams& p, int blocks, hipStream_t s) {
+    hipLaunchKernelGGL(moe_down_combine_kernel<L>, dim3(blocks), dim3(256), 0, s, p);
+    return launched("moe_nvfp4_decode down");
+  }
+};
+
+struct WsLayout {
+  int64_t h_off, y_off, cnt_off, total;
+};
+
+int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+
+WsLayout ws_layout(int64_t M, int64_t k, int64_t H, int64_t I, bool shared) {
+  const int64_t P = M * k + (shared ? M : 0);
+  WsLayout w;
+  w.h_off = 0;
+  w.y_off = align256(P * I * 4);
+  w.cnt_off = w.y_off + align256(P * H * 4);
+  const int64_t groups = (tiles_per_matrix(H, I) + 3) / 4;
+  w.total = w.cnt_off + align256(groups * 4);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4moe_strerror(int32_t status) {
+  switch (status) {
+    case NVFP4MOE_OK: return "NVFP4MOE_OK";
+    case NVFP4MOE_ERR_NULL_ARG: return "NVFP4MOE_ERR_NULL_ARG";
+    case NVFP4MOE_ERR_BAD_SHAPE: return "NVFP4MOE_ERR_BAD_SHAPE";
+    case NVFP4MOE_ERR_UNSUPPORTED: return "NVFP4MOE_ERR_UNSUPPORTED";
+    case NVFP4MOE_ERR_WORKSPACE: return "NVFP4MOE_ERR_WORKSPACE";
+    case NVFP4MOE_ERR_HIP: return "NVFP4MOE_ERR_HIP";
+    default: return "NVFP4MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* nvfp4moe_last_error_detail(void) { return g_detail; }
+
+const char* nvfp4moe_version(void) { return "nvfp4moe 0.1 gfx950"; }
+
+int64_t nvfp4_packed_bytes(int64_t G, int64_t N, int64_t K) {
+  if (G < 1 || N < 1) return fail(NVFP4MOE_ERR_BAD_SHAPE, "G and N must be >= 1");
+  if (!valid_k(K)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "K = %lld: need 32 * 2^j <= 2048",
+                               (long long)K);
+  ok();
+  return G * matrix_bytes(N, K) + align256(4 * G);
+}
+
+int32_t nvfp4_pack(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t G,
+                   int64_t N, int64_t K, void* packed, hipStream_t stream) {
+  if (!codes || !scales || !g || !packed) return fail(NVFP4MOE_ERR_NULL_ARG, "nvfp4_pack: null");
+  const int64_t bytes = nvfp4_packed_bytes(G, N, K);
+  if (bytes < 0) return (int32_t)bytes;
+  if (!aligned(packed, 16)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "packed must be 16-byte aligned");
+  const int64_t chunks = G * tiles_per_matrix(N, K) * 512;
+  hipLaunchKernelGGL(pack_kernel, dim3(grid_for(chunks, 256, 1 << 16)), dim3(256), 0, stream,
+                     codes, scales, g, G, N, K, (uint8_t*)packed);
+  return launched("nvfp4_pack");
+}
+
+int32_t nvfp4_dequant_f32(const void* packed, int64_t G, int64_t N, int64_t K, int32_t apply_g,
+                          int32_t path, float* out, hipStream_t stream) {
+  if (!packed || !out) return fail(NVFP4MOE_ERR_NULL_ARG, "nvfp4_dequant_f32: null");
+  const int64_t bytes = nvfp4_packed_bytes(G, N, K);
+  if (bytes < 0) return (int32_t)bytes;
+  if (path != 0 && path != 1) return fail(NVFP4MOE_ERR_UNSUPPORTED, "path must be 0 or 1");
+  if (!aligned(packed, 16)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "packed must be 16-byte aligned");
+  const int64_t chunks = G * tiles_per_matrix(N, K) * 512;
+  hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(chunks, 256, 1 << 16)), dim3(256), 0, stream,
+                     (const uint8_t*)packed, G, N, K, (int)apply_g, (int)path, out);
+  return launched("nvfp4_dequant_f32");
+}
+
+int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w_packed,
+                          int64_t N, uint16_t* y, hipStream_t stream) {
+  if (!x || !w_packed || !y) return fail(NVFP4MOE_ERR_NULL_ARG, "nvfp4_skinny_gemm: null");
+  if (M < 1 || N < 1) return fail(NVFP4MOE_ERR_BAD_SHAPE, "M and N must be >= 1");
+  if (!valid_k(K)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "K = %lld: need 32 * 2^j <= 2048",
+                               (long long)K);
+  if (!aligned(x, 16) || !aligned(w_packed, 16))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "x and w_packed must be 16-byte aligned");
+  return dispatch_l<GemmLaunch>(K / 32, x, M, (const uint8_t*)w_packed, N, y, stream);
+}
+
+int32_t moe_route_topk(const float* logits, const float* bias, int64_t M, int64_t E, int64_t k,
+                       int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* pairs,
+                       int32_t* active, int32_t* n_active, hipStream_t stream) {
+  if (!logits || !ids || !w || !counts || !offsets || !pairs || !active || !n_active)
+    return fail(NVFP4MOE_ERR_NULL_ARG, "moe_route_topk: null");
+  if (M < 1 || E < 1 || k < 1) return fail(NVFP4MOE_ERR_BAD_SHAPE, "M, E, k must be >= 1");
+  if (E > kRouteMaxE) return fail(NVFP4MOE_ERR_UNSUPPORTED, "E = %lld > 256", (long long)E);
+  if (k > kRouteMaxK || k > E)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "k = %lld: need k <= min(8, E)", (long long)k);
+  if (M * k > kGroupMaxPairs)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "M * k = %lld > %d", (long long)(M * k),
+                kGroupMaxPairs);
+  if (M <= kRouteSingleBlockRows) {
+    hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(1024), 0, stream, logits, bias, (int)M,
+                       (int)E, (int)k, ids, w, counts, offsets, pairs, active, n_active);
+    return launched("moe_route_topk");
+  }
+  hipLaunchKernelGGL(route_rows_kernel, dim3(grid_for(M, kRouteWaves, 1 << 20)), dim3(1024), 0,
+                     stream, logits, bias, (int)M, (int)E, (int)k, ids, w);
+  const int32_t st = launched("moe_route_topk rows");
+  if (st != NVFP4MOE_OK) return st;
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, ids, (int)M, (int)E, (int)k,
+                     counts, offsets, pairs, active, n_active);
+  return launched("moe_route_topk group");
+}
+
+int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, int64_t I,
+                                  int32_t has_shared) {
+  if (M < 1 || E < 1 || k < 1 || H < 1 || I < 1)
+    return fail(NVFP4MOE_ERR_BAD_SHAPE, "sizes must be >= 1");
+  if (!valid_k(H) || !valid_k(I))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be 32 * 2^j <= 2048");
+  ok();
+  return ws_layout(M, k, H, I, has_shared != 0).total;
+}
+
+int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
+  if (!a) return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_decode: args is null");
+  if (!a->x || !a->w || !a->offsets || !a->pairs || !a->active || !a->n_active ||
+      !a->w_gate_up || !a->w_down || !a->out || !a->workspace)
+    return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_decode: a required pointer is null");
+  if ((a->shared_gate_up == nullptr) != (a->shared_down == nullptr))
+    return fail(NVFP4MOE_ERR_NULL_ARG, "shared_gate_up and shared_down go together");
+  const int64_t M = a->M, E = a->E, k = a->k, H = a->H, I = a->I;
+  if (M < 1 || E < 1 || k < 1 || H < 1 || I < 1)
+    return fail(NVFP4MOE_ERR_BAD_SHAPE, "M, E, k, H, I must be >= 1");
+  if (E > kRouteMaxE || k > kRouteMaxK || k > E)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "need E <= 256 and k <= min(8, E)");
+  if (!valid_k(H) || !valid_k(I))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be 32 * 2^j <= 2048");
+  if (I % rows_per_tile(H) != 0)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "I = %lld must be a multiple of 16384 / H = %lld",
+                (long long)I, (long long)rows_per_tile(H));
+  if (M * k + M > (int64_t)1 << 30) return fail(NVFP4MOE_ERR_UNSUPPORTED, "M too large");
+  const bool shared = a->shared_gate_up != nullptr;
+  const WsLayout ws = ws_layout(M, k, H, I, shared);
+  if (a->workspace_bytes < ws.total)
+    return fail(NVFP4MOE_ERR_WORKSPACE, "workspace %lld < %lld bytes",
+                (long long)a->workspace_bytes, (long long)ws.total);
+  if (!aligned(a->x, 16) || !aligned(a->w_gate_up, 16) || !aligned(a->w_down, 16) ||
+      !aligned(a->workspace, 256) || (shared && (!aligned(a->shared_gate_up, 16) ||
+                                                 !aligned(a->shared_down, 16))))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED,
+                "x and weights need 16-byte, workspace 256-byte alignment");
+
+  MoeParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.x = a->x;
+  p.w = a->w;
+  p.offsets = a->offsets;
+  p.pairs = a->pairs;
+  p.active = a->active;
+  p.n_active = a->n_active;
+  p.gu = (const uint8_t*)a->w_gate_up;
+  p.dn = (const uint8_t*)a->w_down;
+  p.sgu = (const uint8_t*)a->shared_gate_up;
+  p.sdn = (const uint8_t*)a->shared_down;
+  p.residual = a->residual;
+  p.out = a->out;
+  uint8_t* wsb = (uint8_t*)a->workspace;
+  p.h = (float*)(wsb + ws.h_off);
+  p.y = (float*)(wsb + ws.y_off);
+  p.counters = (uint32_t*)(wsb + ws.cnt_off);
+  p.M = (int)M;
+  p.E = (int)E;
+  p.k = (int)k;
+  p.H = (int)H;
+  p.I = (int)I;
+  p.routed_slots = (int)(E < M * k ? E : M * k);
+  p.has_shared = shared ? 1 : 0;
+  p.gu_mat_bytes = matrix_bytes(2 * I, H);
+  p.dn_mat_bytes = matrix_bytes(H, I);
+  p.gu_g = (const float*)(p.gu + gscale_offset(E, 2 * I, H));
+  p.dn_g = (const float*)(p.dn + gscale_offset(E, H, I));
+  if (shared) {
+    p.sgu_g = (const float*)(p.sgu + gscale_offset(1, 2 * I, H));
+    p.sdn_g = (const float*)(p.sdn + gscale_offset(1, H, I));
+  }
+  p.gu_tiles_per_half = (int)(I / rows_per_tile(H));
+  p.gu_blocks_per_slot = (p.gu_tiles_per_half + 3) / 4;
+  p.dn_tiles = (int)tiles_per_matrix(H, I);
+  p.dn_groups = (p.dn_tiles + 3) / 4;
+  const int slots = p.routed_slots + p.has_shared;
+  int32_t st = dispatch_l<GateUpLaunch>(H / 32, p, slots * p.gu_blocks_per_slot, stream);
+  if (st != NVFP4MOE_OK) return st;
+  return dispatch_l<DownLaunch>(I / 32, p, slots * p.dn_groups, stream);
+}
+
+}  // extern "C"

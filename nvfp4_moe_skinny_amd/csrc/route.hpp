@@ -1,0 +1,205 @@
+// route.hpp - top-k routing and grouping of (row, slot) pairs by expert.
+//
+// Selection is exact: every logit becomes a 64-bit key whose high word is an
+// order-preserving image of the FP32 value (-0 folded onto +0, NaN below
+// -inf) and whose low word favours the lower expert index, so a wave-wide
+// integer max picks the same expert as a stable sort would. k rounds of that
+// max give the k experts in order; the weights are the softmax over them.
+// Grouping is a stable counting sort: a pair's place inside its expert's run
+// is the number of earlier pairs routed to the same expert.
+#pragma once
+
+#include "common.hpp"
+
+namespace nvfp4moe {
+
+constexpr int kRouteMaxE = 256;
+constexpr int kRouteMaxK = 8;
+constexpr int kRouteWaves = 16;          // 1024 threads
+constexpr int kRouteSingleBlockRows = 64;  // rows routed and grouped in one launch
+
+__device__ __forceinline__ uint64_t route_key(float l, int e) {
+  uint32_t b = __float_as_uint(l);
+  if (b == 0x80000000u) b = 0u;  // -0 ties with +0
+  uint32_t ord;
+  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu))
+    ord = 0u;  // NaN: below every number, -inf included
+  else
+    ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)(0xFFFF - e);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+// Routes one row with one wave: ids and weights to global memory and to
+// ids_lds (if not null).
+__device__ __forceinline__ void route_row(const float* __restrict__ logits,
+                                          const float* __restrict__ bias, int E, int k, int row,
+                                          int lane, float* lp, int32_t* __restrict__ ids,
+                                          float* __restrict__ w, int32_t* ids_lds) {
+  uint64_t key[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int e = lane + 64 * s;
+    if (e < E) {
+      float l = logits[(int64_t)row * E + e];
+      if (bias) l = l + bias[e];
+      lp[e] = l;
+      key[s] = route_key(l, e);
+    } else {
+      key[s] = 0;  // below every real key, NaN ones included
+    }
+  }
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int s = 1; s < 4; ++s) best = key[s] > best ? key[s] : best;
+    best = wave_max_u64(best);
+    const int e = 0xFFFF - (int)(uint32_t)(best & 0xFFFFu);
+    if (lane == (e & 63)) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (s == (e >> 6)) key[s] = 0;
+    }
+    if (lane == j) my_id = e;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const float top = lp[__shfl(my_id, 0, 64)];
+  const float ex = lane < k ? expf(lp[my_id] - top) : 0.0f;
+  const float z = wave_sum(ex);
+  if (lane < k) {
+    ids[(int64_t)row * k + lane] = my_id;
+    w[(int64_t)row * k + lane] = ex / z;
+    if (ids_lds) ids_lds[row * k + lane] = my_id;
+  }
+}
+
+// Inclusive scan over 256 entries held 4 per lane (lane l: entries 4l..4l+3)
+// by one wave; returns the exclusive prefix of each entry in ex[4].
+__device__ __forceinline__ void wave_scan256(const int (&v)[4], int lane, int (&ex)[4], int& total) {
+  const int s0 = v[0], s1 = s0 + v[1], s2 = s1 + v[2], s3 = s2 + v[3];
+  int incl = s3;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  const int base = incl - s3;
+  ex[0] = base;
+  ex[1] = base + s0;
+  ex[2] = base + s1;
+  ex[3] = base + s2;
+  total = __shfl(incl, 63, 64);
+}
+
+// Groups the P = M*k pairs by expert. Needs ids_lds[P] filled; uses counts_lds[256].
+// All threads of the block call it.
+__device__ __forceinline__ void group_pairs(const int32_t* ids_lds, int P, int E, int* counts_lds,
+                                            int* offs_lds, int32_t* __restrict__ counts,
+                                            int32_t* __restrict__ offsets,
+                                            int32_t* __restrict__ pairs,
+                                            int32_t* __restrict__ active,
+                                            int32_t* __restrict__ n_active) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kRouteMaxE; e += blockDim.x) counts_lds[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += blockDim.x) atomicAdd(&counts_lds[ids_lds[p]], 1);
+  __syncthreads();
+  if (tid < 64) {
+    const int lane = tid;
+    int c[4], f[4], cex[4], fex[4], ctot, ftot;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = counts_lds[4 * lane + j];
+      f[j] = c[j] > 0 ? 1 : 0;
+    }
+    wave_scan256(c, lane, cex, ctot);
+    wave_scan256(f, lane, fex, ftot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * lane + j;
+      offs_lds[e] = cex[j];
+      if (e < E) {
+        counts[e] = c[j];
+        offsets[e] = cex[j];
+        if (f[j]) active[fex[j]] = e;  // active slots [0, ftot)
+        if (e >= ftot) active[e] = -1;  // unused slots [ftot, E)
+      }
+    }
+    if (lane == 0) {
+      offsets[E] = ctot;
+      *n_active = ftot;
+    }
+  }
+  __syncthreads();
+  // stable placement: rank of p among earlier pairs of the same expert
+  for (int p = tid; p < P; p += blockDim.x) {
+    const int e = ids_lds[p];
+    int rank = 0;
+    for (int q = 0; q < p; ++q) rank += (ids_lds[q] == e) ? 1 : 0;
+    pairs[offs_lds[e] + rank] = p;
+  }
+}
+
+// Single-launch routing for M <= kRouteSingleBlockRows: one block of 16 waves.
+__global__ void __launch_bounds__(1024) route_group_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int M, int E, int k,
+    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ pairs, int32_t* __restrict__ active,
+    int32_t* __restrict__ n_active) {
+  __shared__ float lp[kRouteWaves][kRouteMaxE];
+  __shared__ int32_t ids_lds[kRouteSingleBlockRows * kRouteMaxK];
+  __shared__ int counts_lds[kRouteMaxE];
+  __shared__ int offs_lds[kRouteMaxE];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int row = wave; row < M; row += kRouteWaves)
+    route_row(logits, bias, E, k, row, lane, lp[wave], ids, w, ids_lds);
+  __syncthreads();
+  group_pairs(ids_lds, M * k, E, counts_lds, offs_lds, counts, offsets, pairs, active, n_active);
+}
+
+// Larger M, first launch: one wave per row.
+__global__ void __launch_bounds__(1024) route_rows_kernel(const float* __restrict__ logits,
+                                                          const float* __restrict__ bias, int M,
+                                                          int E, int k, int32_t* __restrict__ ids,
+                                                          float* __restrict__ w) {
+  __shared__ float lp[kRouteWaves][kRouteMaxE];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRouteWaves + wave;
+  if (row < M) route_row(logits, bias, E, k, row, lane, lp[wave], ids, w, nullptr);
+}
+
+// Larger M, second launch: group all pairs in one block (P <= kGroupMaxPairs).
+constexpr int kGroupMaxPairs = 8192;
+__global__ void __launch_bounds__(1024) group_kernel(const int32_t* __restrict__ ids, int M, int E,
+                                                     int k, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ pairs,
+                                                     int32_t* __restrict__ active,
+                                                     int32_t* __restrict__ n_active) {
+  __shared__ int32_t ids_lds[kGroupMaxPairs];
+  __shared__ int counts_lds[kRouteMaxE];
+  __shared__ int offs_lds[kRouteMaxE];
+  const int P = M * k;
+  for (int p = threadIdx.x; p < P; p += blockDim.x) ids_lds[p] = ids[p];
+  __syncthreads();
+  group_pairs(ids_lds, P, E, counts_lds, offs_lds, counts, offsets, pairs, active, n_active);
+}
+
+}  // namespace nvfp4moe

@@ -1,0 +1,117 @@
+// tile.hpp - one wavefront x one packed tile x R activation rows.
+//
+// A wave loads a whole tile (8 x 1 KB of codes, 1 KB of scales) with nine
+// 128-bit loads per lane, keeps it in registers, and multiplies it with up
+// to 8 activation rows at a time. Per slab and row a lane forms two 16-element
+// partial sums (one per E4M3 block) and scales each once:
+//   BF16 rows: codes -> BF16 pairs (v_cvt_scalef32_pk_bf16_fp4), then
+//              v_dot2c_f32_bf16 against the BF16 activation pairs;
+//   FP32 rows: codes -> FP32 pairs (v_cvt_scalef32_pk_f32_fp4), then FMA.
+// E2M1 x BF16 products are exact in FP32, so only the FP32 sums round.
+#pragma once
+
+#include "common.hpp"
+
+namespace nvfp4moe {
+
+struct TileRegs {
+  uint4 codes[8];
+  uint4 scales;
+};
+
+__device__ __forceinline__ void load_tile(const uint8_t* tile, int lane, TileRegs& t) {
+  const uint4* c = reinterpret_cast<const uint4*>(tile);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t.codes[i] = load_stream(c + i * 64 + lane);
+  t.scales = load_stream(reinterpret_cast<const uint4*>(tile + kTileCodeBytes) + lane);
+}
+
+// part[r][i] = sum over the lane's 32 columns of slab i of W * x_r (no g).
+// x[r] holds the row's 32 BF16 values of the lane's columns as 4 x uint4.
+template <int R>
+__device__ __forceinline__ void tile_dot_bf16(const TileRegs& t, const uint4 (&x)[R][4],
+                                              float (&part)[R][8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    bf16x2 w[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) w[p] = fp4_pair_bf16(u4_get(t.codes[i], p >> 2), p & 3);
+    const float s0 = tile_scale(t.scales, i, 0);
+    const float s1 = tile_scale(t.scales, i, 1);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(w[p], as_bf16x2(u4_get(x[r][p >> 2], p & 3)), a0,
+                                             false);
+#pragma unroll
+      for (int p = 8; p < 16; ++p)
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(w[p], as_bf16x2(u4_get(x[r][p >> 2], p & 3)), a1,
+                                             false);
+      part[r][i] = a0 * s0 + a1 * s1;
+    }
+  }
+}
+
+// Same with FP32 activation rows: h[r] = 32 FP32 values of the lane's columns.
+template <int R>
+__device__ __forceinline__ void tile_dot_f32(const TileRegs& t, const float (&h)[R][32],
+                                             float (&part)[R][8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f32x2 w[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) w[p] = fp4_pair_f32(u4_get(t.codes[i], p >> 2), p & 3);
+    const float s0 = tile_scale(t.scales, i, 0);
+    const float s1 = tile_scale(t.scales, i, 1);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        a0 = __builtin_fmaf(w[p][0], h[r][2 * p], a0);
+        a0 = __builtin_fmaf(w[p][1], h[r][2 * p + 1], a0);
+      }
+#pragma unroll
+      for (int p = 8; p < 16; ++p) {
+        a1 = __builtin_fmaf(w[p][0], h[r][2 * p], a1);
+        a1 = __builtin_fmaf(w[p][1], h[r][2 * p + 1], a1);
+      }
+      part[r][i] = a0 * s0 + a1 * s1;
+    }
+  }
+}
+
+// Loads the lane's 32 BF16 columns of activation row `row` (or zeros).
+__device__ __forceinline__ void load_x_bf16(const uint16_t* x, int64_t ld, int64_t row, bool valid,
+                                            int col0, uint4 (&xr)[4]) {
+  if (valid) {
+    const uint4* p = reinterpret_cast<const uint4*>(x + row * ld + col0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xr[j] = p[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xr[j] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void load_h_f32(const float* h, int64_t ld, int64_t row, bool valid,
+                                           int col0, float (&hr)[32]) {
+  if (valid) {
+    const float4* p = reinterpret_cast<const float4*>(h + row * ld + col0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 v = p[j];
+      hr[4 * j] = v.x;
+      hr[4 * j + 1] = v.y;
+      hr[4 * j + 2] = v.z;
+      hr[4 * j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) hr[j] = 0.0f;
+  }
+}
+
+}  // namespace nvfp4moe

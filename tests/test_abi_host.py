@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol the header declares, and rejects bad arguments with the
+documented status codes before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import nvfp4_moe_skinny_amd as m
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(m):
+    names = declared_functions()
+    assert set(m.EXPORTS) == set(names), names
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(m):
+    for code, name in [(0, "NVFP4MOE_OK"), (-1, "NVFP4MOE_ERR_NULL_ARG"),
+                       (-2, "NVFP4MOE_ERR_BAD_SHAPE"), (-3, "NVFP4MOE_ERR_UNSUPPORTED"),
+                       (-4, "NVFP4MOE_ERR_WORKSPACE"), (-5, "NVFP4MOE_ERR_HIP")]:
+        assert m.strerror(code) == name
+    assert m.strerror(7) == "NVFP4MOE_ERR_UNKNOWN"
+    assert "gfx950" in m.version()
+
+
+def test_packed_bytes(m):
+    # tile = 8 KB codes + 1 KB scales; 16384 / K rows per tile
+    assert m.nvfp4_packed_bytes(1, 512, 2048) == 64 * 9216 + 256
+    assert m.nvfp4_packed_bytes(256, 1024, 2048) == 256 * 128 * 9216 + 1024
+    assert m.nvfp4_packed_bytes(256, 2048, 512) == 256 * 64 * 9216 + 1024
+    assert m.nvfp4_packed_bytes(1, 33, 512) == 2 * 9216 + 256     # ragged rows pad
+    for K in (16, 48, 96, 4096, 0):
+        assert m.lib.nvfp4_packed_bytes(1, 8, K) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert m.lib.nvfp4_packed_bytes(0, 8, 64) == m.NVFP4MOE_ERR_BAD_SHAPE
+
+
+def test_validation_errors_before_launch(m):
+    L = m.lib
+    fake = 4096  # never dereferenced: every call below fails validation first
+    assert L.nvfp4_pack(None, fake, fake, 1, 8, 64, fake, None) == m.NVFP4MOE_ERR_NULL_ARG
+    assert L.nvfp4_pack(fake, fake, fake, 1, 8, 96, fake, None) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert L.nvfp4_dequant_f32(fake, 1, 8, 64, 1, 2, fake, None) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert L.nvfp4_skinny_gemm(fake, 0, 64, fake, 8, fake, None) == m.NVFP4MOE_ERR_BAD_SHAPE
+    assert L.nvfp4_skinny_gemm(fake, 1, 4096, fake, 8, fake, None) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert L.nvfp4_skinny_gemm(fake + 2, 1, 64, fake, 8, fake, None) == \
+        m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned x
+    r = [fake] * 7
+    assert L.moe_route_topk(None, None, 4, 256, 8, *r, None) == m.NVFP4MOE_ERR_NULL_ARG
+    assert L.moe_route_topk(fake, None, 4, 257, 8, *r, None) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert L.moe_route_topk(fake, None, 4, 256, 9, *r, None) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert L.moe_route_topk(fake, None, 4, 4, 5, *r, None) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert L.moe_route_topk(fake, None, 0, 256, 8, *r, None) == m.NVFP4MOE_ERR_BAD_SHAPE
+    assert L.moe_route_topk(fake, None, 2000, 256, 8, *r, None) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert "k" in m.last_error_detail() or "M" in m.last_error_detail()
+
+
+def _args(m, **kw):
+    a = m.MoeArgs()
+    fake = 4096
+    for f in ("x", "ids", "w", "offsets", "pairs", "active", "n_active", "w_gate_up", "w_down",
+              "out", "workspace"):
+        setattr(a, f, fake)
+    a.workspace_bytes = 1 << 30
+    a.M, a.E, a.k, a.H, a.I = 4, 256, 8, 2048, 512
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_validation(m):
+    L = m.lib
+    dec = lambda a: L.moe_nvfp4_decode(ctypes.byref(a), None)
+    assert L.moe_nvfp4_decode(None, None) == m.NVFP4MOE_ERR_NULL_ARG
+    assert dec(_args(m, x=None)) == m.NVFP4MOE_ERR_NULL_ARG
+    assert dec(_args(m, shared_gate_up=4096)) == m.NVFP4MOE_ERR_NULL_ARG  # down missing
+    assert dec(_args(m, M=0)) == m.NVFP4MOE_ERR_BAD_SHAPE
+    assert dec(_args(m, E=300)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert dec(_args(m, k=9)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert dec(_args(m, H=3000)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert dec(_args(m, I=100)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert dec(_args(m, H=2048, I=4)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    need = m.moe_nvfp4_workspace_bytes(4, 256, 8, 2048, 512, False)
+    assert dec(_args(m, workspace_bytes=need - 1)) == m.NVFP4MOE_ERR_WORKSPACE
+    assert "workspace" in m.last_error_detail()
+    assert dec(_args(m, x=4096 + 8)) == m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned
+    # h [M*k][I] + y [M*k][H] FP32 + counters
+    assert need >= 4 * 8 * (512 + 2048) * 4
+    assert m.moe_nvfp4_workspace_bytes(4, 256, 8, 2048, 512, True) > need

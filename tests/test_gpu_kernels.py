@@ -1,0 +1,155 @@
+"""GPU parity of each kernel against the oracle, through the C ABI.
+
+Decode and routing are compared bit for bit; products under
+|gpu - ref| <= 1e-2 |ref| + 1e-3 against the oracle's float64 result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.workloads import NVFP4, dense_skinny, moe_layer
+from tests.helpers import (check_routing_exact, dev_bf16_to_f64, pack, to_dev_bf16, tol_ratio,
+                           upload_layer)
+
+pytestmark = pytest.mark.gpu
+
+FINITE_E4M3 = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+@pytest.fixture(scope="module")
+def m(gpu):
+    import nvfp4_moe_skinny_amd as m
+    return m
+
+
+def _all_codes_all_scales(G, N, K, gvals, seed=0):
+    """Every 16-element block enumerates the 16 E2M1 codes; the scales cycle
+    through every finite E4M3 code (with a per-row offset)."""
+    codes = np.tile(np.array([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE], np.uint8),
+                    (G, N, K // 16))
+    nb = K // 16
+    idx = (np.arange(G * N * nb).reshape(G, N, nb) + seed) % len(FINITE_E4M3)
+    scales = FINITE_E4M3[idx]
+    return NVFP4(codes, scales, np.asarray(gvals, np.float32))
+
+
+@pytest.mark.parametrize("K,N", [(2048, 8), (2048, 11), (512, 33), (64, 300), (32, 513),
+                                 (1024, 16), (128, 128)])
+@pytest.mark.parametrize("path", [0, 1])
+def test_dequant_bit_exact_every_code_and_scale(m, gpu, K, N, path):
+    nv = _all_codes_all_scales(3, N, K, [1.0, 2.0 ** -9, 0.37], seed=K + N)
+    pw = pack(nv, gpu, m)
+    for apply_g in (True, False):
+        got = m.nvfp4_dequant_f32(pw, apply_g=apply_g, path=path).cpu().numpy()
+        g = nv.g if apply_g else np.ones_like(nv.g)
+        ref = oracle.dequant_f32(nv.codes, nv.scales, g)
+        assert (got.view(np.uint32) == ref.view(np.uint32)).all()
+
+
+def test_dequant_random_tensor(m, gpu):
+    rng = np.random.default_rng(1)
+    G, N, K = 4, 77, 256
+    nv = NVFP4(rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8),
+               rng.choice(FINITE_E4M3, (G, N, K // 16)).astype(np.uint8),
+               np.array([1.0, 0.5, 3.0, 2.0 ** -8], np.float32))
+    pw = pack(nv, gpu, m)
+    got = m.nvfp4_dequant_f32(pw, path=0).cpu().numpy()
+    ref = oracle.dequant_f32(nv.codes, nv.scales, nv.g)
+    assert (got.view(np.uint32) == ref.view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("M,K,N,g", [(1, 2048, 512, 1.0),      # the single dense matrix
+                                     (8, 2048, 64, 2.0 ** -9),  # per-layer 2048 -> 64
+                                     (3, 2048, 37, 0.37), (19, 512, 100, 1.0),
+                                     (5, 256, 64, 2.0 ** -4), (2, 32, 700, 1.0),
+                                     (16, 1024, 48, 0.5), (4, 64, 5, 1.0)])
+def test_skinny_gemm(m, gpu, M, K, N, g):
+    x, w = dense_skinny(seed=0, M=M, K=K, N=N, g=g)
+    pw = pack(w, gpu, m)
+    y = m.nvfp4_skinny_gemm(to_dev_bf16(x, gpu), pw)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(x, w.codes[0], w.scales[0], g)
+    assert tol_ratio(dev_bf16_to_f64(y), ref) <= 1.0
+
+
+@pytest.mark.parametrize("M,E,k,bias", [(1, 256, 8, False), (4, 256, 8, False),
+                                        (8, 256, 8, False), (16, 256, 8, True),
+                                        (64, 256, 8, True), (65, 256, 8, False),
+                                        (256, 256, 8, False), (1024, 256, 8, False),
+                                        (3, 5, 2, False), (7, 64, 1, True), (20, 8, 8, False)])
+def test_route_bit_exact(m, gpu, M, E, k, bias):
+    for seed in range(3):
+        lg = synth.normal_f32(synth.key(seed, 100, M, E), (M, E))
+        b = synth.normal_f32(synth.key(seed, 101, E), (E,), 0.0, 0.5) if bias else None
+        r = m.moe_route_topk(torch.from_numpy(lg).to(gpu), k,
+                             None if b is None else torch.from_numpy(b).to(gpu))
+        torch.cuda.synchronize()
+        ids, w = oracle.route_topk(lg, k, b)
+        check_routing_exact(r, ids, w, E)
+
+
+def test_route_zipf_logits(m, gpu):
+    lg = synth.zipf_gumbel_logits(synth.key(0, 102), synth.key(0, 103), 256, 256, 1.1)
+    r = m.moe_route_topk(torch.from_numpy(lg).to(gpu), 8)
+    torch.cuda.synchronize()
+    ids, w = oracle.route_topk(lg, 8)
+    check_routing_exact(r, ids, w, 256)
+
+
+def test_route_constructed_ties(m, gpu):
+    E, k = 16, 4
+    rows = np.array([
+        [1.0] * E,
+        [0.0, -0.0, 0.0, -0.0] + [-1.0] * 12,
+        [np.nan, 2.0, np.nan, 2.0, 1.0, -np.inf] + [-3.0] * 10,
+        [-np.inf] * 2 + [5.0, 5.0, 5.0] + [-np.inf] * 11,
+        [-0.0] * E,
+        [3.0, 3.0, -0.0, 0.0] + [2.0] * 12,
+    ], dtype=np.float32)
+    r = m.moe_route_topk(torch.from_numpy(rows).to(gpu), k)
+    torch.cuda.synchronize()
+    ids, w = oracle.route_topk(rows, k)
+    check_routing_exact(r, ids, w, E)
+    # the FP32 bias add decides a tie that exact arithmetic would not
+    lg = np.array([[1.0, 1.0 + 2 ** -23, 0.0, 0.0]], np.float32)
+    b = np.array([3 * 2 ** -25, 0.0, 0.0, 0.0], np.float32)
+    r = m.moe_route_topk(torch.from_numpy(lg).to(gpu), 1, torch.from_numpy(b).to(gpu))
+    torch.cuda.synchronize()
+    assert int(r.ids.cpu()[0, 0]) == 0
+
+
+def _run_block(m, gpu, lay, residual=None):
+    d = upload_layer(lay, gpu, m)
+    r = m.moe_route_topk(d["logits"], lay.k, d["bias"])
+    res = None if residual is None else to_dev_bf16(residual, gpu)
+    out = m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=res)
+    torch.cuda.synchronize()
+    return r, dev_bf16_to_f64(out)
+
+
+@pytest.mark.parametrize("M,E,H,I,k,shared,resid", [
+    (1, 16, 256, 64, 4, False, False), (3, 16, 256, 64, 4, True, False),
+    (8, 16, 256, 64, 4, False, True), (17, 16, 256, 64, 4, True, True),
+    (5, 8, 512, 64, 8, True, False), (2, 32, 1024, 128, 2, False, True),
+    (6, 4, 2048, 512, 1, True, True), (11, 256, 128, 128, 8, False, False)])
+def test_moe_block_small(m, gpu, M, E, H, I, k, shared, resid):
+    lay = moe_layer(seed=M + E, wl=200, M=M, E_=E, H_=H, I_=I, k=k, shared=shared)
+    residual = synth.normal_bf16(synth.key(5, 201, M), (M, H)) if resid else None
+    r, out = _run_block(m, gpu, lay, residual)
+    ids, w = oracle.route_topk(lay.logits, k, lay.bias)
+    check_routing_exact(r, ids, w, E)
+    ref = oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down, lay.shared_gate_up,
+                           lay.shared_down, residual)
+    assert tol_ratio(out, ref) <= 1.0
+
+
+def test_moe_block_deterministic(m, gpu):
+    lay = moe_layer(seed=3, wl=202, M=16, E_=32, H_=512, I_=128, k=8, shared=True)
+    d = upload_layer(lay, gpu, m)
+    r = m.moe_route_topk(d["logits"], lay.k)
+    a = m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"])
+    b = m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"])
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -1,0 +1,100 @@
+"""GPU parity on the five workloads at full size, against the oracle.
+
+Routing is compared bit for bit on every row. Outputs are compared under
+|gpu - ref| <= 1e-2 |ref| + 1e-3 on every element where the oracle finishes in
+seconds, otherwise on sampled rows (the oracle computes a row on its own).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import workloads as W
+from tests.helpers import (check_routing_exact, dev_bf16_to_f64, pack, to_dev_bf16, tol_ratio,
+                           upload_layer)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m(gpu):
+    import nvfp4_moe_skinny_amd as m
+    return m
+
+
+def test_dense_single_matrix(m, gpu):
+    x, w = W.dense_skinny(seed=0)
+    pw = pack(w, gpu, m)
+    y = m.nvfp4_skinny_gemm(to_dev_bf16(x, gpu), pw)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(x, w.codes[0], w.scales[0], 1.0)
+    assert tol_ratio(dev_bf16_to_f64(y), ref) <= 1.0
+
+
+def _block(m, gpu, lay):
+    d = upload_layer(lay, gpu, m)
+    r = m.moe_route_topk(d["logits"], lay.k, d["bias"])
+    out = m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"])
+    torch.cuda.synchronize()
+    return r, dev_bf16_to_f64(out)
+
+
+def test_decode_m4(m, gpu):
+    lay = W.decode_m4()
+    r, out = _block(m, gpu, lay)
+    ids, w = oracle.route_topk(lay.logits, lay.k)
+    check_routing_exact(r, ids, w, lay.E)
+    ref = oracle.moe_block_touched(lay, ids, w)
+    assert tol_ratio(out, ref) <= 1.0
+
+
+def test_decode_m16_bias_shared(m, gpu):
+    lay = W.decode_m16_shared()
+    r, out = _block(m, gpu, lay)
+    ids, w = oracle.route_topk(lay.logits, lay.k, lay.bias)
+    check_routing_exact(r, ids, w, lay.E)
+    ref = oracle.moe_block_touched(lay, ids, w)
+    assert tol_ratio(out, ref) <= 1.0
+
+
+def test_prefill_m256_zipf(m, gpu):
+    lay = W.prefill_m256()
+    r, out = _block(m, gpu, lay)
+    ids, w = oracle.route_topk(lay.logits, lay.k)
+    g = check_routing_exact(r, ids, w, lay.E)
+    counts = g["counts"]
+    assert counts.max() > 100  # Zipf(1.1) over 256 experts: a few experts take most rows
+    rows = np.arange(0, lay.M, 17)
+    ref = oracle.moe_block_touched(lay, ids, w, rows=rows)
+    assert tol_ratio(out[rows], ref) <= 1.0
+
+
+@pytest.mark.parametrize("check_layers", [(0, 1, 20, 39)])
+def test_stack_40_layers_teacher_forced(m, gpu, check_layers):
+    """40 MoE blocks (routed + shared expert + residual) and a dense 2048->64
+    projection per layer, run as a chain on the GPU. Checked layers are
+    recomputed by the oracle from the GPU's own BF16 input of that layer."""
+    x_host = W.stack_x0()
+    x = to_dev_bf16(x_host, gpu)
+    worst = 0.0
+    for l in range(W.STACK_LAYERS):
+        lay = W.stack_layer(l, x=x_host)
+        d = upload_layer(lay, gpu, m)
+        pw = pack(lay.extra["proj"], gpu, m)
+        r = m.moe_route_topk(d["logits"], lay.k)
+        proj = m.nvfp4_skinny_gemm(x, pw)
+        x_next = m.moe_nvfp4_decode(x, r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=x)
+        torch.cuda.synchronize()
+        if l in check_layers:
+            ids, w = oracle.route_topk(lay.logits, lay.k)
+            check_routing_exact(r, ids, w, lay.E)
+            ref = oracle.moe_block_touched(lay, ids, w, residual=x_host)
+            worst = max(worst, tol_ratio(dev_bf16_to_f64(x_next), ref))
+            p = lay.extra["proj"]
+            pref = oracle.gemm(x_host, p.codes[0], p.scales[0], float(p.g[0]))
+            worst = max(worst, tol_ratio(dev_bf16_to_f64(proj), pref))
+        x = x_next
+        x_host = x.cpu().view(torch.int16).numpy().view(np.uint16)
+        del d, pw
+    assert np.isfinite(dev_bf16_to_f64(x)).all()
+    assert worst <= 1.0
