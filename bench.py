@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 MoE decode step on one MI355X.
+
+A step is one pass of the routed MoE hot path over one batch of rows: router
+top-k + grouping (moe_route_topk), then gate_up -> SiLU*up -> down -> combine
+(moe_nvfp4_decode). The headline workload is one MoE block at M = 4 rows (one
+token plus three draft tokens verified together): 256 experts, top-8,
+hidden 2048, expert width 512, NVFP4 weights, BF16 activations.
+
+To keep the 256 MB Infinity Cache from serving weights, each step uses the
+next of `copies` independently seeded weight sets (>= 1 GB streams between two
+uses of the same bytes) and the next of 64 router-logit sets. Inputs are
+resident in HBM before timing starts. Steps are captured into a HIP graph and
+replayed; `value` is algorithmic bytes per step (touched expert codes + scales
++ tensor scales, activations in and out, logits and routing arrays) over the
+step time. The dominant call (moe_nvfp4_decode) is also timed on its own with
+HIP events on the stream it runs on, for the roofline entry.
+
+The oracle (float64 C++ on the host) is timed on a bounded sample of the same
+steps as a reported CPU baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 MoE decode achieved HBM GB/s (% of peak) + token-rows/s at M=4"
+HBM_PEAK_GBS = 8000.0
+CPU_LAYERS = 12  # weight copies kept on the host for the CPU-baseline sample
+
+
+def expert_bytes(H, I):
+    """Canonical NVFP4 bytes of one expert: gate_up [2I][H] + down [H][I]
+    (codes + E4M3 scales + FP32 tensor scale)."""
+    gu = 2 * I * H // 2 + 2 * I * H // 16 + 4
+    dn = H * I // 2 + H * I // 16 + 4
+    return gu + dn
+
+
+def step_bytes(M, E, k, H, I, n_active, shared, bias):
+    b = n_active * expert_bytes(H, I) + (expert_bytes(H, I) if shared else 0)
+    b += M * H * 2 * 2          # x in, out
+    b += M * E * 4              # logits
+    b += E * 4 if bias else 0   # logit bias
+    b += M * k * (4 + 4) * 2    # ids, w written then read
+    b += (E + E + 1 + E + 1) * 4 + M * k * 4 * 2  # counts, offsets, active, n_active, pairs
+    return b
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20000)
+    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--workload", default="m4", choices=["m4", "m16"])
+    p.add_argument("--copies", type=int, default=0, help="weight sets cycled (0: >= 1 GB)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--eager-calls", type=int, default=400)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path runs on one GPU's share; see DESIGN.md for sharding)", file=sys.stderr)
+        return 2
+    import torch
+
+    import nvfp4_moe_skinny_amd as m
+    from synth import workloads as W
+    from tests.helpers import pack, to_dev_bf16
+
+    dev = torch.device("cuda:0")
+    if args.workload == "m4":
+        make = lambda c: W.moe_layer(0, wl=2, layer=c, M=4)
+        name = "moe_block_m4_e256_top8_h2048_i512"
+    else:
+        make = lambda c: W.moe_layer(0, wl=3, layer=c, M=16, bias=True, shared=True)
+        name = "moe_block_m16_e256_top8_h2048_i512_bias_shared"
+    lay0 = make(0)
+    M, E, k, H, I = lay0.M, lay0.E, lay0.k, lay0.H, lay0.I
+    shared = lay0.shared_gate_up is not None
+    bias = lay0.bias is not None
+    per_step_est = 31 * expert_bytes(H, I) if M == 4 else 84 * expert_bytes(H, I)
+    copies = args.copies or int(np.ceil(1e9 / per_step_est)) + 1
+
+    # ---- resident inputs -------------------------------------------------------------
+    t0 = time.time()
+    weights = []
+    layers_host = []
+    for c in range(copies):
+        lay = lay0 if c == 0 else make(c)
+        gu, dn = pack(lay.gate_up, dev, m), pack(lay.down, dev, m)
+        sgu = pack(lay.shared_gate_up, dev, m) if shared else None
+        sdn = pack(lay.shared_down, dev, m) if shared else None
+        weights.append((gu, dn, sgu, sdn))
+        if c < CPU_LAYERS:
+            layers_host.append(lay)
+        torch.cuda.synchronize()
+    # 64 router-logit / activation sets (small tensors: only the logits and x are used)
+    n_sets = 64
+    wl = 2 if M == 4 else 3
+    logit_sets = [W.moe_layer(0, wl=wl, layer=1000 + i, M=M, E_=E, H_=32, I_=32, k=k, bias=bias)
+                  for i in range(n_sets)]
+    x_host = [W.normal_bf16(W.key(0, wl, 1000 + i, W.T_X, 1), (M, H)) for i in range(n_sets)]
+    xs = [to_dev_bf16(xh, dev) for xh in x_host]
+    lg = [torch.from_numpy(L.logits).to(dev) for L in logit_sets]
+    bs = [torch.from_numpy(L.bias).to(dev) if bias else None for L in logit_sets]
+    routes = [m.routing_buffers(M, E, k, dev) for _ in range(n_sets)]
+    outs = [torch.empty((M, H), dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+    ws = m.moe_workspace(M, E, k, H, I, shared, dev)  # zero-filled once
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    # one step of the hot path: (weight copy c, logits/x set j)
+    def step(i):
+        c, j = i % copies, i % n_sets
+        gu, dn, sgu, sdn = weights[c]
+        r = m.moe_route_topk(lg[j], k, bs[j], out=routes[j])
+        m.moe_nvfp4_decode(xs[j], r, gu, dn, sgu, sdn, workspace=ws, out=outs[j])
+
+    # the graph holds S steps: step i uses weight copy i % copies and set i % n_sets
+    S = copies * int(np.ceil(n_sets / copies))
+    for i in range(max(args.warmup, S)):
+        step(i)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(S):
+                step(i)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+
+    replays = max(1, args.steps // S)
+    steps = replays * S
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.time()
+    ev0.record()
+    for _ in range(replays):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / steps
+
+    # bytes from each step's actual routing (read back after the timed region)
+    n_act = np.array([int(routes[j].n_active.item()) for j in range(n_sets)])
+    bytes_per_set = np.array([step_bytes(M, E, k, H, I, int(na), shared, bias) for na in n_act])
+    mean_bytes = float(np.mean([bytes_per_set[i % n_sets] for i in range(S)]))
+    gbs = mean_bytes / (ms_per_step * 1e-3) / 1e9
+    rows_per_s = M / (ms_per_step * 1e-3)
+
+    # eager: each decode call timed with events on its own stream (roofline entry)
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.eager_calls)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.eager_calls)]
+    decode_bytes = []
+    for i in range(args.eager_calls):
+        c, j = i % copies, i % n_sets
+        gu, dn, sgu, sdn = weights[c]
+        r = m.moe_route_topk(lg[j], k, bs[j], out=routes[j])
+        starts[i].record(stream)
+        m.moe_nvfp4_decode(xs[j], r, gu, dn, sgu, sdn, workspace=ws, out=outs[j])
+        ends[i].record(stream)
+        decode_bytes.append(n_act[j] * expert_bytes(H, I) + (expert_bytes(H, I) if shared else 0)
+                            + M * H * 4 + M * k * 8 + (E + 1 + E + 1) * 4 + M * k * 4)
+    torch.cuda.synchronize()
+    dec_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])[20:]
+    dec_bytes = float(np.mean(decode_bytes[20:]))
+    dec_avg_ms = float(dec_ms.mean())
+    achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+
+    # eager step rate (host launch included), for context
+    torch.cuda.synchronize()
+    e0 = time.time()
+    for i in range(args.eager_calls):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.time() - e0) * 1e3 / args.eager_calls
+
+    outs_ok = all(torch.isfinite(o.float()).all().item() for o in outs)
+
+    record = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "M": M, "E": E, "top_k": k, "hidden": H,
+                   "expert_inter": I, "weights": "nvfp4 e2m1 + e4m3/16 + f32",
+                   "accumulate": "f32", "shared_expert": shared, "logit_bias": bias,
+                   "weight_copies": copies, "logit_sets": n_sets, "graph_steps": S,
+                   "timing": "hip graph replay, events"},
+        "rows_per_s": round(rows_per_s, 1),
+        "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "bytes_per_step": round(mean_bytes),
+        "touched_experts_mean": float(np.mean(n_act)),
+        "eager_ms_per_step": round(eager_ms, 4),
+        "roofline": {"bound": "hbm", "kernel": "moe_nvfp4_decode",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(dec_avg_ms * 1e3, 3),
+                     "bytes_per_launch": round(dec_bytes)},
+        "outputs_finite": outs_ok, "setup_s": round(setup_s, 1), "wall_s": round(wall, 3),
+    }
+    if not outs_ok or gbs <= 0 or not np.isfinite(gbs):
+        print(json.dumps(record), flush=True)
+        print("bench: invalid result", file=sys.stderr)
+        return 1
+
+    if not args.no_cpu_baseline:
+        record["cpu_baseline"] = cpu_baseline(layers_host, logit_sets, x_host, copies, n_sets,
+                                              args.cpu_seconds, shared, bias)
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+def cpu_baseline(layers_host, logit_sets, x_host, copies, n_sets, budget_s, shared, bias):
+    """The oracle, single-threaded, on the first steps of the same sequence
+    (weight copy i % copies, logits/x set i % n_sets) until the time budget."""
+    import oracle
+    done, t0, nbytes = 0, time.time(), 0
+    while True:
+        c, j = done % copies, done % n_sets
+        if c >= len(layers_host):
+            break
+        lay = layers_host[c]
+        L = logit_sets[j]
+        ids, w, out = oracle.moe_decode(x_host[j], L.logits, lay.k, lay.gate_up, lay.down,
+                                        bias=L.bias, shared_gate_up=lay.shared_gate_up,
+                                        shared_down=lay.shared_down)
+        nbytes += step_bytes(lay.M, lay.E, lay.k, lay.H, lay.I, len(np.unique(ids)), shared,
+                             bias)
+        done += 1
+        if time.time() - t0 >= budget_s:
+            break
+    el = time.time() - t0
+    M = layers_host[0].M
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "rows_per_s": round(M * done / el, 3), "seconds": round(el, 2),
+            "sample": f"{done} decode steps (route + expert FFNs + combine, float64) of the "
+                      f"same workload, single thread"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

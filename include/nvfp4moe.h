@@ -143,19 +143,26 @@ typedef struct moe_nvfp4_args {
   int64_t M, E, k, H, I;
 } moe_nvfp4_args;
 
-/* Workspace bytes for moe_nvfp4_decode: FP32 h rows [M*k (+M)][I], FP32
- * expert outputs [M*k (+M)][H] and per-tile counters. Its contents need no
- * initialisation and are overwritten by every call. */
+/* Workspace bytes for moe_nvfp4_decode: a control block of counters, FP32 h
+ * rows [M*k (+M)][I] and FP32 expert outputs [M*k (+M)][H].
+ * The workspace must be ZERO-FILLED ONCE before its first use; every call
+ * leaves the control block at zero again when it completes, so it can be
+ * reused (and replayed inside a HIP graph) without clearing. A workspace
+ * serves one call at a time: calls that may overlap (different streams) need
+ * their own. Word 2 of the workspace is a sticky error flag that a call sets
+ * if one of its internal dependency waits ever exceeds its bound (the call
+ * still completes; its output is then not valid). */
 int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, int64_t I,
                                   int32_t has_shared);
 
 /* out[m] = bf16_rne( sum_j w[m][j] * y_{ids[m][j]}(x[m]) + y_shared(x[m]) + residual[m] ),
  * y_e(x) = W_dn,e ( silu(u[0:I]) * u[I:2I] ),  u = W_gu,e x,  silu(a) = a / (1 + e^-a),
  * with FP32 accumulation and FP32 h. The slot sum runs in j order, then the
- * shared term, then the residual. Extra support-set conditions: H and I are
- * each 32 * 2^j <= 2048, and I is a multiple of 16384 / H (gate and up
- * halves start on a tile boundary). Returns NVFP4MOE_ERR_WORKSPACE if the
- * workspace is too small. */
+ * shared term, then the residual; the result is bit-reproducible from run to
+ * run (no floating-point atomics). One kernel launch. Extra support-set
+ * conditions: H and I are each 32 * 2^j in [256, 2048], and I is a multiple
+ * of 16384 / H (gate and up halves start on a tile boundary). Returns
+ * NVFP4MOE_ERR_WORKSPACE if the workspace is too small. */
 int32_t moe_nvfp4_decode(const moe_nvfp4_args* args, hipStream_t stream);
 
 #ifdef __cplusplus

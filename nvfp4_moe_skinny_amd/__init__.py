@@ -211,6 +211,18 @@ def moe_nvfp4_workspace_bytes(M: int, E: int, k: int, H: int, I: int, has_shared
     return int(n)
 
 
+def moe_workspace(M: int, E: int, k: int, H: int, I: int, has_shared: bool,
+                  device) -> torch.Tensor:
+    """A zero-filled workspace (the library keeps its control block at zero)."""
+    return torch.zeros(moe_nvfp4_workspace_bytes(M, E, k, H, I, has_shared), dtype=torch.uint8,
+                       device=device)
+
+
+def workspace_error_flag(workspace: torch.Tensor) -> int:
+    """Sticky flag (word 2) set if a dependency wait inside a call hit its bound."""
+    return int(workspace[8:12].view(torch.int32).item())
+
+
 def moe_nvfp4_decode(x: torch.Tensor, routing: Routing, w_gate_up: PackedNVFP4,
                      w_down: PackedNVFP4, shared_gate_up: Optional[PackedNVFP4] = None,
                      shared_down: Optional[PackedNVFP4] = None,
@@ -227,8 +239,7 @@ def moe_nvfp4_decode(x: torch.Tensor, routing: Routing, w_gate_up: PackedNVFP4,
         raise ValueError("expert weight shapes do not match x")
     has_shared = shared_gate_up is not None
     if workspace is None:
-        workspace = torch.empty(moe_nvfp4_workspace_bytes(M, E, k, H, I, has_shared),
-                                dtype=torch.uint8, device=x.device)
+        workspace = moe_workspace(M, E, k, H, I, has_shared, x.device)
     if out is None:
         out = torch.empty_like(x)
     a = MoeArgs()

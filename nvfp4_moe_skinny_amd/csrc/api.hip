@@ -77,38 +77,47 @@ struct GemmLaunch {
   }
 };
 
-template <int L>
-struct GateUpLaunch {
-  static int32_t run(const MoeParams& p, int blocks, hipStream_t s) {
-    hipLaunchKernelGGL(moe_gate_up_kernel<L>, dim3(blocks), dim3(256), 0, s, p);
-    return launched("moe_nvfp4_decode gate_up");
-  }
-};
+template <int LH, int LI, int RMAX>
+int32_t launch_decode(const MoeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((moe_decode_kernel<LH, LI, RMAX>), dim3(p.total_blocks), dim3(128), 0, s, p);
+  return launched("moe_nvfp4_decode");
+}
 
-template <int L>
-struct DownLaunch {
-  static int32_t run(const MoeParams& p, int blocks, hipStream_t s) {
-    hipLaunchKernelGGL(moe_down_combine_kernel<L>, dim3(blocks), dim3(256), 0, s, p);
-    return launched("moe_nvfp4_decode down");
+template <int LH, int LI>
+int32_t launch_decode_rows(const MoeParams& p, int rmax, hipStream_t s) {
+  switch (rmax) {
+    case 1: return launch_decode<LH, LI, 1>(p, s);
+    case 2: return launch_decode<LH, LI, 2>(p, s);
+    case 4: return launch_decode<LH, LI, 4>(p, s);
+    default: return launch_decode<LH, LI, 8>(p, s);
   }
-};
+}
 
 struct WsLayout {
-  int64_t h_off, y_off, cnt_off, total;
+  int64_t ctl_off, cnt_gu_off, cnt_dn_off, h_off, y_off, total;
 };
 
 int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
 
-WsLayout ws_layout(int64_t M, int64_t k, int64_t H, int64_t I, bool shared) {
+// [control words | per-slot counters | per-group counters] (zero between
+// launches), then h [P][I] and y [P][H] in FP32, P = M*k (+ M with a shared expert).
+WsLayout ws_layout(int64_t M, int64_t E, int64_t k, int64_t H, int64_t I, bool shared) {
   const int64_t P = M * k + (shared ? M : 0);
+  const int64_t slots = (E < M * k ? E : M * k) + (shared ? 1 : 0);
+  const int64_t groups = (tiles_per_matrix(H, I) + 1) / 2;
   WsLayout w;
-  w.h_off = 0;
-  w.y_off = align256(P * I * 4);
-  w.cnt_off = w.y_off + align256(P * H * 4);
-  const int64_t groups = (tiles_per_matrix(H, I) + 3) / 4;
-  w.total = w.cnt_off + align256(groups * 4);
+  w.ctl_off = 0;
+  w.cnt_gu_off = 16;
+  w.cnt_dn_off = w.cnt_gu_off + slots * 4;
+  w.h_off = align256(w.cnt_dn_off + groups * 4);
+  w.y_off = w.h_off + align256(P * I * 4);
+  w.total = w.y_off + align256(P * H * 4);
   return w;
 }
+
+int rows_per_batch(int64_t M) { return M == 1 ? 1 : (M <= 16 ? 2 : (M <= 64 ? 4 : 8)); }
+
+bool valid_moe_dim(int64_t v) { return valid_k(v) && v >= 256; }
 
 }  // namespace
 
@@ -204,10 +213,10 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
                                   int32_t has_shared) {
   if (M < 1 || E < 1 || k < 1 || H < 1 || I < 1)
     return fail(NVFP4MOE_ERR_BAD_SHAPE, "sizes must be >= 1");
-  if (!valid_k(H) || !valid_k(I))
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be 32 * 2^j <= 2048");
+  if (!valid_moe_dim(H) || !valid_moe_dim(I))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be 32 * 2^j in [256, 2048]");
   ok();
-  return ws_layout(M, k, H, I, has_shared != 0).total;
+  return ws_layout(M, E, k, H, I, has_shared != 0).total;
 }
 
 int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
@@ -222,14 +231,14 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
     return fail(NVFP4MOE_ERR_BAD_SHAPE, "M, E, k, H, I must be >= 1");
   if (E > kRouteMaxE || k > kRouteMaxK || k > E)
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "need E <= 256 and k <= min(8, E)");
-  if (!valid_k(H) || !valid_k(I))
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be 32 * 2^j <= 2048");
+  if (!valid_moe_dim(H) || !valid_moe_dim(I))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be 32 * 2^j in [256, 2048]");
   if (I % rows_per_tile(H) != 0)
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "I = %lld must be a multiple of 16384 / H = %lld",
                 (long long)I, (long long)rows_per_tile(H));
-  if (M * k + M > (int64_t)1 << 30) return fail(NVFP4MOE_ERR_UNSUPPORTED, "M too large");
+  if (M * k + M > (int64_t)1 << 24) return fail(NVFP4MOE_ERR_UNSUPPORTED, "M too large");
   const bool shared = a->shared_gate_up != nullptr;
-  const WsLayout ws = ws_layout(M, k, H, I, shared);
+  const WsLayout ws = ws_layout(M, E, k, H, I, shared);
   if (a->workspace_bytes < ws.total)
     return fail(NVFP4MOE_ERR_WORKSPACE, "workspace %lld < %lld bytes",
                 (long long)a->workspace_bytes, (long long)ws.total);
@@ -254,16 +263,21 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
   p.residual = a->residual;
   p.out = a->out;
   uint8_t* wsb = (uint8_t*)a->workspace;
+  p.ctl = (uint32_t*)(wsb + ws.ctl_off);
+  p.cnt_gu = (uint32_t*)(wsb + ws.cnt_gu_off);
+  p.cnt_dn = (uint32_t*)(wsb + ws.cnt_dn_off);
   p.h = (float*)(wsb + ws.h_off);
   p.y = (float*)(wsb + ws.y_off);
-  p.counters = (uint32_t*)(wsb + ws.cnt_off);
   p.M = (int)M;
   p.E = (int)E;
   p.k = (int)k;
   p.H = (int)H;
   p.I = (int)I;
+  p.LH = (int)(H / 32);
+  p.LI = (int)(I / 32);
   p.routed_slots = (int)(E < M * k ? E : M * k);
   p.has_shared = shared ? 1 : 0;
+  p.slots = p.routed_slots + p.has_shared;
   p.gu_mat_bytes = matrix_bytes(2 * I, H);
   p.dn_mat_bytes = matrix_bytes(H, I);
   p.gu_g = (const float*)(p.gu + gscale_offset(E, 2 * I, H));
@@ -272,14 +286,16 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
     p.sgu_g = (const float*)(p.sgu + gscale_offset(1, 2 * I, H));
     p.sdn_g = (const float*)(p.sdn + gscale_offset(1, H, I));
   }
-  p.gu_tiles_per_half = (int)(I / rows_per_tile(H));
-  p.gu_blocks_per_slot = (p.gu_tiles_per_half + 3) / 4;
+  p.gu_pairs = (int)(I / rows_per_tile(H));
   p.dn_tiles = (int)tiles_per_matrix(H, I);
-  p.dn_groups = (p.dn_tiles + 3) / 4;
-  const int slots = p.routed_slots + p.has_shared;
-  int32_t st = dispatch_l<GateUpLaunch>(H / 32, p, slots * p.gu_blocks_per_slot, stream);
-  if (st != NVFP4MOE_OK) return st;
-  return dispatch_l<DownLaunch>(I / 32, p, slots * p.dn_groups, stream);
+  p.dn_groups = (p.dn_tiles + 1) / 2;
+  p.gu_items = p.slots * p.gu_pairs;
+  p.dn_items = p.slots * p.dn_groups;
+  p.total_blocks = p.gu_items + p.dn_items;
+  p.spin_limit = 1u << 22;
+  const int rmax = rows_per_batch(M);
+  if (H == 2048 && I == 512) return launch_decode_rows<64, 16>(p, rmax, stream);
+  return launch_decode_rows<0, 0>(p, rmax, stream);
 }
 
 }  // extern "C"

@@ -45,7 +45,9 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const uint16_t* __rest
   TileRegs T;
   load_tile(w + tile * kTileBytes, lane, T);
   const int col0 = 32 * (lane % L);
+#pragma unroll 1
   for (int64_t m0 = 0; m0 < M; m0 += 8) {
+    opaque_tile(T);
     const int rows = (int)((M - m0) < 8 ? (M - m0) : 8);
     if (rows > 4)
       gemm_rows<L, 8>(T, x, K, m0, rows, col0, lane, tile, N, g, y);

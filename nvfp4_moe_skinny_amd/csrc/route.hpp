@@ -1,10 +1,11 @@
 // route.hpp - top-k routing and grouping of (row, slot) pairs by expert.
 //
-// Selection is exact: every logit becomes a 64-bit key whose high word is an
-// order-preserving image of the FP32 value (-0 folded onto +0, NaN below
-// -inf) and whose low word favours the lower expert index, so a wave-wide
-// integer max picks the same expert as a stable sort would. k rounds of that
-// max give the k experts in order; the weights are the softmax over them.
+// Selection is exact: every logit becomes a 32-bit key, an order-preserving
+// image of the FP32 value (-0 folded onto +0, NaN below -inf). Each of k
+// rounds takes the wave-wide maximum key and, among lanes holding it, the
+// lowest expert index, so the k experts come out in the order a stable sort
+// by (logit descending, index ascending) gives. The weights are the softmax
+// over the selected logits.
 // Grouping is a stable counting sort: a pair's place inside its expert's run
 // is the number of earlier pairs routed to the same expert.
 #pragma once
@@ -18,41 +19,62 @@ constexpr int kRouteMaxK = 8;
 constexpr int kRouteWaves = 16;          // 1024 threads
 constexpr int kRouteSingleBlockRows = 64;  // rows routed and grouped in one launch
 
-__device__ __forceinline__ uint64_t route_key(float l, int e) {
+// Order-preserving image of an FP32 logit: larger logit -> larger key; -0
+// and +0 map together; NaN maps to 1, below -inf (0x007FFFFF); 0 marks an
+// empty or already-selected slot.
+__device__ __forceinline__ uint32_t route_ord(float l) {
   uint32_t b = __float_as_uint(l);
-  if (b == 0x80000000u) b = 0u;  // -0 ties with +0
-  uint32_t ord;
-  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu))
-    ord = 0u;  // NaN: below every number, -inf included
-  else
-    ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)ord << 32) | (uint32_t)(0xFFFF - e);
+  if (b == 0x80000000u) b = 0u;
+  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu)) return 1u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
+// DPP controls (gfx9 encoding)
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, int ctrl) {
+  switch (ctrl) {
+    case kDppQuadXor1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor1, 0xF, 0xF, false);
+    case kDppQuadXor2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor2, 0xF, 0xF, false);
+    case kDppRowRor4: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor4, 0xF, 0xF, false);
+    default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor8, 0xF, 0xF, false);
   }
-  return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
+// Maximum over the wave, returned uniform: DPP within each 16-lane row, then
+// the four row results through readlane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32(v, kDppQuadXor1));
+  v = max(v, dpp_u32(v, kDppQuadXor2));
+  v = max(v, dpp_u32(v, kDppRowRor4));
+  v = max(v, dpp_u32(v, kDppRowRor8));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Sum of lanes 0..15 (the others may hold anything), returned uniform.
+__device__ __forceinline__ float row0_sum(float v) {
+  v += __uint_as_float(dpp_u32(__float_as_uint(v), kDppQuadXor1));
+  v += __uint_as_float(dpp_u32(__float_as_uint(v), kDppQuadXor2));
+  v += __uint_as_float(dpp_u32(__float_as_uint(v), kDppRowRor4));
+  v += __uint_as_float(dpp_u32(__float_as_uint(v), kDppRowRor8));
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
 }
 
 // Routes one row with one wave: ids and weights to global memory and to
-// ids_lds (if not null).
+// ids_lds (if not null). Each round takes the largest remaining key; among
+// equal keys the ballots pick the lowest expert index (e = lane + 64 s).
 __device__ __forceinline__ void route_row(const float* __restrict__ logits,
                                           const float* __restrict__ bias, int E, int k, int row,
                                           int lane, float* lp, int32_t* __restrict__ ids,
                                           float* __restrict__ w, int32_t* ids_lds) {
-  uint64_t key[4];
+  uint32_t ord[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int e = lane + 64 * s;
@@ -60,29 +82,31 @@ __device__ __forceinline__ void route_row(const float* __restrict__ logits,
       float l = logits[(int64_t)row * E + e];
       if (bias) l = l + bias[e];
       lp[e] = l;
-      key[s] = route_key(l, e);
+      ord[s] = route_ord(l);
     } else {
-      key[s] = 0;  // below every real key, NaN ones included
+      ord[s] = 0u;
     }
   }
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    const uint32_t best = wave_max_u32(max(max(ord[0], ord[1]), max(ord[2], ord[3])));
+    int e = 0;
 #pragma unroll
-    for (int s = 1; s < 4; ++s) best = key[s] > best ? key[s] : best;
-    best = wave_max_u64(best);
-    const int e = 0xFFFF - (int)(uint32_t)(best & 0xFFFFu);
+    for (int s = 3; s >= 0; --s) {
+      const uint64_t b = __ballot(ord[s] == best);
+      if (b) e = 64 * s + (int)__builtin_ctzll(b);
+    }
     if (lane == (e & 63)) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        if (s == (e >> 6)) key[s] = 0;
+        if (s == (e >> 6)) ord[s] = 0u;
     }
     if (lane == j) my_id = e;
   }
   __builtin_amdgcn_wave_barrier();
-  const float top = lp[__shfl(my_id, 0, 64)];
+  const float top = lp[__builtin_amdgcn_readfirstlane(my_id)];
   const float ex = lane < k ? expf(lp[my_id] - top) : 0.0f;
-  const float z = wave_sum(ex);
+  const float z = row0_sum(ex);
   if (lane < k) {
     ids[(int64_t)row * k + lane] = my_id;
     w[(int64_t)row * k + lane] = ex / z;

@@ -26,6 +26,18 @@ __device__ __forceinline__ void load_tile(const uint8_t* tile, int lane, TileReg
   t.scales = load_stream(reinterpret_cast<const uint4*>(tile + kTileCodeBytes) + lane);
 }
 
+// Makes the tile registers opaque to the optimiser (no instruction is
+// emitted). Called at the top of every row batch, it stops the compiler from
+// hoisting the decode of the whole tile out of the batch loop, which would
+// keep 128-256 decoded values live and spill.
+__device__ __forceinline__ void opaque_tile(TileRegs& t) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    asm volatile("" : "+v"(t.codes[i].x), "+v"(t.codes[i].y), "+v"(t.codes[i].z),
+                 "+v"(t.codes[i].w));
+  asm volatile("" : "+v"(t.scales.x), "+v"(t.scales.y), "+v"(t.scales.z), "+v"(t.scales.w));
+}
+
 // part[r][i] = sum over the lane's 32 columns of slab i of W * x_r (no g).
 // x[r] holds the row's 32 BF16 values of the lane's columns as 4 x uint4.
 template <int R>
@@ -51,6 +63,8 @@ __device__ __forceinline__ void tile_dot_bf16(const TileRegs& t, const uint4 (&x
                                              false);
       part[r][i] = a0 * s0 + a1 * s1;
     }
+    // keep each slab's decode next to its use (no hoisting of all decodes)
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -80,6 +94,7 @@ __device__ __forceinline__ void tile_dot_f32(const TileRegs& t, const float (&h)
       }
       part[r][i] = a0 * s0 + a1 * s1;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

@@ -96,10 +96,13 @@ def test_decode_validation(m):
     assert dec(_args(m, H=3000)) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert dec(_args(m, I=100)) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert dec(_args(m, H=2048, I=4)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert dec(_args(m, H=128, I=256)) == m.NVFP4MOE_ERR_UNSUPPORTED  # below 256
+    assert dec(_args(m, H=256, I=128)) == m.NVFP4MOE_ERR_UNSUPPORTED
     need = m.moe_nvfp4_workspace_bytes(4, 256, 8, 2048, 512, False)
     assert dec(_args(m, workspace_bytes=need - 1)) == m.NVFP4MOE_ERR_WORKSPACE
     assert "workspace" in m.last_error_detail()
     assert dec(_args(m, x=4096 + 8)) == m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned
     # h [M*k][I] + y [M*k][H] FP32 + counters
     assert need >= 4 * 8 * (512 + 2048) * 4
+    assert need <= 4 * 8 * (512 + 2048) * 4 + 4096
     assert m.moe_nvfp4_workspace_bytes(4, 256, 8, 2048, 512, True) > need

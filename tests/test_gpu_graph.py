@@ -1,0 +1,58 @@
+"""HIP-graph capture of the decode step (route + MoE decode): every replay must
+reproduce the eager outputs bit for bit, with eager work and synchronisation
+between replays, and the workspace control block must stay at zero."""
+import numpy as np
+import pytest
+import torch
+
+from synth.workloads import moe_layer
+from tests.helpers import upload_layer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m(gpu):
+    import nvfp4_moe_skinny_amd as m
+    return m
+
+
+@pytest.mark.parametrize("M,shared", [(4, False), (16, True)])
+def test_graph_replay_matches_eager(m, gpu, M, shared):
+    lays = [moe_layer(seed=s, wl=400, layer=s, M=M, E_=64, H_=2048, I_=512, k=8, bias=shared,
+                      shared=shared) for s in range(3)]
+    devs = [upload_layer(l, gpu, m) for l in lays]
+    ws = m.moe_workspace(M, 64, 8, 2048, 512, shared, gpu)
+    routes = [m.routing_buffers(M, 64, 8, gpu) for _ in lays]
+    outs = [torch.empty((M, 2048), dtype=torch.bfloat16, device=gpu) for _ in lays]
+
+    def step(i):
+        d = devs[i]
+        r = m.moe_route_topk(d["logits"], 8, d["bias"], out=routes[i])
+        m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=d["x"],
+                           workspace=ws, out=outs[i])
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(3):
+                step(i)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, o in zip(eager, outs):
+            assert torch.equal(e.view(torch.int16), o.view(torch.int16)), rep
+        step(rep % 3)  # eager work between replays
+        torch.cuda.synchronize()
+    assert m.workspace_error_flag(ws) == 0
+    assert int(ws[:256].count_nonzero().item()) == 0

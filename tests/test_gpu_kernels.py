@@ -130,10 +130,12 @@ def _run_block(m, gpu, lay, residual=None):
 
 
 @pytest.mark.parametrize("M,E,H,I,k,shared,resid", [
-    (1, 16, 256, 64, 4, False, False), (3, 16, 256, 64, 4, True, False),
-    (8, 16, 256, 64, 4, False, True), (17, 16, 256, 64, 4, True, True),
-    (5, 8, 512, 64, 8, True, False), (2, 32, 1024, 128, 2, False, True),
-    (6, 4, 2048, 512, 1, True, True), (11, 256, 128, 128, 8, False, False)])
+    (1, 16, 256, 256, 4, False, False), (3, 16, 256, 256, 4, True, False),
+    (8, 16, 256, 512, 4, False, True), (17, 16, 512, 256, 4, True, True),
+    (5, 8, 512, 512, 8, True, False), (2, 32, 1024, 256, 2, False, True),
+    (6, 4, 2048, 512, 1, True, True), (11, 256, 256, 256, 8, False, False),
+    (70, 64, 2048, 512, 8, True, True), (33, 40, 1024, 1024, 3, False, False),
+    (4, 256, 2048, 2048, 8, False, False), (16, 8, 2048, 256, 8, True, False)])
 def test_moe_block_small(m, gpu, M, E, H, I, k, shared, resid):
     lay = moe_layer(seed=M + E, wl=200, M=M, E_=E, H_=H, I_=I, k=k, shared=shared)
     residual = synth.normal_bf16(synth.key(5, 201, M), (M, H)) if resid else None
@@ -145,11 +147,19 @@ def test_moe_block_small(m, gpu, M, E, H, I, k, shared, resid):
     assert tol_ratio(out, ref) <= 1.0
 
 
-def test_moe_block_deterministic(m, gpu):
-    lay = moe_layer(seed=3, wl=202, M=16, E_=32, H_=512, I_=128, k=8, shared=True)
+def test_moe_block_deterministic_and_workspace_reuse(m, gpu):
+    """Repeated calls on one workspace give bit-identical outputs and leave its
+    control block at zero with no wait timeouts flagged."""
+    lay = moe_layer(seed=3, wl=202, M=16, E_=32, H_=512, I_=256, k=8, shared=True)
     d = upload_layer(lay, gpu, m)
     r = m.moe_route_topk(d["logits"], lay.k)
-    a = m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"])
-    b = m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"])
+    ws = m.moe_workspace(16, 32, 8, 512, 256, True, gpu)
+    a = m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"], workspace=ws)
+    outs = [m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"], workspace=ws)
+            for _ in range(5)]
     torch.cuda.synchronize()
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for b in outs:
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert m.workspace_error_flag(ws) == 0
+    assert int(ws[:256].count_nonzero().item()) == 0
+
