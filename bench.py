@@ -63,7 +63,23 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager-calls", type=int, default=400)
+    p.add_argument("--calibrate-copy-mb", type=int, default=0,
+                   help="only run a plain device copy of this many MB (counter calibration)")
     return p.parse_args()
+
+
+def calibrate_copy(mb):
+    """A plain device-to-device copy of known size: reading FETCH_SIZE and
+    WRITE_SIZE for it under rocprofv3 gives the counters' scale factor."""
+    import torch
+    n = mb * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n, "copies": 5}), flush=True)
+    return 0
 
 
 def main():
@@ -72,6 +88,8 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path runs on one GPU's share; see DESIGN.md for sharding)", file=sys.stderr)
         return 2
+    if args.calibrate_copy_mb:
+        return calibrate_copy(args.calibrate_copy_mb)
     import torch
 
     import nvfp4_moe_skinny_amd as m

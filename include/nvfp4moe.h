@@ -114,13 +114,16 @@ int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w
  *   counts[E]      pairs per expert
  *   offsets[E+1]   exclusive prefix sum of counts
  *   pairs[M*k]     for experts in ascending order, their p ascending
- *   active[E]      experts with counts > 0 in ascending order, then -1
- *   n_active[1]    number of such experts
+ *   active[E]      experts with counts > 0 in ascending order ("slots"), then -1
+ *   active_offsets[E+1]  where each slot's run starts in pairs:
+ *                  offsets[active[s]] for s < n_active, M*k from there on
+ *   n_active[1]    number of slots
  * All outputs are device memory and are never read back, so the call can be
  * captured. logits [M][E] FP32, bias [E] FP32. */
 int32_t moe_route_topk(const float* logits, const float* bias, int64_t M, int64_t E, int64_t k,
                        int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* pairs,
-                       int32_t* active, int32_t* n_active, hipStream_t stream);
+                       int32_t* active, int32_t* active_offsets, int32_t* n_active,
+                       hipStream_t stream);
 
 /* ---- MoE block -------------------------------------------------------------------------- */
 
@@ -131,6 +134,7 @@ typedef struct moe_nvfp4_args {
   const int32_t* offsets;     /* [E+1]    from moe_route_topk */
   const int32_t* pairs;       /* [M*k]    from moe_route_topk */
   const int32_t* active;      /* [E]      from moe_route_topk */
+  const int32_t* active_offsets; /* [E+1] from moe_route_topk */
   const int32_t* n_active;    /* [1]      from moe_route_topk */
   const void* w_gate_up;      /* packed G = E, N = 2I, K = H; rows 0..I-1 gate, I..2I-1 up */
   const void* w_down;         /* packed G = E, N = H, K = I */
@@ -143,11 +147,12 @@ typedef struct moe_nvfp4_args {
   int64_t M, E, k, H, I;
 } moe_nvfp4_args;
 
-/* Workspace bytes for moe_nvfp4_decode: a control block of counters, FP32 h
- * rows [M*k (+M)][I] and FP32 expert outputs [M*k (+M)][H].
+/* Workspace bytes for moe_nvfp4_decode: a control block of counters, then h
+ * rows [M*k (+M)][I] and expert outputs [M*k (+M)][H] as 64-bit (FP32 value,
+ * ready flag) words.
  * The workspace must be ZERO-FILLED ONCE before its first use; every call
- * leaves the control block at zero again when it completes, so it can be
- * reused (and replayed inside a HIP graph) without clearing. A workspace
+ * leaves all of it at zero again when it completes, so it can be reused (and
+ * replayed inside a HIP graph) without clearing. A workspace
  * serves one call at a time: calls that may overlap (different streams) need
  * their own. Word 2 of the workspace is a sticky error flag that a call sets
  * if one of its internal dependency waits ever exceeds its bound (the call

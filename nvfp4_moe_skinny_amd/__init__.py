@@ -38,7 +38,8 @@ class MoeArgs(ctypes.Structure):
     """Mirror of struct moe_nvfp4_args."""
     _fields_ = [
         ("x", _vp), ("ids", _vp), ("w", _vp), ("offsets", _vp), ("pairs", _vp),
-        ("active", _vp), ("n_active", _vp), ("w_gate_up", _vp), ("w_down", _vp),
+        ("active", _vp), ("active_offsets", _vp), ("n_active", _vp), ("w_gate_up", _vp),
+        ("w_down", _vp),
         ("shared_gate_up", _vp), ("shared_down", _vp), ("residual", _vp), ("out", _vp),
         ("workspace", _vp), ("workspace_bytes", _i64),
         ("M", _i64), ("E", _i64), ("k", _i64), ("H", _i64), ("I", _i64),
@@ -65,7 +66,7 @@ def _load():
     L.nvfp4_skinny_gemm.restype = _i32
     L.nvfp4_skinny_gemm.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _vp]
     L.moe_route_topk.restype = _i32
-    L.moe_route_topk.argtypes = [_vp, _vp, _i64, _i64, _i64] + [_vp] * 8
+    L.moe_route_topk.argtypes = [_vp, _vp, _i64, _i64, _i64] + [_vp] * 9
     L.moe_nvfp4_workspace_bytes.restype = _i64
     L.moe_nvfp4_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32]
     L.moe_nvfp4_decode.restype = _i32
@@ -178,6 +179,7 @@ class Routing:
     offsets: torch.Tensor   # int32 [E+1]
     pairs: torch.Tensor     # int32 [M*k]
     active: torch.Tensor    # int32 [E]
+    active_offsets: torch.Tensor  # int32 [E+1]
     n_active: torch.Tensor  # int32 [1]
 
 
@@ -186,7 +188,7 @@ def routing_buffers(M: int, E: int, k: int, device) -> Routing:
     return Routing(torch.empty((M, k), **i32), torch.empty((M, k), dtype=torch.float32,
                                                            device=device),
                    torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(M * k, **i32),
-                   torch.empty(E, **i32), torch.empty(1, **i32))
+                   torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(1, **i32))
 
 
 def moe_route_topk(logits: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None,
@@ -198,7 +200,8 @@ def moe_route_topk(logits: torch.Tensor, k: int, bias: Optional[torch.Tensor] = 
     r = routing_buffers(M, E, k, logits.device) if out is None else out
     _check(lib.moe_route_topk(_ptr(logits), _ptr(bias), M, E, k, _ptr(r.ids), _ptr(r.w),
                               _ptr(r.counts), _ptr(r.offsets), _ptr(r.pairs), _ptr(r.active),
-                              _ptr(r.n_active), _stream(stream)), "moe_route_topk")
+                              _ptr(r.active_offsets), _ptr(r.n_active), _stream(stream)),
+           "moe_route_topk")
     return r
 
 
@@ -246,6 +249,7 @@ def moe_nvfp4_decode(x: torch.Tensor, routing: Routing, w_gate_up: PackedNVFP4,
     a.x, a.ids, a.w = _ptr(x), _ptr(routing.ids), _ptr(routing.w)
     a.offsets, a.pairs = _ptr(routing.offsets), _ptr(routing.pairs)
     a.active, a.n_active = _ptr(routing.active), _ptr(routing.n_active)
+    a.active_offsets = _ptr(routing.active_offsets)
     a.w_gate_up, a.w_down = _ptr(w_gate_up.data), _ptr(w_down.data)
     a.shared_gate_up = _ptr(shared_gate_up.data) if has_shared else None
     a.shared_down = _ptr(shared_down.data) if has_shared else None

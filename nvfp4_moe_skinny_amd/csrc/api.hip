@@ -79,7 +79,8 @@ struct GemmLaunch {
 
 template <int LH, int LI, int RMAX>
 int32_t launch_decode(const MoeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((moe_decode_kernel<LH, LI, RMAX>), dim3(p.total_blocks), dim3(128), 0, s, p);
+  const size_t lds = (size_t)RMAX * p.I * sizeof(float);
+  hipLaunchKernelGGL((moe_decode_kernel<LH, LI, RMAX>), dim3(p.total_blocks), dim3(64), lds, s, p);
   return launched("moe_nvfp4_decode");
 }
 
@@ -94,28 +95,31 @@ int32_t launch_decode_rows(const MoeParams& p, int rmax, hipStream_t s) {
 }
 
 struct WsLayout {
-  int64_t ctl_off, cnt_gu_off, cnt_dn_off, h_off, y_off, total;
+  int64_t ctl_off, cnt_ds_off, cnt_dn_off, h_off, y_off, total;
 };
 
 int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
 
-// [control words | per-slot counters | per-group counters] (zero between
-// launches), then h [P][I] and y [P][H] in FP32, P = M*k (+ M with a shared expert).
+// [control words | per-slot counters | per-output-tile counters] (one
+// 128-byte line per counter), then h [P][I] and y [P][H] as 64-bit (value,
+// ready) words, P = M*k (+ M with a shared expert). All of it is zero between
+// launches.
 WsLayout ws_layout(int64_t M, int64_t E, int64_t k, int64_t H, int64_t I, bool shared) {
   const int64_t P = M * k + (shared ? M : 0);
   const int64_t slots = (E < M * k ? E : M * k) + (shared ? 1 : 0);
-  const int64_t groups = (tiles_per_matrix(H, I) + 1) / 2;
+  const int64_t tiles = tiles_per_matrix(H, I);
+  const int64_t line = 4 * kCounterStride;
   WsLayout w;
   w.ctl_off = 0;
-  w.cnt_gu_off = 16;
-  w.cnt_dn_off = w.cnt_gu_off + slots * 4;
-  w.h_off = align256(w.cnt_dn_off + groups * 4);
-  w.y_off = w.h_off + align256(P * I * 4);
-  w.total = w.y_off + align256(P * H * 4);
+  w.cnt_ds_off = line;
+  w.cnt_dn_off = w.cnt_ds_off + slots * line;
+  w.h_off = align256(w.cnt_dn_off + tiles * line);
+  w.y_off = w.h_off + align256(P * I * 8);
+  w.total = w.y_off + align256(P * H * 8);
   return w;
 }
 
-int rows_per_batch(int64_t M) { return M == 1 ? 1 : (M <= 16 ? 2 : (M <= 64 ? 4 : 8)); }
+int rows_per_batch(int64_t M) { return M <= 4 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8)); }
 
 bool valid_moe_dim(int64_t v) { return valid_k(v) && v >= 256; }
 
@@ -185,8 +189,10 @@ int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w
 
 int32_t moe_route_topk(const float* logits, const float* bias, int64_t M, int64_t E, int64_t k,
                        int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* pairs,
-                       int32_t* active, int32_t* n_active, hipStream_t stream) {
-  if (!logits || !ids || !w || !counts || !offsets || !pairs || !active || !n_active)
+                       int32_t* active, int32_t* active_offsets, int32_t* n_active,
+                       hipStream_t stream) {
+  if (!logits || !ids || !w || !counts || !offsets || !pairs || !active || !active_offsets ||
+      !n_active)
     return fail(NVFP4MOE_ERR_NULL_ARG, "moe_route_topk: null");
   if (M < 1 || E < 1 || k < 1) return fail(NVFP4MOE_ERR_BAD_SHAPE, "M, E, k must be >= 1");
   if (E > kRouteMaxE) return fail(NVFP4MOE_ERR_UNSUPPORTED, "E = %lld > 256", (long long)E);
@@ -197,7 +203,8 @@ int32_t moe_route_topk(const float* logits, const float* bias, int64_t M, int64_
                 kGroupMaxPairs);
   if (M <= kRouteSingleBlockRows) {
     hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(1024), 0, stream, logits, bias, (int)M,
-                       (int)E, (int)k, ids, w, counts, offsets, pairs, active, n_active);
+                       (int)E, (int)k, ids, w, counts, offsets, pairs, active, active_offsets,
+                       n_active);
     return launched("moe_route_topk");
   }
   hipLaunchKernelGGL(route_rows_kernel, dim3(grid_for(M, kRouteWaves, 1 << 20)), dim3(1024), 0,
@@ -205,7 +212,7 @@ int32_t moe_route_topk(const float* logits, const float* bias, int64_t M, int64_
   const int32_t st = launched("moe_route_topk rows");
   if (st != NVFP4MOE_OK) return st;
   hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, ids, (int)M, (int)E, (int)k,
-                     counts, offsets, pairs, active, n_active);
+                     counts, offsets, pairs, active, active_offsets, n_active);
   return launched("moe_route_topk group");
 }
 
@@ -221,7 +228,8 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
 
 int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
   if (!a) return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_decode: args is null");
-  if (!a->x || !a->w || !a->offsets || !a->pairs || !a->active || !a->n_active ||
+  if (!a->x || !a->w || !a->offsets || !a->pairs || !a->active || !a->active_offsets ||
+      !a->n_active ||
       !a->w_gate_up || !a->w_down || !a->out || !a->workspace)
     return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_decode: a required pointer is null");
   if ((a->shared_gate_up == nullptr) != (a->shared_down == nullptr))
@@ -255,6 +263,7 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
   p.offsets = a->offsets;
   p.pairs = a->pairs;
   p.active = a->active;
+  p.active_offsets = a->active_offsets;
   p.n_active = a->n_active;
   p.gu = (const uint8_t*)a->w_gate_up;
   p.dn = (const uint8_t*)a->w_down;
@@ -264,10 +273,10 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
   p.out = a->out;
   uint8_t* wsb = (uint8_t*)a->workspace;
   p.ctl = (uint32_t*)(wsb + ws.ctl_off);
-  p.cnt_gu = (uint32_t*)(wsb + ws.cnt_gu_off);
+  p.cnt_ds = (uint32_t*)(wsb + ws.cnt_ds_off);
   p.cnt_dn = (uint32_t*)(wsb + ws.cnt_dn_off);
-  p.h = (float*)(wsb + ws.h_off);
-  p.y = (float*)(wsb + ws.y_off);
+  p.h = (uint64_t*)(wsb + ws.h_off);
+  p.y = (uint64_t*)(wsb + ws.y_off);
   p.M = (int)M;
   p.E = (int)E;
   p.k = (int)k;
@@ -286,14 +295,11 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
     p.sgu_g = (const float*)(p.sgu + gscale_offset(1, 2 * I, H));
     p.sdn_g = (const float*)(p.sdn + gscale_offset(1, H, I));
   }
-  p.gu_pairs = (int)(I / rows_per_tile(H));
-  p.dn_tiles = (int)tiles_per_matrix(H, I);
-  p.dn_groups = (p.dn_tiles + 1) / 2;
-  p.gu_items = p.slots * p.gu_pairs;
-  p.dn_items = p.slots * p.dn_groups;
-  p.total_blocks = p.gu_items + p.dn_items;
+  p.P = (int)(I / rows_per_tile(H));  // == tiles_per_matrix(H, I) == H * I / 16384
+  p.total_blocks = (p.slots + 1) * p.P;
   p.spin_limit = 1u << 22;
-  const int rmax = rows_per_batch(M);
+  int rmax = rows_per_batch(M);
+  while (rmax > 1 && (int64_t)rmax * I * 4 > 48 * 1024) rmax /= 2;  // LDS for staged h rows
   if (H == 2048 && I == 512) return launch_decode_rows<64, 16>(p, rmax, stream);
   return launch_decode_rows<0, 0>(p, rmax, stream);
 }

@@ -139,6 +139,7 @@ __device__ __forceinline__ void group_pairs(const int32_t* ids_lds, int P, int E
                                             int32_t* __restrict__ offsets,
                                             int32_t* __restrict__ pairs,
                                             int32_t* __restrict__ active,
+                                            int32_t* __restrict__ active_offsets,
                                             int32_t* __restrict__ n_active) {
   const int tid = threadIdx.x;
   for (int e = tid; e < kRouteMaxE; e += blockDim.x) counts_lds[e] = 0;
@@ -162,12 +163,19 @@ __device__ __forceinline__ void group_pairs(const int32_t* ids_lds, int P, int E
       if (e < E) {
         counts[e] = c[j];
         offsets[e] = cex[j];
-        if (f[j]) active[fex[j]] = e;  // active slots [0, ftot)
-        if (e >= ftot) active[e] = -1;  // unused slots [ftot, E)
+        if (f[j]) {  // active slots [0, ftot)
+          active[fex[j]] = e;
+          active_offsets[fex[j]] = cex[j];
+        }
+        if (e >= ftot) {  // unused slots [ftot, E)
+          active[e] = -1;
+          active_offsets[e] = ctot;
+        }
       }
     }
     if (lane == 0) {
       offsets[E] = ctot;
+      active_offsets[E] = ctot;
       *n_active = ftot;
     }
   }
@@ -186,7 +194,7 @@ __global__ void __launch_bounds__(1024) route_group_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int M, int E, int k,
     int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ pairs, int32_t* __restrict__ active,
-    int32_t* __restrict__ n_active) {
+    int32_t* __restrict__ active_offsets, int32_t* __restrict__ n_active) {
   __shared__ float lp[kRouteWaves][kRouteMaxE];
   __shared__ int32_t ids_lds[kRouteSingleBlockRows * kRouteMaxK];
   __shared__ int counts_lds[kRouteMaxE];
@@ -195,7 +203,8 @@ __global__ void __launch_bounds__(1024) route_group_kernel(
   for (int row = wave; row < M; row += kRouteWaves)
     route_row(logits, bias, E, k, row, lane, lp[wave], ids, w, ids_lds);
   __syncthreads();
-  group_pairs(ids_lds, M * k, E, counts_lds, offs_lds, counts, offsets, pairs, active, n_active);
+  group_pairs(ids_lds, M * k, E, counts_lds, offs_lds, counts, offsets, pairs, active,
+              active_offsets, n_active);
 }
 
 // Larger M, first launch: one wave per row.
@@ -216,6 +225,7 @@ __global__ void __launch_bounds__(1024) group_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ pairs,
                                                      int32_t* __restrict__ active,
+                                                     int32_t* __restrict__ active_offsets,
                                                      int32_t* __restrict__ n_active) {
   __shared__ int32_t ids_lds[kGroupMaxPairs];
   __shared__ int counts_lds[kRouteMaxE];
@@ -223,7 +233,8 @@ __global__ void __launch_bounds__(1024) group_kernel(const int32_t* __restrict__
   const int P = M * k;
   for (int p = threadIdx.x; p < P; p += blockDim.x) ids_lds[p] = ids[p];
   __syncthreads();
-  group_pairs(ids_lds, P, E, counts_lds, offs_lds, counts, offsets, pairs, active, n_active);
+  group_pairs(ids_lds, P, E, counts_lds, offs_lds, counts, offsets, pairs, active, active_offsets,
+              n_active);
 }
 
 }  // namespace nvfp4moe

@@ -38,7 +38,7 @@ def lib():
         L.oracle_route_topk.restype = ctypes.c_int
         L.oracle_route_topk.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp]
         L.oracle_group_by_expert.restype = None
-        L.oracle_group_by_expert.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_group_by_expert.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
         L.oracle_expert_ffn.restype = None
         L.oracle_expert_ffn.argtypes = [_vp, _i64, _i64, _vp, _vp, ctypes.c_float, _vp, _vp,
                                         ctypes.c_float, _vp]
@@ -121,10 +121,11 @@ def group_by_expert(ids, E):
     offsets = np.empty(E + 1, np.int32)
     pairs = np.empty(M * k, np.int32)
     active = np.empty(E, np.int32)
+    active_offsets = np.empty(E + 1, np.int32)
     na = np.zeros(1, np.int32)
     lib().oracle_group_by_expert(_p(ids), M, E, k, _p(counts), _p(offsets), _p(pairs),
-                                 _p(active), _p(na))
-    return counts, offsets, pairs, active, int(na[0])
+                                 _p(active), _p(active_offsets), _p(na))
+    return counts, offsets, pairs, active, active_offsets, int(na[0])
 
 
 def expert_ffn(x_row, gate_up, down):

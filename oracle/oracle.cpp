@@ -146,7 +146,7 @@ int oracle_route_topk(const float* logits, const float* bias, int64_t M, int64_t
 
 void oracle_group_by_expert(const int32_t* ids, int64_t M, int64_t E, int64_t k, int32_t* counts,
                             int32_t* offsets, int32_t* pairs, int32_t* active,
-                            int32_t* n_active) {
+                            int32_t* active_offsets, int32_t* n_active) {
   const int64_t P = M * k;
   for (int64_t e = 0; e < E; ++e) counts[e] = 0;
   for (int64_t p = 0; p < P; ++p) counts[ids[p]] += 1;
@@ -160,6 +160,7 @@ void oracle_group_by_expert(const int32_t* ids, int64_t M, int64_t E, int64_t k,
   for (int64_t e = 0; e < E; ++e)
     if (counts[e] > 0) active[na++] = (int32_t)e;
   for (int64_t s = na; s < E; ++s) active[s] = -1;
+  for (int64_t s = 0; s <= E; ++s) active_offsets[s] = s < na ? offsets[active[s]] : (int32_t)P;
   *n_active = na;
 }
 

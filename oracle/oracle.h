@@ -59,10 +59,11 @@ int oracle_route_topk(const float* logits, const float* bias, int64_t M, int64_t
 
 /* counts[E]; offsets[E+1] exclusive prefix sum; pairs[M*k]: for experts in
  * ascending order, the pair indices p = m*k + j with ids[p] == e, ascending;
- * active[E]: experts with counts > 0 ascending, then -1; *n_active. */
+ * active[E]: experts with counts > 0 ascending, then -1; active_offsets[E+1]:
+ * offsets[active[s]] for s < n_active, M*k from there on; *n_active. */
 void oracle_group_by_expert(const int32_t* ids, int64_t M, int64_t E, int64_t k, int32_t* counts,
                             int32_t* offsets, int32_t* pairs, int32_t* active,
-                            int32_t* n_active);
+                            int32_t* active_offsets, int32_t* n_active);
 
 /* y[H] = W_dn (silu(u[0:I]) * u[I:2I]),  u = W_gu x,  for one BF16 row x[H]. */
 void oracle_expert_ffn(const uint16_t* x, int64_t H, int64_t I, const uint8_t* gu_codes,

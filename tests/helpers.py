@@ -54,7 +54,7 @@ def upload_layer(lay, dev, m):
 
 def routing_to_np(r):
     return {k: getattr(r, k).cpu().numpy() for k in
-            ("ids", "w", "counts", "offsets", "pairs", "active", "n_active")}
+            ("ids", "w", "counts", "offsets", "pairs", "active", "active_offsets", "n_active")}
 
 
 def check_routing_exact(r, ids_ref, w_ref, E):
@@ -62,8 +62,9 @@ def check_routing_exact(r, ids_ref, w_ref, E):
     import oracle
     g = routing_to_np(r)
     assert (g["ids"] == ids_ref).all(), "routing ids differ"
-    counts, offsets, pairs, active, na = oracle.group_by_expert(ids_ref, E)
+    counts, offsets, pairs, active, active_offsets, na = oracle.group_by_expert(ids_ref, E)
     assert (g["counts"] == counts).all()
+    assert (g["active_offsets"] == active_offsets).all()
     assert (g["offsets"] == offsets).all()
     assert (g["pairs"] == pairs).all()
     assert (g["active"] == active).all()

@@ -61,7 +61,7 @@ def test_validation_errors_before_launch(m):
     assert L.nvfp4_skinny_gemm(fake, 1, 4096, fake, 8, fake, None) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert L.nvfp4_skinny_gemm(fake + 2, 1, 64, fake, 8, fake, None) == \
         m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned x
-    r = [fake] * 7
+    r = [fake] * 8
     assert L.moe_route_topk(None, None, 4, 256, 8, *r, None) == m.NVFP4MOE_ERR_NULL_ARG
     assert L.moe_route_topk(fake, None, 4, 257, 8, *r, None) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert L.moe_route_topk(fake, None, 4, 256, 9, *r, None) == m.NVFP4MOE_ERR_UNSUPPORTED
@@ -74,8 +74,8 @@ def test_validation_errors_before_launch(m):
 def _args(m, **kw):
     a = m.MoeArgs()
     fake = 4096
-    for f in ("x", "ids", "w", "offsets", "pairs", "active", "n_active", "w_gate_up", "w_down",
-              "out", "workspace"):
+    for f in ("x", "ids", "w", "offsets", "pairs", "active", "active_offsets", "n_active",
+              "w_gate_up", "w_down", "out", "workspace"):
         setattr(a, f, fake)
     a.workspace_bytes = 1 << 30
     a.M, a.E, a.k, a.H, a.I = 4, 256, 8, 2048, 512
@@ -102,7 +102,8 @@ def test_decode_validation(m):
     assert dec(_args(m, workspace_bytes=need - 1)) == m.NVFP4MOE_ERR_WORKSPACE
     assert "workspace" in m.last_error_detail()
     assert dec(_args(m, x=4096 + 8)) == m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned
-    # h [M*k][I] + y [M*k][H] FP32 + counters
-    assert need >= 4 * 8 * (512 + 2048) * 4
-    assert need <= 4 * 8 * (512 + 2048) * 4 + 4096
+    # h [M*k][I] + y [M*k][H] as 8-byte (value, flag) words + counters
+    assert need >= 4 * 8 * (512 + 2048) * 8
+    # plus the control block: one 128-byte counter line per slot and per output tile
+    assert need <= 4 * 8 * (512 + 2048) * 8 + 128 * (1 + 32 + 64) + 512
     assert m.moe_nvfp4_workspace_bytes(4, 256, 8, 2048, 512, True) > need

@@ -260,7 +260,7 @@ def test_group_by_expert_matches_brute_counting_sort():
     for seed, (M, E, k) in enumerate([(4, 256, 8), (16, 256, 8), (256, 256, 8), (3, 5, 2)]):
         logits = synth.normal_f32(synth.key(seed, 12), (M, E))
         ids, _ = oracle.route_topk(logits, k)
-        counts, offsets, pairs, active, na = oracle.group_by_expert(ids, E)
+        counts, offsets, pairs, active, active_offsets, na = oracle.group_by_expert(ids, E)
         flat = ids.reshape(-1)
         assert (counts == np.bincount(flat, minlength=E)).all()
         assert offsets[0] == 0 and (np.diff(offsets) == counts).all()
@@ -274,6 +274,11 @@ def test_group_by_expert_matches_brute_counting_sort():
         assert na == int((counts > 0).sum())
         assert active[:na].tolist() == [e for e in range(E) if counts[e] > 0]
         assert (active[na:] == -1).all()
+        # per-slot run starts: slot s's pairs are pairs[active_offsets[s]:active_offsets[s+1]]
+        for s_ in range(na):
+            run = pairs[active_offsets[s_]:active_offsets[s_ + 1]]
+            assert len(run) == counts[active[s_]] and (flat[run] == active[s_]).all()
+        assert (active_offsets[na:] == M * k).all()
 
 
 # ---- expert FFN and MoE block ----------------------------------------------------------
