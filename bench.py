@@ -35,6 +35,30 @@ HBM_PEAK_GBS = 8000.0
 CPU_LAYERS = 12  # weight copies kept on the host for the CPU-baseline sample
 
 
+def kernel_source_hash():
+    """Hash of the decode kernel's sources, to tie recorded counters to the code."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("common.hpp", "tile.hpp", "moe.hpp"):
+        with open(os.path.join(ROOT, "nvfp4_moe_skinny_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch from the committed FETCH_SIZE/WRITE_SIZE
+    summary, or None once the kernel has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "moe_decode_m4_counters.md")
+    try:
+        fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                      if line.startswith(("traffic_bytes_per_launch: ", "source_hash: ")))
+    except OSError:
+        return None
+    if fields.get("source_hash", "").strip() != kernel_source_hash():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def expert_bytes(H, I):
     """Canonical NVFP4 bytes of one expert: gate_up [2I][H] + down [H][I]
     (codes + E4M3 scales + FP32 tensor scale)."""
@@ -230,7 +254,8 @@ def main():
         "eager_ms_per_step": round(eager_ms, 4),
         "roofline": {"bound": "hbm", "kernel": "moe_nvfp4_decode",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic() if args.workload == "m4" else None,
                      "avg_launch_us": round(dec_avg_ms * 1e3, 3),
                      "bytes_per_launch": round(dec_bytes)},
         "outputs_finite": outs_ok, "setup_s": round(setup_s, 1), "wall_s": round(wall, 3),
