@@ -297,6 +297,7 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
   }
   p.P = (int)(I / rows_per_tile(H));  // == tiles_per_matrix(H, I) == H * I / 16384
   p.total_blocks = (p.slots + 1) * p.P;
+  p.pair_regs = M * k <= 128 ? (int)((M * k + 63) / 64) : 0;
   p.spin_limit = 1u << 22;
   int rmax = rows_per_batch(M);
   while (rmax > 1 && (int64_t)rmax * I * 4 > 48 * 1024) rmax /= 2;  // LDS for staged h rows

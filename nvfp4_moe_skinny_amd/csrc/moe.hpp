@@ -73,6 +73,7 @@ struct MoeParams {
   int routed_slots, has_shared, slots;
   int P;               // tiles per gate half = tiles per down matrix = H * I / 16384
   int total_blocks;    // (slots + 1) * P
+  int pair_regs;       // ceil(M * k / 64) <= 2: pairs[] is held in registers; else 0
   uint32_t spin_limit;
 };
 
@@ -153,9 +154,33 @@ __device__ __forceinline__ bool slot_info(const MoeParams& p, int slot, SlotInfo
   return true;
 }
 
+// pairs[] in registers (entry q * 64 + l in v[q] of lane l) when M * k <= 128:
+// loaded in the same round trip as the slot's routing entries, so the first
+// activation rows can be requested before the weight tiles.
+struct PairCache {
+  int v[2];
+};
+
+__device__ __forceinline__ void load_pair_cache(const MoeParams& p, int lane, PairCache& c) {
+  const int n = p.M * p.k;
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    c.v[q] = (q < p.pair_regs && q * 64 + lane < n) ? p.pairs[q * 64 + lane] : 0;
+}
+
+// Reads another lane's register: call with every lane of the wave active (in
+// a branch, the source lane's value may not have been copied where it is read).
+__device__ __forceinline__ int cached_pair(const PairCache& c, int idx) {
+  idx = __builtin_amdgcn_readfirstlane(idx);
+  const int l = idx & 63;
+  return idx < 64 ? __builtin_amdgcn_readlane(c.v[0], l) : __builtin_amdgcn_readlane(c.v[1], l);
+}
+
 // Workspace row (pair index) and activation row of row r of a slot.
-__device__ __forceinline__ int slot_pair(const MoeParams& p, const SlotInfo& s, int r) {
-  return s.shared ? p.M * p.k + r : p.pairs[s.row_begin + r];
+__device__ __forceinline__ int slot_pair(const MoeParams& p, const SlotInfo& s, int r,
+                                         const PairCache& c) {
+  if (s.shared) return p.M * p.k + r;
+  return p.pair_regs ? cached_pair(c, s.row_begin + r) : p.pairs[s.row_begin + r];
 }
 __device__ __forceinline__ int pair_xrow(const MoeParams& p, int pair) {
   return pair >= p.M * p.k ? pair - p.M * p.k : pair / p.k;
@@ -204,18 +229,13 @@ __device__ __forceinline__ bool reduced_writer_rt(int lane, int L) {
 
 // ---- gate_up + SiLU * up ------------------------------------------------------------------
 
-template <int LC, int R>
-__device__ __forceinline__ void gate_up_batch(const MoeParams& p, const SlotInfo& s,
-                                              const TileRegs& TG, const TileRegs& TU, int r0,
-                                              int rows, int lane, int j, float g, int L) {
-  const int col0 = 32 * (lane % L);
-  int pr[R];
-  uint4 xr[R][4];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    pr[r] = r < rows ? slot_pair(p, s, r0 + r) : 0;
-    load_x_bf16(p.x, p.H, pair_xrow(p, pr[r]), r < rows, col0, xr[r]);
-  }
+// h for R rows whose activations xr / pair ids pr are loaded: gate tile, up
+// tile, h stores, then `after()` (the caller's hook, e.g. the next tile request).
+template <int LC, int R, class After>
+__device__ __forceinline__ void gate_up_rows(const MoeParams& p, const TileRegs& TG,
+                                             const TileRegs& TU, const uint4 (&xr)[R][4],
+                                             const int (&pr)[R], int rows, int lane, int j,
+                                             float g, int L, After after) {
   float ug[R], uu[R];
   {
     float part[R][8];
@@ -241,54 +261,94 @@ __device__ __forceinline__ void gate_up_batch(const MoeParams& p, const SlotInfo
     for (int r = 0; r < R; ++r)
       if (r < rows) publish(&p.h[(int64_t)pr[r] * p.I + i], silu(ug[r] * g) * (uu[r] * g));
   }
+  after();
 }
 
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// Pair ids and activation rows r0 .. r0 + R - 1 of a slot (rows past `rows` are zero).
+template <int R>
+__device__ __forceinline__ void load_rows(const MoeParams& p, const SlotInfo& s,
+                                          const PairCache& c, int r0, int rows, int col0,
+                                          int (&pr)[R], uint4 (&xr)[R][4]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    pr[r] = r < rows ? slot_pair(p, s, r0 + r, c) : 0;
+    load_x_bf16(p.x, p.H, pair_xrow(p, pr[r]), r < rows, col0, xr[r]);
+  }
+}
+
+template <int LC, int R>
+__device__ __forceinline__ void gate_up_batch(const MoeParams& p, const SlotInfo& s,
+                                              const PairCache& c, const TileRegs& TG,
+                                              const TileRegs& TU, int r0, int rows, int lane,
+                                              int j, float g, int L) {
+  int pr[R];
+  uint4 xr[R][4];
+  load_rows<R>(p, s, c, r0, rows, 32 * (lane % L), pr, xr);
+  gate_up_rows<LC, R>(p, TG, TU, xr, pr, rows, lane, j, g, L, NoHook{});
+}
+
+// Row batches from r0 on; the tile registers are made opaque per batch.
 template <int LC, int RMAX>
-__device__ __forceinline__ void gate_up_compute(const MoeParams& p, int slot, const SlotInfo& s,
-                                                int j, TileRegs& TG, TileRegs& TU, float g) {
+__device__ __forceinline__ void gate_up_compute(const MoeParams& p, const SlotInfo& s,
+                                                const PairCache& c, int r_begin, int j,
+                                                TileRegs& TG, TileRegs& TU, float g) {
   const int lane = threadIdx.x;
   const int L = LC ? LC : p.LH;
 #pragma unroll 1
-  for (int r0 = 0; r0 < s.rows; r0 += RMAX) {
+  for (int r0 = r_begin; r0 < s.rows; r0 += RMAX) {
     opaque_tile(TG);
     opaque_tile(TU);
     const int rows = (s.rows - r0) < RMAX ? (s.rows - r0) : RMAX;
     if (RMAX >= 8 && rows > 4)
-      gate_up_batch<LC, (RMAX >= 8 ? 8 : 1)>(p, s, TG, TU, r0, rows, lane, j, g, L);
+      gate_up_batch<LC, (RMAX >= 8 ? 8 : 1)>(p, s, c, TG, TU, r0, rows, lane, j, g, L);
     else if (RMAX >= 4 && rows > 2)
-      gate_up_batch<LC, (RMAX >= 4 ? 4 : 1)>(p, s, TG, TU, r0, rows, lane, j, g, L);
+      gate_up_batch<LC, (RMAX >= 4 ? 4 : 1)>(p, s, c, TG, TU, r0, rows, lane, j, g, L);
     else if (RMAX >= 2 && rows > 1)
-      gate_up_batch<LC, (RMAX >= 2 ? 2 : 1)>(p, s, TG, TU, r0, rows, lane, j, g, L);
+      gate_up_batch<LC, (RMAX >= 2 ? 2 : 1)>(p, s, c, TG, TU, r0, rows, lane, j, g, L);
     else
-      gate_up_batch<LC, 1>(p, s, TG, TU, r0, rows, lane, j, g, L);
+      gate_up_batch<LC, 1>(p, s, c, TG, TU, r0, rows, lane, j, g, L);
   }
 }
 
 // ---- down + combine ---------------------------------------------------------------------------
 
 template <int LC, int R>
-__device__ __forceinline__ void down_batch(const MoeParams& p, const SlotInfo& s, const TileRegs& T,
-                                           int r0, int rows, int lane, int tile, float g, int L,
+__device__ __forceinline__ void down_batch(const MoeParams& p, const SlotInfo& s,
+                                           const PairCache& c, const TileRegs& T, int r0,
+                                           int rows, int lane, int tile, float g, int L,
                                            float* s_h) {
-  // stage the batch's h rows in LDS, polling until every word is ready
+  // stage the batch's h rows in LDS: every row's words are loaded in one
+  // round trip and polled again only while some are not ready
   const int I = p.I;
   const int per_row = I / 64;  // words per lane per row
-  Poller poll;
+  int pr[R];
+  const uint64_t* src[R];
+#pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r >= rows) break;
-    const uint64_t* src = p.h + (int64_t)slot_pair(p, s, r0 + r) * I;
-    bool done = false;
-    while (!done) {
-      bool mine = true;
-      for (int q = 0; q < per_row; ++q) {
-        const int c = q * 64 + lane;
-        const uint64_t wd = load_word(src + c);
-        mine = mine && word_ready(wd);
-        s_h[r * I + c] = word_value(wd);
+    pr[r] = slot_pair(p, s, r0 + (r < rows ? r : 0), c);
+    src[r] = p.h + (int64_t)pr[r] * I;
+  }
+  Poller poll;
+  bool done = false;
+  while (!done) {
+    bool mine = true;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r < rows) {
+        for (int q = 0; q < per_row; ++q) {
+          const int c = q * 64 + lane;
+          const uint64_t wd = load_word(src[r] + c);
+          mine = mine && word_ready(wd);
+          s_h[r * I + c] = word_value(wd);
+        }
       }
-      done = __builtin_amdgcn_read_exec() == __ballot(mine);
-      if (!done && !poll.next(p)) break;
     }
+    done = __builtin_amdgcn_read_exec() == __ballot(mine);
+    if (!done && !poll.next(p)) break;
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS writes have landed
   __builtin_amdgcn_wave_barrier();
@@ -314,48 +374,76 @@ __device__ __forceinline__ void down_batch(const MoeParams& p, const SlotInfo& s
   if (reduced_writer_rt(lane, L) && n < p.H) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (r < rows) {
-        const int pr = slot_pair(p, s, r0 + r);
-        publish(&p.y[(int64_t)pr * p.H + n], part[r][0] * g);
-      }
+      if (r < rows) publish(&p.y[(int64_t)pr[r] * p.H + n], part[r][0] * g);
   }
   __builtin_amdgcn_wave_barrier();  // s_h is rewritten by the next batch
 }
 
-// y word of pair row `pr`, output n: polls until ready, then clears it (the
-// combining block is its only reader).
-__device__ __forceinline__ float take_y(const MoeParams& p, int pr, int n, Poller& poll) {
-  uint64_t* a = &p.y[(int64_t)pr * p.H + n];
-  uint64_t wd = load_word(a);
-  while (!word_ready(wd)) {
-    if (!poll.next(p)) break;
-    wd = load_word(a);
-  }
-  clear_word(a);
-  return word_value(wd);
-}
+// out rows of output tile t: sum over slots in j order, then shared, then
+// residual. A lane takes up to kCombineBatch outputs at a time and loads all
+// their y words, routing weights and residual values in one round trip; only
+// words not yet ready are polled again. The combining block is the y words'
+// only reader, so it clears them.
+constexpr int kMaxTerms = 9;  // k <= 8 routed slots + the shared expert
+constexpr int kCombineBatch = 4;
 
-// out rows of output tile t: sum over slots in j order, then shared, then residual.
 __device__ __forceinline__ void combine_tile(const MoeParams& p, int tile) {
   const int rpt = 16384 / p.I;
   const int n0 = tile * rpt;
   const int n1 = (n0 + rpt) < p.H ? (n0 + rpt) : p.H;
   const int nrows = n1 - n0;
+  const int terms = p.k + p.has_shared;
+  const int total = p.M * nrows;
   Poller poll;
-  for (int idx = threadIdx.x; idx < p.M * nrows; idx += 64) {
-    const int m = idx / nrows;
-    const int n = n0 + idx % nrows;
-    float acc = 0.0f;
-    for (int j = 0; j < p.k; ++j) acc += p.w[m * p.k + j] * take_y(p, m * p.k + j, n, poll);
-    if (p.has_shared) acc += take_y(p, p.M * p.k + m, n, poll);
-    if (p.residual) acc += bf16_to_f32(p.residual[(int64_t)m * p.H + n]);
-    p.out[(int64_t)m * p.H + n] = f32_to_bf16_rne(acc);
+  for (int base = 0; base < total; base += 64 * kCombineBatch) {
+    uint64_t wd[kCombineBatch][kMaxTerms];
+    float wt[kCombineBatch][kMaxTerms];
+    float res[kCombineBatch];
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      const int idx = base + b * 64 + (int)threadIdx.x;
+      const int m = idx / nrows, n = n0 + idx % nrows;
+      res[b] = (idx < total && p.residual) ? bf16_to_f32(p.residual[(int64_t)m * p.H + n]) : 0.0f;
+#pragma unroll
+      for (int t = 0; t < kMaxTerms; ++t) {
+        wd[b][t] = 0;
+        wt[b][t] = 0.0f;
+        if (idx < total && t < terms) {
+          const int pr = t < p.k ? m * p.k + t : p.M * p.k + m;
+          wd[b][t] = load_word(&p.y[(int64_t)pr * p.H + n]);
+          wt[b][t] = t < p.k ? p.w[m * p.k + t] : 1.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      const int idx = base + b * 64 + (int)threadIdx.x;
+      if (idx >= total) continue;
+      const int m = idx / nrows, n = n0 + idx % nrows;
+      float acc = 0.0f;
+#pragma unroll
+      for (int t = 0; t < kMaxTerms; ++t) {
+        if (t < terms) {
+          const int pr = t < p.k ? m * p.k + t : p.M * p.k + m;
+          uint64_t* a = &p.y[(int64_t)pr * p.H + n];
+          while (!word_ready(wd[b][t])) {
+            if (!poll.next(p)) break;
+            wd[b][t] = load_word(a);
+          }
+          clear_word(a);
+          acc += wt[b][t] * word_value(wd[b][t]);  // routed slots in j order, then shared
+        }
+      }
+      if (p.residual) acc += res[b];
+      p.out[(int64_t)m * p.H + n] = f32_to_bf16_rne(acc);
+    }
   }
 }
 
 template <int LC, int RMAX>
 __device__ __forceinline__ void down_compute(const MoeParams& p, int slot, const SlotInfo& s,
-                                             int tile, TileRegs& T, float g, float* s_h) {
+                                             const PairCache& c, int tile, TileRegs& T, float g,
+                                             float* s_h) {
   const int lane = threadIdx.x;
   const int L = LC ? LC : p.LI;
 #pragma unroll 1
@@ -363,65 +451,121 @@ __device__ __forceinline__ void down_compute(const MoeParams& p, int slot, const
     opaque_tile(T);
     const int rows = (s.rows - r0) < RMAX ? (s.rows - r0) : RMAX;
     if (RMAX >= 8 && rows > 4)
-      down_batch<LC, (RMAX >= 8 ? 8 : 1)>(p, s, T, r0, rows, lane, tile, g, L, s_h);
+      down_batch<LC, (RMAX >= 8 ? 8 : 1)>(p, s, c, T, r0, rows, lane, tile, g, L, s_h);
     else if (RMAX >= 4 && rows > 2)
-      down_batch<LC, (RMAX >= 4 ? 4 : 1)>(p, s, T, r0, rows, lane, tile, g, L, s_h);
+      down_batch<LC, (RMAX >= 4 ? 4 : 1)>(p, s, c, T, r0, rows, lane, tile, g, L, s_h);
     else if (RMAX >= 2 && rows > 1)
-      down_batch<LC, (RMAX >= 2 ? 2 : 1)>(p, s, T, r0, rows, lane, tile, g, L, s_h);
+      down_batch<LC, (RMAX >= 2 ? 2 : 1)>(p, s, c, T, r0, rows, lane, tile, g, L, s_h);
     else
-      down_batch<LC, 1>(p, s, T, r0, rows, lane, tile, g, L, s_h);
+      down_batch<LC, 1>(p, s, c, T, r0, rows, lane, tile, g, L, s_h);
   }
-  // done reading the slot's h: the last reader clears the slot's h words
-  int last_reader = 0;
-  if (lane == 0)
-    last_reader = add_coherent(&p.cnt_ds[slot * kCounterStride], 1u) + 1u == (uint32_t)p.P;
-  if (__builtin_amdgcn_readfirstlane(last_reader)) {
-    for (int r = 0; r < s.rows; ++r) {
-      uint64_t* row = p.h + (int64_t)slot_pair(p, s, r) * p.I;
-      for (int c = lane; c < p.I; c += 64) clear_word(row + c);
-    }
-    if (lane == 0) store_coherent_u32(&p.cnt_ds[slot * kCounterStride], 0u);
-  }
-  // y is published; the last down item of the output tile combines it
-  int last = 0;
+  // y is published and the slot's h has been read: count both at once. The
+  // last down item of the output tile combines it; the last reader of the
+  // slot's h clears those words.
+  int last = 0, last_reader = 0;
   if (lane == 0) {
     const uint32_t participants = (uint32_t)(*p.n_active + p.has_shared);
-    last = add_coherent(&p.cnt_dn[tile * kCounterStride], 1u) + 1u == participants;
+    const uint32_t t_prev = add_coherent(&p.cnt_dn[tile * kCounterStride], 1u);
+    const uint32_t r_prev = add_coherent(&p.cnt_ds[slot * kCounterStride], 1u);
+    last = t_prev + 1u == participants;
+    last_reader = r_prev + 1u == (uint32_t)p.P;
     if (last) store_coherent_u32(&p.cnt_dn[tile * kCounterStride], 0u);
+    if (last_reader) store_coherent_u32(&p.cnt_ds[slot * kCounterStride], 0u);
   }
   if (__builtin_amdgcn_readfirstlane(last)) combine_tile(p, tile);
+  if (__builtin_amdgcn_readfirstlane(last_reader)) {
+    for (int r = 0; r < s.rows; ++r) {
+      uint64_t* row = p.h + (int64_t)slot_pair(p, s, r, c) * p.I;
+      for (int c = lane; c < p.I; c += 64) clear_word(row + c);
+    }
+  }
 }
 
 // ---- the kernel ----------------------------------------------------------------------------------
 
-// One wave per block; dynamic LDS: RMAX rows of h (RMAX * I floats). The
-// block reads both items' routing entries first, then issues all three
-// tiles (gate, up, down) before any compute, so the only dependent memory
-// round trip left on its path is the exchange of h.
+// Gate and up tiles in one interleaved request stream, scales first, so that
+// slab i of both tiles has arrived once the loads issued before it have.
+__device__ __forceinline__ void load_tile_pair(const uint8_t* a, const uint8_t* b, int lane,
+                                               TileRegs& ta, TileRegs& tb) {
+  ta.scales = load_stream(reinterpret_cast<const uint4*>(a + kTileCodeBytes) + lane);
+  tb.scales = load_stream(reinterpret_cast<const uint4*>(b + kTileCodeBytes) + lane);
+  const uint4* ca = reinterpret_cast<const uint4*>(a);
+  const uint4* cb = reinterpret_cast<const uint4*>(b);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ta.codes[i] = load_stream(ca + i * 64 + lane);
+    tb.codes[i] = load_stream(cb + i * 64 + lane);
+  }
+}
+
+struct IssueTile {
+  const uint8_t* tile;
+  TileRegs* t;
+  __device__ __forceinline__ void operator()() const {
+    if (tile) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(tile, threadIdx.x, *t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+// One wave per block; dynamic LDS: RMAX rows of h (RMAX * I floats).
+//   1. one round trip: both items' routing entries and (M * k <= 128) pairs[];
+//   2. the first gate_up batch's activation rows, then the gate and up tiles;
+//   3. slab i of each tile is multiplied as soon as it has arrived; h of the
+//      first batch is stored, and only then is the down tile requested: once
+//      the memory queues are full a request stalls its wave until there is
+//      room, which must not delay the h that other blocks wait for;
+//   4. further row batches; then the down item.
+// Blocks with at most two rows per batch take this path; wider batches load
+// their rows after the tiles.
 template <int LHC, int LIC, int RMAX>
 __global__ void __launch_bounds__(64) moe_decode_kernel(MoeParams p) {
   extern __shared__ float s_h[];
   const int lane = threadIdx.x;
   const int w = blockIdx.x;
   const int gslot = w / p.P, dslot = w / p.P - 1, j = w % p.P;
+  PairCache pc;
+  load_pair_cache(p, lane, pc);
   SlotInfo gs, ds;
   const bool has_gu = gslot < p.slots && slot_info(p, gslot, gs);
   const bool has_dn = dslot >= 0 && slot_info(p, dslot, ds);
   TileRegs TG, TU, TD;
-  float ggu = 0.0f, gdn = 0.0f;
-  if (has_gu) {
-    const uint8_t* mat = gs.shared ? p.sgu : p.gu + (int64_t)gs.e * p.gu_mat_bytes;
-    ggu = gs.shared ? p.sgu_g[0] : p.gu_g[gs.e];
-    load_tile(mat + (int64_t)j * kTileBytes, lane, TG);
-    load_tile(mat + (int64_t)(j + p.P) * kTileBytes, lane, TU);
-  }
+  float gdn = 0.0f;
+  const uint8_t* dtile = nullptr;
   if (has_dn) {
     const uint8_t* mat = ds.shared ? p.sdn : p.dn + (int64_t)ds.e * p.dn_mat_bytes;
     gdn = ds.shared ? p.sdn_g[0] : p.dn_g[ds.e];
-    load_tile(mat + (int64_t)j * kTileBytes, lane, TD);
+    dtile = mat + (int64_t)j * kTileBytes;
   }
-  if (has_gu) gate_up_compute<LHC, RMAX>(p, gslot, gs, j, TG, TU, ggu);
-  if (has_dn) down_compute<LIC, RMAX>(p, dslot, ds, j, TD, gdn, s_h);
+  if (has_gu) {
+    const uint8_t* mat = gs.shared ? p.sgu : p.gu + (int64_t)gs.e * p.gu_mat_bytes;
+    const float ggu = gs.shared ? p.sgu_g[0] : p.gu_g[gs.e];
+    const uint8_t* tg = mat + (int64_t)j * kTileBytes;
+    const uint8_t* tu = mat + (int64_t)(j + p.P) * kTileBytes;
+    if constexpr (RMAX <= 2) {
+      const int L = LHC ? LHC : p.LH;
+      const int rows0 = gs.rows < RMAX ? gs.rows : RMAX;
+      int pr[RMAX];
+      uint4 xr[RMAX][4];
+      load_rows<RMAX>(p, gs, pc, 0, rows0, 32 * (lane % L), pr, xr);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile_pair(tg, tu, lane, TG, TU);
+      __builtin_amdgcn_sched_barrier(0);
+      gate_up_rows<LHC, RMAX>(p, TG, TU, xr, pr, rows0, lane, j, ggu, L, IssueTile{dtile, &TD});
+      gate_up_compute<LHC, RMAX>(p, gs, pc, RMAX, j, TG, TU, ggu);
+    } else {
+      load_tile_pair(tg, tu, lane, TG, TU);
+      opaque_tile(TG);  // waits for the gate and up bytes before the down request
+      opaque_tile(TU);
+      IssueTile{dtile, &TD}();
+      gate_up_compute<LHC, RMAX>(p, gs, pc, 0, j, TG, TU, ggu);
+    }
+  } else if (has_dn) {
+    load_tile(dtile, lane, TD);
+  }
+  if (has_dn) down_compute<LIC, RMAX>(p, dslot, ds, pc, j, TD, gdn, s_h);
 }
 
 }  // namespace nvfp4moe
