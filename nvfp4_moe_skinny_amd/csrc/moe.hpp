@@ -321,9 +321,13 @@ __device__ __forceinline__ void down_batch(const MoeParams& p, const SlotInfo& s
                                            const PairCache& c, const TileRegs& T, int r0,
                                            int rows, int lane, int tile, float g, int L,
                                            float* s_h) {
-  // stage the batch's h rows in LDS: every row's words are loaded in one
-  // round trip and polled again only while some are not ready
+  // Stage the batch's h rows in LDS: every row's words are loaded in one
+  // round trip. While some are not ready the block polls only one word per
+  // gate_up item and row (an item stores its h segment of a row with one
+  // instruction), then loads the rows again: waiting blocks would otherwise
+  // re-read whole rows and crowd the memory system the weights stream through.
   const int I = p.I;
+  const int seg = 16384 / p.H;  // h words per gate_up item
   const int per_row = I / 64;  // words per lane per row
   int pr[R];
   const uint64_t* src[R];
@@ -333,8 +337,8 @@ __device__ __forceinline__ void down_batch(const MoeParams& p, const SlotInfo& s
     src[r] = p.h + (int64_t)pr[r] * I;
   }
   Poller poll;
-  bool done = false;
-  while (!done) {
+  bool waiting = true;
+  while (waiting) {
     bool mine = true;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -347,8 +351,20 @@ __device__ __forceinline__ void down_batch(const MoeParams& p, const SlotInfo& s
         }
       }
     }
-    done = __builtin_amdgcn_read_exec() == __ballot(mine);
-    if (!done && !poll.next(p)) break;
+    if (__ballot(!mine) == 0) break;
+    for (;;) {  // sentinel words until every item's has arrived
+      if (!poll.next(p)) {
+        waiting = false;
+        break;
+      }
+      bool seen = true;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (r < rows)
+          for (int it = lane; it < p.P; it += 64)
+            seen = seen && word_ready(load_word(src[r] + it * seg));
+      if (__ballot(!seen) == 0) break;
+    }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS writes have landed
   __builtin_amdgcn_wave_barrier();
@@ -415,27 +431,42 @@ __device__ __forceinline__ void combine_tile(const MoeParams& p, int tile) {
         }
       }
     }
+    // every load has returned before any store is issued: loads and stores
+    // share one counter, so a wait for a load issued after a store would
+    // also wait for that store's round trip
+    float acc[kCombineBatch];
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      const int idx = base + b * 64 + (int)threadIdx.x;
+      const int m = idx / nrows, n = n0 + idx % nrows;
+      acc[b] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < kMaxTerms; ++t) {
+        if (idx < total && t < terms) {
+          const int pr = t < p.k ? m * p.k + t : p.M * p.k + m;
+          const uint64_t* a = &p.y[(int64_t)pr * p.H + n];
+          while (!word_ready(wd[b][t])) {
+            if (!poll.next(p)) break;
+            wd[b][t] = load_word(a);
+          }
+          acc[b] += wt[b][t] * word_value(wd[b][t]);  // routed slots in j order, then shared
+        }
+      }
+      if (p.residual) acc[b] += res[b];
+    }
 #pragma unroll
     for (int b = 0; b < kCombineBatch; ++b) {
       const int idx = base + b * 64 + (int)threadIdx.x;
       if (idx >= total) continue;
       const int m = idx / nrows, n = n0 + idx % nrows;
-      float acc = 0.0f;
 #pragma unroll
       for (int t = 0; t < kMaxTerms; ++t) {
         if (t < terms) {
           const int pr = t < p.k ? m * p.k + t : p.M * p.k + m;
-          uint64_t* a = &p.y[(int64_t)pr * p.H + n];
-          while (!word_ready(wd[b][t])) {
-            if (!poll.next(p)) break;
-            wd[b][t] = load_word(a);
-          }
-          clear_word(a);
-          acc += wt[b][t] * word_value(wd[b][t]);  // routed slots in j order, then shared
+          clear_word(&p.y[(int64_t)pr * p.H + n]);
         }
       }
-      if (p.residual) acc += res[b];
-      p.out[(int64_t)m * p.H + n] = f32_to_bf16_rne(acc);
+      p.out[(int64_t)m * p.H + n] = f32_to_bf16_rne(acc[b]);
     }
   }
 }
@@ -514,10 +545,10 @@ struct IssueTile {
 //   1. one round trip: both items' routing entries and (M * k <= 128) pairs[];
 //   2. the first gate_up batch's activation rows, then the gate and up tiles;
 //   3. slab i of each tile is multiplied as soon as it has arrived; h of the
-//      first batch is stored, and only then is the down tile requested: once
-//      the memory queues are full a request stalls its wave until there is
-//      room, which must not delay the h that other blocks wait for;
-//   4. further row batches; then the down item.
+//      first batch is stored; further row batches;
+//   4. only then is the down tile requested (once the memory queues are full
+//      a request stalls its wave until there is room, which must not delay the
+//      h that other blocks wait for), and the down item runs.
 // Blocks with at most two rows per batch take this path; wider batches load
 // their rows after the tiles.
 template <int LHC, int LIC, int RMAX>
@@ -553,8 +584,9 @@ __global__ void __launch_bounds__(64) moe_decode_kernel(MoeParams p) {
       __builtin_amdgcn_sched_barrier(0);
       load_tile_pair(tg, tu, lane, TG, TU);
       __builtin_amdgcn_sched_barrier(0);
-      gate_up_rows<LHC, RMAX>(p, TG, TU, xr, pr, rows0, lane, j, ggu, L, IssueTile{dtile, &TD});
+      gate_up_rows<LHC, RMAX>(p, TG, TU, xr, pr, rows0, lane, j, ggu, L, NoHook{});
       gate_up_compute<LHC, RMAX>(p, gs, pc, RMAX, j, TG, TU, ggu);
+      IssueTile{dtile, &TD}();
     } else {
       load_tile_pair(tg, tu, lane, TG, TU);
       opaque_tile(TG);  // waits for the gate and up bytes before the down request
