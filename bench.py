@@ -82,7 +82,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20000)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--workload", default="m4", choices=["m4", "m16"])
+    p.add_argument("--workload", default="m4", choices=["m4", "m16", "m256"])
     p.add_argument("--copies", type=int, default=0, help="weight sets cycled (0: >= 1 GB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -121,17 +121,25 @@ def main():
     from tests.helpers import pack, to_dev_bf16
 
     dev = torch.device("cuda:0")
+    zipf = None
     if args.workload == "m4":
         make = lambda c: W.moe_layer(0, wl=2, layer=c, M=4)
         name = "moe_block_m4_e256_top8_h2048_i512"
-    else:
+        wl, touched = 2, 31
+    elif args.workload == "m16":
         make = lambda c: W.moe_layer(0, wl=3, layer=c, M=16, bias=True, shared=True)
         name = "moe_block_m16_e256_top8_h2048_i512_bias_shared"
+        wl, touched = 3, 84
+    else:
+        zipf = 1.1
+        make = lambda c: W.moe_layer(0, wl=5, layer=c, M=256, zipf_s=zipf)
+        name = "moe_block_m256_e256_top8_h2048_i512_zipf1.1"
+        wl, touched = 5, 229
     lay0 = make(0)
     M, E, k, H, I = lay0.M, lay0.E, lay0.k, lay0.H, lay0.I
     shared = lay0.shared_gate_up is not None
     bias = lay0.bias is not None
-    per_step_est = 31 * expert_bytes(H, I) if M == 4 else 84 * expert_bytes(H, I)
+    per_step_est = touched * expert_bytes(H, I)
     copies = args.copies or int(np.ceil(1e9 / per_step_est)) + 1
 
     # ---- resident inputs -------------------------------------------------------------
@@ -149,9 +157,8 @@ def main():
         torch.cuda.synchronize()
     # 64 router-logit / activation sets (small tensors: only the logits and x are used)
     n_sets = 64
-    wl = 2 if M == 4 else 3
-    logit_sets = [W.moe_layer(0, wl=wl, layer=1000 + i, M=M, E_=E, H_=32, I_=32, k=k, bias=bias)
-                  for i in range(n_sets)]
+    logit_sets = [W.moe_layer(0, wl=wl, layer=1000 + i, M=M, E_=E, H_=32, I_=32, k=k, bias=bias,
+                              zipf_s=zipf) for i in range(n_sets)]
     x_host = [W.normal_bf16(W.key(0, wl, 1000 + i, W.T_X, 1), (M, H)) for i in range(n_sets)]
     xs = [to_dev_bf16(xh, dev) for xh in x_host]
     lg = [torch.from_numpy(L.logits).to(dev) for L in logit_sets]

@@ -145,18 +145,23 @@ typedef struct moe_nvfp4_args {
   void* workspace;            /* device scratch, >= moe_nvfp4_workspace_bytes(...) */
   int64_t workspace_bytes;
   int64_t M, E, k, H, I;
+  int64_t dense_min_rows;     /* three-launch schedule: slots with at least this many rows
+                                 use BF16 MFMA (0 = library default, 16; above M = never) */
+  int32_t schedule;           /* 0 = library choice, 1 = one launch, 2 = three launches */
 } moe_nvfp4_args;
 
 /* Workspace bytes for moe_nvfp4_decode: a control block of counters, then h
  * rows [M*k (+M)][I] and expert outputs [M*k (+M)][H] as 64-bit (FP32 value,
- * ready flag) words.
+ * ready flag) words for the one-launch schedule, then the same rows as plain
+ * 32-bit words for the three-launch schedule.
  * The workspace must be ZERO-FILLED ONCE before its first use; every call
- * leaves all of it at zero again when it completes, so it can be reused (and
- * replayed inside a HIP graph) without clearing. A workspace
- * serves one call at a time: calls that may overlap (different streams) need
- * their own. Word 2 of the workspace is a sticky error flag that a call sets
- * if one of its internal dependency waits ever exceeds its bound (the call
- * still completes; its output is then not valid). */
+ * leaves the counters and the 64-bit words at zero again when it completes
+ * (the plain words are simply overwritten by the next three-launch call), so
+ * it can be reused (and replayed inside a HIP graph) without clearing. A
+ * workspace serves one call at a time: calls that may overlap (different
+ * streams) need their own. Word 2 of the workspace is a sticky error flag that
+ * a call sets if one of its internal dependency waits ever exceeds its bound
+ * (the call still completes; its output is then not valid). */
 int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, int64_t I,
                                   int32_t has_shared);
 
@@ -164,10 +169,17 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
  * y_e(x) = W_dn,e ( silu(u[0:I]) * u[I:2I] ),  u = W_gu,e x,  silu(a) = a / (1 + e^-a),
  * with FP32 accumulation and FP32 h. The slot sum runs in j order, then the
  * shared term, then the residual; the result is bit-reproducible from run to
- * run (no floating-point atomics). One kernel launch. Extra support-set
- * conditions: H and I are each 32 * 2^j in [256, 2048], and I is a multiple
- * of 16384 / H (gate and up halves start on a tile boundary). Returns
- * NVFP4MOE_ERR_WORKSPACE if the workspace is too small. */
+ * run (no floating-point atomics).
+ * Schedules: one launch (every tile item of gate_up and down in one grid,
+ * exchanging h and y through the workspace; chosen while all of its blocks
+ * fit on the GPU at once), or three launches (gate_up, down, combine; chosen
+ * for larger grids). In the three-launch schedule, when H = 2048 and I = 512,
+ * slots with at least dense_min_rows rows run on BF16 MFMA: weights exact in
+ * BF16, x as stored, h as a hi + lo BF16 pair (relative error <= 2^-17).
+ * Extra support-set conditions: H and I are each 32 * 2^j in [256, 2048], and
+ * I is a multiple of 16384 / H (gate and up halves start on a tile boundary).
+ * Returns NVFP4MOE_ERR_WORKSPACE if the workspace is too small and
+ * NVFP4MOE_ERR_BAD_SHAPE for a schedule other than 0, 1 or 2. */
 int32_t moe_nvfp4_decode(const moe_nvfp4_args* args, hipStream_t stream);
 
 #ifdef __cplusplus

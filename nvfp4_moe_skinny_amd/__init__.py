@@ -43,7 +43,11 @@ class MoeArgs(ctypes.Structure):
         ("shared_gate_up", _vp), ("shared_down", _vp), ("residual", _vp), ("out", _vp),
         ("workspace", _vp), ("workspace_bytes", _i64),
         ("M", _i64), ("E", _i64), ("k", _i64), ("H", _i64), ("I", _i64),
+        ("dense_min_rows", _i64), ("schedule", _i32),
     ]
+
+# moe_nvfp4_args.schedule
+SCHEDULE_AUTO, SCHEDULE_ONE_LAUNCH, SCHEDULE_THREE_LAUNCHES = 0, 1, 2
 
 
 def _load():
@@ -231,8 +235,11 @@ def moe_nvfp4_decode(x: torch.Tensor, routing: Routing, w_gate_up: PackedNVFP4,
                      shared_down: Optional[PackedNVFP4] = None,
                      residual: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None, stream=None,
-                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """x bfloat16 [M][H] -> bfloat16 [M][H] (routed experts + shared + residual)."""
+                     out: Optional[torch.Tensor] = None, schedule: int = SCHEDULE_AUTO,
+                     dense_min_rows: int = 0) -> torch.Tensor:
+    """x bfloat16 [M][H] -> bfloat16 [M][H] (routed experts + shared + residual).
+    schedule: SCHEDULE_AUTO / SCHEDULE_ONE_LAUNCH / SCHEDULE_THREE_LAUNCHES;
+    dense_min_rows: rows from which a slot uses MFMA (0 = library default)."""
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bfloat16")
     M, H = x.shape
@@ -257,5 +264,6 @@ def moe_nvfp4_decode(x: torch.Tensor, routing: Routing, w_gate_up: PackedNVFP4,
     a.out = _ptr(out)
     a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     a.M, a.E, a.k, a.H, a.I = M, E, k, H, I
+    a.dense_min_rows, a.schedule = dense_min_rows, schedule
     _check(lib.moe_nvfp4_decode(ctypes.byref(a), _stream(stream)), "moe_nvfp4_decode")
     return out

@@ -10,6 +10,7 @@
 
 #include "gemm.hpp"
 #include "moe.hpp"
+#include "staged.hpp"
 #include "pack.hpp"
 #include "route.hpp"
 
@@ -84,6 +85,26 @@ int32_t launch_decode(const MoeParams& p, hipStream_t s) {
   return launched("moe_nvfp4_decode");
 }
 
+template <int LH, int LI, int RMAX, bool DENSE>
+int32_t launch_staged(const MoeParams& p, hipStream_t s) {
+  const int grid = p.slots * p.P;
+  hipLaunchKernelGGL((staged_gate_kernel<LH, RMAX, DENSE>), dim3(grid), dim3(64), 0, s, p);
+  hipLaunchKernelGGL((staged_down_kernel<LI, RMAX, DENSE>), dim3(grid), dim3(64), 0, s, p);
+  const int64_t outs = (int64_t)p.M * p.H;
+  hipLaunchKernelGGL(staged_combine_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s,
+                     p);
+  return launched("moe_nvfp4_decode");
+}
+
+template <int LH, int LI, bool DENSE>
+int32_t launch_staged_rows(const MoeParams& p, int rmax, hipStream_t s) {
+  switch (rmax) {
+    case 1: return launch_staged<LH, LI, 1, DENSE>(p, s);
+    case 2: return launch_staged<LH, LI, 2, DENSE>(p, s);
+    default: return launch_staged<LH, LI, 4, DENSE>(p, s);
+  }
+}
+
 template <int LH, int LI>
 int32_t launch_decode_rows(const MoeParams& p, int rmax, hipStream_t s) {
   switch (rmax) {
@@ -95,15 +116,16 @@ int32_t launch_decode_rows(const MoeParams& p, int rmax, hipStream_t s) {
 }
 
 struct WsLayout {
-  int64_t ctl_off, cnt_ds_off, cnt_dn_off, h_off, y_off, total;
+  int64_t ctl_off, cnt_ds_off, cnt_dn_off, h_off, y_off, hp_off, yp_off, total;
 };
 
 int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
 
 // [control words | per-slot counters | per-output-tile counters] (one
 // 128-byte line per counter), then h [P][I] and y [P][H] as 64-bit (value,
-// ready) words, P = M*k (+ M with a shared expert). All of it is zero between
-// launches.
+// ready) words, P = M*k (+ M with a shared expert): all of it zero between
+// calls. Then h [P][I] and y [P][H] as plain 32-bit words for the three-launch
+// schedule (overwritten by every call that uses them).
 WsLayout ws_layout(int64_t M, int64_t E, int64_t k, int64_t H, int64_t I, bool shared) {
   const int64_t P = M * k + (shared ? M : 0);
   const int64_t slots = (E < M * k ? E : M * k) + (shared ? 1 : 0);
@@ -115,9 +137,15 @@ WsLayout ws_layout(int64_t M, int64_t E, int64_t k, int64_t H, int64_t I, bool s
   w.cnt_dn_off = w.cnt_ds_off + slots * line;
   w.h_off = align256(w.cnt_dn_off + tiles * line);
   w.y_off = w.h_off + align256(P * I * 8);
-  w.total = w.y_off + align256(P * H * 8);
+  w.hp_off = w.y_off + align256(P * H * 8);
+  w.yp_off = w.hp_off + align256(P * I * 4);
+  w.total = w.yp_off + align256(P * H * 4);
   return w;
 }
+
+// One-wave blocks resident at once at the one-launch kernel's register budget
+// (three waves per SIMD): 256 CUs x 4 SIMDs x 3.
+constexpr int64_t kResidentBlocks = 3072;
 
 int rows_per_batch(int64_t M) { return M <= 4 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8)); }
 
@@ -245,6 +273,8 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "I = %lld must be a multiple of 16384 / H = %lld",
                 (long long)I, (long long)rows_per_tile(H));
   if (M * k + M > (int64_t)1 << 24) return fail(NVFP4MOE_ERR_UNSUPPORTED, "M too large");
+  if (a->schedule < 0 || a->schedule > 2)
+    return fail(NVFP4MOE_ERR_BAD_SHAPE, "schedule must be 0, 1 or 2 (got %d)", (int)a->schedule);
   const bool shared = a->shared_gate_up != nullptr;
   const WsLayout ws = ws_layout(M, E, k, H, I, shared);
   if (a->workspace_bytes < ws.total)
@@ -298,6 +328,19 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
   p.P = (int)(I / rows_per_tile(H));  // == tiles_per_matrix(H, I) == H * I / 16384
   p.total_blocks = (p.slots + 1) * p.P;
   p.pair_regs = M * k <= 128 ? (int)((M * k + 63) / 64) : 0;
+  p.hp = (float*)(wsb + ws.hp_off);
+  p.yp = (float*)(wsb + ws.yp_off);
+  p.dense_min_rows = a->dense_min_rows > 0
+                         ? (int)(a->dense_min_rows < (int64_t)1 << 30 ? a->dense_min_rows : 1 << 30)
+                         : kDenseRowsDefault;
+  const bool specialised = H == 2048 && I == 512;
+  // one launch while all of its blocks can be resident at once, else three
+  const bool staged = a->schedule == 2 || (a->schedule == 0 && p.total_blocks > kResidentBlocks);
+  if (staged) {
+    const int rmax_s = rows_per_batch(M) < 4 ? rows_per_batch(M) : 4;
+    if (specialised) return launch_staged_rows<64, 16, true>(p, rmax_s, stream);
+    return launch_staged_rows<0, 0, false>(p, rmax_s, stream);
+  }
   p.spin_limit = 1u << 22;
   int rmax = rows_per_batch(M);
   while (rmax > 1 && (int64_t)rmax * I * 4 > 48 * 1024) rmax /= 2;  // LDS for staged h rows

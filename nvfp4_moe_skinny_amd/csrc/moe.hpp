@@ -74,6 +74,10 @@ struct MoeParams {
   int P;               // tiles per gate half = tiles per down matrix = H * I / 16384
   int total_blocks;    // (slots + 1) * P
   int pair_regs;       // ceil(M * k / 64) <= 2: pairs[] is held in registers; else 0
+  // three-launch schedule (staged.hpp)
+  float* hp;           // [P_tot][I] h words (FP32, or hi / lo BF16 for MFMA slots)
+  float* yp;           // [P_tot][H] expert outputs (FP32)
+  int dense_min_rows;  // slots with at least this many rows use MFMA
   uint32_t spin_limit;
 };
 

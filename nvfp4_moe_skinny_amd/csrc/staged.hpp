@@ -1,0 +1,314 @@
+// staged.hpp - the MoE decode step in three launches, for larger row counts:
+//   1. gate_up: one wave per (slot, gate tile j) writes h for the slot's rows;
+//   2. down:    one wave per (slot, down tile t) writes y for the slot's rows;
+//   3. combine: one thread per output, sum over slots in j order (+ shared)
+//               (+ residual), rounded once to BF16.
+// A launch starts after the previous one has finished, so h and y are plain
+// 32-bit words: nothing is polled, nothing needs clearing, and the repeated
+// reads of x and h (every tile item of a slot reads all of the slot's rows)
+// are served by the L2.
+//
+// Slots with at least dense_min_rows rows (and the shapes the dense code
+// covers: H = 2048, I = 512) use BF16 MFMA; their h words hold hi / lo BF16
+// halves (dense.hpp). Other slots use the VALU tile products of tile.hpp and
+// FP32 h words.
+#pragma once
+
+#include "dense.hpp"
+#include "moe.hpp"
+
+namespace nvfp4moe {
+
+// Pair index (row of h / y) of row r of a slot, per lane.
+__device__ __forceinline__ int lane_pair(const MoeParams& p, const SlotInfo& s, int r) {
+  return s.shared ? p.M * p.k + r : p.pairs[s.row_begin + r];
+}
+
+__device__ __forceinline__ const uint8_t* gate_matrix(const MoeParams& p, const SlotInfo& s) {
+  return s.shared ? p.sgu : p.gu + (int64_t)s.e * p.gu_mat_bytes;
+}
+__device__ __forceinline__ const uint8_t* down_matrix(const MoeParams& p, const SlotInfo& s) {
+  return s.shared ? p.sdn : p.dn + (int64_t)s.e * p.dn_mat_bytes;
+}
+
+// ---- gate_up ------------------------------------------------------------------------------
+
+// VALU: R rows at a time, h as FP32 words.
+template <int LC, int R>
+__device__ __forceinline__ void staged_gate_rows(const MoeParams& p, const SlotInfo& s,
+                                                 const PairCache& c, const TileRegs& TG,
+                                                 const TileRegs& TU, int r0, int rows, int j,
+                                                 float g, int L) {
+  const int lane = threadIdx.x;
+  int pr[R];
+  uint4 xr[R][4];
+  load_rows<R>(p, s, c, r0, rows, 32 * (lane % L), pr, xr);
+  float ug[R], uu[R];
+  {
+    float part[R][8];
+    tile_dot_bf16<R>(TG, xr, part);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      reduce_slabs_rt<LC>(part[r], lane, L);
+      ug[r] = part[r][0];
+    }
+  }
+  {
+    float part[R][8];
+    tile_dot_bf16<R>(TU, xr, part);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      reduce_slabs_rt<LC>(part[r], lane, L);
+      uu[r] = part[r][0];
+    }
+  }
+  if (reduced_writer_rt(lane, L)) {
+    const int i = j * (16384 / p.H) + reduced_row(lane, L);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < rows) p.hp[(int64_t)pr[r] * p.I + i] = silu(ug[r] * g) * (uu[r] * g);
+  }
+}
+
+// MFMA (H = 2048: a gate tile and an up tile hold 8 rows each, together one
+// 16-row block): h packed as hi / lo BF16 for the dense down product.
+template <int NCB>
+__device__ __forceinline__ void staged_gate_dense(const MoeParams& p, const SlotInfo& s,
+                                                  const uint8_t* tg, const uint8_t* tu, int j,
+                                                  float g) {
+  const int lane = threadIdx.x, m = lane & 15, grp = lane >> 4;
+  DenseRows<16> d;
+  {
+    const int n = m;  // 0-7 gate rows, 8-15 up rows
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      load_dense_chunk(n < 8 ? tg : tu, 64, n & 7, 4 * q + grp, d.c[q], d.s[q]);
+  }
+  uint32_t* hw = reinterpret_cast<uint32_t*>(p.hp);
+#pragma unroll 1
+  for (int cb0 = 0; cb0 < s.rows; cb0 += 16 * NCB) {
+    opaque_dense<16>(d);
+    int xrow[NCB], pr[NCB];
+#pragma unroll
+    for (int b = 0; b < NCB; ++b) {
+      const int r = cb0 + 16 * b + m;
+      pr[b] = r < s.rows ? lane_pair(p, s, r) : -1;
+      xrow[b] = pr[b] < 0 ? 0 : pair_xrow(p, pr[b]);
+    }
+    f32x4 acc[NCB];
+#pragma unroll
+    for (int b = 0; b < NCB; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      bf16x8 a[4];
+      dense_a<16>(d, q, a);
+#pragma unroll
+      for (int b = 0; b < NCB; ++b) {
+        uint4 xv[4];
+        load_x_bf16(p.x, p.H, xrow[b], pr[b] >= 0, 32 * (4 * q + grp), xv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[b] = mfma_bf16(a[e], as_bf16x8(xv[e]), acc[b]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one chunk column's loads in flight at a time
+    }
+    // D row 4 grp + r: gate rows 0-7 in lanes 0-31, the matching up rows in lanes 32-63
+#pragma unroll
+    for (int b = 0; b < NCB; ++b) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = acc[b][r];
+        const float u = xor_shuffle(v, 32);
+        if (lane < 32 && pr[b] >= 0) {
+          const int i = j * 8 + 4 * grp + r;
+          hw[(int64_t)pr[b] * p.I + i] = pack_hilo(silu(v * g) * (u * g));
+        }
+      }
+    }
+  }
+}
+
+template <int LHC, int RMAX, bool DENSE>
+__global__ void __launch_bounds__(64) staged_gate_kernel(MoeParams p) {
+  const int lane = threadIdx.x;
+  const int slot = blockIdx.x / p.P, j = blockIdx.x % p.P;
+  PairCache pc;
+  load_pair_cache(p, lane, pc);
+  SlotInfo s;
+  if (!slot_info(p, slot, s)) return;
+  const uint8_t* mat = gate_matrix(p, s);
+  const float g = s.shared ? p.sgu_g[0] : p.gu_g[s.e];
+  const uint8_t* tg = mat + (int64_t)j * kTileBytes;
+  const uint8_t* tu = mat + (int64_t)(j + p.P) * kTileBytes;
+  if constexpr (DENSE) {
+    if (s.rows >= p.dense_min_rows) {
+      staged_gate_dense<2>(p, s, tg, tu, j, g);
+      return;
+    }
+  }
+  const int L = LHC ? LHC : p.LH;
+  TileRegs TG, TU;
+  load_tile_pair(tg, tu, lane, TG, TU);
+#pragma unroll 1
+  for (int r0 = 0; r0 < s.rows; r0 += RMAX) {
+    opaque_tile(TG);
+    opaque_tile(TU);
+    const int rows = (s.rows - r0) < RMAX ? (s.rows - r0) : RMAX;
+    if (RMAX >= 8 && rows > 4)
+      staged_gate_rows<LHC, (RMAX >= 8 ? 8 : 1)>(p, s, pc, TG, TU, r0, rows, j, g, L);
+    else if (RMAX >= 4 && rows > 2)
+      staged_gate_rows<LHC, (RMAX >= 4 ? 4 : 1)>(p, s, pc, TG, TU, r0, rows, j, g, L);
+    else if (RMAX >= 2 && rows > 1)
+      staged_gate_rows<LHC, (RMAX >= 2 ? 2 : 1)>(p, s, pc, TG, TU, r0, rows, j, g, L);
+    else
+      staged_gate_rows<LHC, 1>(p, s, pc, TG, TU, r0, rows, j, g, L);
+  }
+}
+
+// ---- down ----------------------------------------------------------------------------------
+
+// VALU: R rows at a time from FP32 h, y as FP32 words.
+template <int LC, int R>
+__device__ __forceinline__ void staged_down_rows(const MoeParams& p, const SlotInfo& s,
+                                                 const PairCache& c, const TileRegs& T, int r0,
+                                                 int rows, int t, float g, int L) {
+  const int lane = threadIdx.x;
+  const int col0 = 32 * (lane % L);
+  int pr[R];
+  float hr[R][32];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    pr[r] = r < rows ? slot_pair(p, s, r0 + r, c) : 0;
+    load_h_f32(p.hp, p.I, pr[r], r < rows, col0, hr[r]);
+  }
+  float part[R][8];
+  tile_dot_f32<R>(T, hr, part);
+#pragma unroll
+  for (int r = 0; r < R; ++r) reduce_slabs_rt<LC>(part[r], lane, L);
+  const int n = t * (16384 / p.I) + reduced_row(lane, L);
+  if (reduced_writer_rt(lane, L) && n < p.H) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < rows) p.yp[(int64_t)pr[r] * p.H + n] = part[r][0] * g;
+  }
+}
+
+// MFMA (I = 512: a down tile holds 32 rows, two 16-row blocks; K = 512 is 4
+// chunk columns per lane group).
+template <int NCB>
+__device__ __forceinline__ void staged_down_dense(const MoeParams& p, const SlotInfo& s,
+                                                  const uint8_t* tile, int t, float g) {
+  const int lane = threadIdx.x, m = lane & 15, grp = lane >> 4;
+  DenseRows<4> d[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      load_dense_chunk(tile, 16, 16 * rb + m, 4 * q + grp, d[rb].c[q], d[rb].s[q]);
+  const uint32_t* hw = reinterpret_cast<const uint32_t*>(p.hp);
+#pragma unroll 1
+  for (int cb0 = 0; cb0 < s.rows; cb0 += 16 * NCB) {
+    opaque_dense<4>(d[0]);
+    opaque_dense<4>(d[1]);
+    int pr[NCB];
+#pragma unroll
+    for (int b = 0; b < NCB; ++b) {
+      const int r = cb0 + 16 * b + m;
+      pr[b] = r < s.rows ? lane_pair(p, s, r) : -1;
+    }
+    f32x4 acc[2][NCB];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int b = 0; b < NCB; ++b) acc[rb][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x8 a[2][4];
+      dense_a<4>(d[0], q, a[0]);
+      dense_a<4>(d[1], q, a[1]);
+#pragma unroll
+      for (int b = 0; b < NCB; ++b) {
+        // the lane's 32 h values of chunk column q: 8 words per operand pair
+        uint4 hv[8];
+        if (pr[b] >= 0) {
+          const uint4* src =
+              reinterpret_cast<const uint4*>(hw + (int64_t)pr[b] * p.I + 32 * (4 * q + grp));
+#pragma unroll
+          for (int v = 0; v < 8; ++v) hv[v] = src[v];
+        } else {
+#pragma unroll
+          for (int v = 0; v < 8; ++v) hv[v] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf16x8 hi, lo;
+          split_hilo(hv[2 * e], hv[2 * e + 1], hi, lo);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            acc[rb][b] = mfma_bf16(a[rb][e], hi, acc[rb][b]);
+            acc[rb][b] = mfma_bf16(a[rb][e], lo, acc[rb][b]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int b = 0; b < NCB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = t * 32 + 16 * rb + 4 * grp + r;
+          if (pr[b] >= 0 && n < p.H) p.yp[(int64_t)pr[b] * p.H + n] = acc[rb][b][r] * g;
+        }
+  }
+}
+
+template <int LIC, int RMAX, bool DENSE>
+__global__ void __launch_bounds__(64) staged_down_kernel(MoeParams p) {
+  const int lane = threadIdx.x;
+  const int slot = blockIdx.x / p.P, t = blockIdx.x % p.P;
+  PairCache pc;
+  load_pair_cache(p, lane, pc);
+  SlotInfo s;
+  if (!slot_info(p, slot, s)) return;
+  const uint8_t* tile = down_matrix(p, s) + (int64_t)t * kTileBytes;
+  const float g = s.shared ? p.sdn_g[0] : p.dn_g[s.e];
+  if constexpr (DENSE) {
+    if (s.rows >= p.dense_min_rows) {
+      staged_down_dense<2>(p, s, tile, t, g);
+      return;
+    }
+  }
+  const int L = LIC ? LIC : p.LI;
+  TileRegs T;
+  load_tile(tile, lane, T);
+#pragma unroll 1
+  for (int r0 = 0; r0 < s.rows; r0 += RMAX) {
+    opaque_tile(T);
+    const int rows = (s.rows - r0) < RMAX ? (s.rows - r0) : RMAX;
+    if (RMAX >= 8 && rows > 4)
+      staged_down_rows<LIC, (RMAX >= 8 ? 8 : 1)>(p, s, pc, T, r0, rows, t, g, L);
+    else if (RMAX >= 4 && rows > 2)
+      staged_down_rows<LIC, (RMAX >= 4 ? 4 : 1)>(p, s, pc, T, r0, rows, t, g, L);
+    else if (RMAX >= 2 && rows > 1)
+      staged_down_rows<LIC, (RMAX >= 2 ? 2 : 1)>(p, s, pc, T, r0, rows, t, g, L);
+    else
+      staged_down_rows<LIC, 1>(p, s, pc, T, r0, rows, t, g, L);
+  }
+}
+
+// ---- combine -------------------------------------------------------------------------------
+
+// One thread per output (m, n): routed slots in j order, then shared, then residual.
+__global__ void __launch_bounds__(256) staged_combine_kernel(MoeParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)p.M * p.H) return;
+  const int m = (int)(idx / p.H), n = (int)(idx % p.H);
+  float acc = 0.0f;
+  for (int t = 0; t < p.k; ++t)
+    acc += p.w[m * p.k + t] * p.yp[((int64_t)m * p.k + t) * p.H + n];
+  if (p.has_shared) acc += p.yp[((int64_t)p.M * p.k + m) * p.H + n];
+  if (p.residual) acc += bf16_to_f32(p.residual[(int64_t)m * p.H + n]);
+  p.out[idx] = f32_to_bf16_rne(acc);
+}
+
+}  // namespace nvfp4moe

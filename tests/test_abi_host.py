@@ -102,8 +102,10 @@ def test_decode_validation(m):
     assert dec(_args(m, workspace_bytes=need - 1)) == m.NVFP4MOE_ERR_WORKSPACE
     assert "workspace" in m.last_error_detail()
     assert dec(_args(m, x=4096 + 8)) == m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned
-    # h [M*k][I] + y [M*k][H] as 8-byte (value, flag) words + counters
-    assert need >= 4 * 8 * (512 + 2048) * 8
+    assert dec(_args(m, schedule=3)) == m.NVFP4MOE_ERR_BAD_SHAPE
+    assert dec(_args(m, schedule=-1)) == m.NVFP4MOE_ERR_BAD_SHAPE
+    # h [M*k][I] + y [M*k][H] as 8-byte (value, flag) words, then as 4-byte words
+    assert need >= 4 * 8 * (512 + 2048) * (8 + 4)
     # plus the control block: one 128-byte counter line per slot and per output tile
-    assert need <= 4 * 8 * (512 + 2048) * 8 + 128 * (1 + 32 + 64) + 512
+    assert need <= 4 * 8 * (512 + 2048) * (8 + 4) + 128 * (1 + 32 + 64) + 1024
     assert m.moe_nvfp4_workspace_bytes(4, 256, 8, 2048, 512, True) > need

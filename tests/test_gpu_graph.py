@@ -1,6 +1,6 @@
 """HIP-graph capture of the decode step (route + MoE decode): every replay must
 reproduce the eager outputs bit for bit, with eager work and synchronisation
-between replays, and the workspace control block must stay at zero."""
+between replays, and (one-launch schedule) the workspace must stay at zero."""
 import numpy as np
 import pytest
 import torch
@@ -17,8 +17,9 @@ def m(gpu):
     return m
 
 
-@pytest.mark.parametrize("M,shared", [(4, False), (16, True)])
-def test_graph_replay_matches_eager(m, gpu, M, shared):
+@pytest.mark.parametrize("M,shared,schedule", [(4, False, 1), (16, True, 1), (16, True, 2),
+                                               (4, False, 2)])
+def test_graph_replay_matches_eager(m, gpu, M, shared, schedule):
     lays = [moe_layer(seed=s, wl=400, layer=s, M=M, E_=64, H_=2048, I_=512, k=8, bias=shared,
                       shared=shared) for s in range(3)]
     devs = [upload_layer(l, gpu, m) for l in lays]
@@ -31,7 +32,7 @@ def test_graph_replay_matches_eager(m, gpu, M, shared):
         d = devs[i]
         r = m.moe_route_topk(d["logits"], 8, d["bias"], out=routes[i])
         m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=d["x"],
-                           workspace=ws, out=outs[i])
+                           workspace=ws, out=outs[i], schedule=schedule)
 
     for i in range(3):
         step(i)
@@ -56,4 +57,5 @@ def test_graph_replay_matches_eager(m, gpu, M, shared):
         step(rep % 3)  # eager work between replays
         torch.cuda.synchronize()
     assert m.workspace_error_flag(ws) == 0
-    assert int(ws.count_nonzero().item()) == 0  # counters and exchange words all cleared
+    if schedule == 1:
+        assert int(ws.count_nonzero().item()) == 0  # counters and exchange words all cleared

@@ -120,15 +120,16 @@ def test_route_constructed_ties(m, gpu):
     assert int(r.ids.cpu()[0, 0]) == 0
 
 
-def _run_block(m, gpu, lay, residual=None):
+def _run_block(m, gpu, lay, residual=None, **kw):
     d = upload_layer(lay, gpu, m)
     r = m.moe_route_topk(d["logits"], lay.k, d["bias"])
     res = None if residual is None else to_dev_bf16(residual, gpu)
-    out = m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=res)
+    out = m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=res, **kw)
     torch.cuda.synchronize()
     return r, dev_bf16_to_f64(out)
 
 
+@pytest.mark.parametrize("schedule", [1, 2])
 @pytest.mark.parametrize("M,E,H,I,k,shared,resid", [
     (1, 16, 256, 256, 4, False, False), (3, 16, 256, 256, 4, True, False),
     (8, 16, 256, 512, 4, False, True), (17, 16, 512, 256, 4, True, True),
@@ -136,10 +137,29 @@ def _run_block(m, gpu, lay, residual=None):
     (6, 4, 2048, 512, 1, True, True), (11, 256, 256, 256, 8, False, False),
     (70, 64, 2048, 512, 8, True, True), (33, 40, 1024, 1024, 3, False, False),
     (4, 256, 2048, 2048, 8, False, False), (16, 8, 2048, 256, 8, True, False)])
-def test_moe_block_small(m, gpu, M, E, H, I, k, shared, resid):
+def test_moe_block_small(m, gpu, M, E, H, I, k, shared, resid, schedule):
     lay = moe_layer(seed=M + E, wl=200, M=M, E_=E, H_=H, I_=I, k=k, shared=shared)
     residual = synth.normal_bf16(synth.key(5, 201, M), (M, H)) if resid else None
-    r, out = _run_block(m, gpu, lay, residual)
+    r, out = _run_block(m, gpu, lay, residual, schedule=schedule)
+    ids, w = oracle.route_topk(lay.logits, k, lay.bias)
+    check_routing_exact(r, ids, w, E)
+    ref = oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down, lay.shared_gate_up,
+                           lay.shared_down, residual)
+    assert tol_ratio(out, ref) <= 1.0
+
+
+@pytest.mark.parametrize("M,E,k,shared,resid,dense_min_rows", [
+    (6, 4, 1, True, True, 1),      # every slot on MFMA, most blocks with one row
+    (17, 8, 8, True, False, 16),   # each expert holds all 17 rows: a 1-row second block
+    (48, 2, 2, True, False, 16),   # 48 rows: two passes over column blocks
+    (40, 3, 2, False, True, 8),    # MFMA and VALU slots side by side
+    (33, 64, 8, True, True, 4)])
+def test_moe_block_dense_mfma(m, gpu, M, E, k, shared, resid, dense_min_rows):
+    """Three-launch schedule at H = 2048, I = 512, where slots with at least
+    dense_min_rows rows run on BF16 MFMA (exact BF16 weights, h as hi + lo)."""
+    lay = moe_layer(seed=7 * M + E, wl=203, M=M, E_=E, H_=2048, I_=512, k=k, shared=shared)
+    residual = synth.normal_bf16(synth.key(5, 204, M), (M, 2048)) if resid else None
+    r, out = _run_block(m, gpu, lay, residual, schedule=2, dense_min_rows=dense_min_rows)
     ids, w = oracle.route_topk(lay.logits, k, lay.bias)
     check_routing_exact(r, ids, w, E)
     ref = oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down, lay.shared_gate_up,
@@ -155,12 +175,23 @@ def test_moe_block_deterministic_and_workspace_reuse(m, gpu):
     r = m.moe_route_topk(d["logits"], lay.k)
     WS_SHAPE = (16, 32, 8, 512, 256, True)
     ws = m.moe_workspace(*WS_SHAPE, gpu)
-    a = m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"], workspace=ws)
-    outs = [m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"], workspace=ws)
-            for _ in range(5)]
+    call = lambda s: m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"],
+                                        workspace=ws, schedule=s)
+    a = call(1)
+    outs = [call(1) for _ in range(5)]
     torch.cuda.synchronize()
     for b in outs:
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert m.workspace_error_flag(ws) == 0
-    assert int(ws.count_nonzero().item()) == 0  # counters and exchange words all cleared
+    # counters and exchange words all cleared (the three-launch region is untouched)
+    assert int(ws.count_nonzero().item()) == 0
+    # the three-launch schedule on the same workspace: deterministic too, and it
+    # leaves the one-launch region at zero
+    b3 = [call(2) for _ in range(3)]
+    c = call(1)
+    torch.cuda.synchronize()
+    for b in b3[1:]:
+        assert torch.equal(b3[0].view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    assert m.workspace_error_flag(ws) == 0
 
