@@ -83,6 +83,10 @@ def parse():
     p.add_argument("--steps", type=int, default=20000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="m4", choices=["m4", "m16", "m256"])
+    p.add_argument("--dense-min-rows", type=int, default=0,
+                   help="rows from which a slot uses MFMA (0 = library default)")
+    p.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2],
+                   help="0 = library choice, 1 = one launch, 2 = three launches")
     p.add_argument("--copies", type=int, default=0, help="weight sets cycled (0: >= 1 GB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -174,7 +178,8 @@ def main():
         c, j = i % copies, i % n_sets
         gu, dn, sgu, sdn = weights[c]
         r = m.moe_route_topk(lg[j], k, bs[j], out=routes[j])
-        m.moe_nvfp4_decode(xs[j], r, gu, dn, sgu, sdn, workspace=ws, out=outs[j])
+        m.moe_nvfp4_decode(xs[j], r, gu, dn, sgu, sdn, workspace=ws, out=outs[j],
+                           schedule=args.schedule, dense_min_rows=args.dense_min_rows)
 
     # the graph holds S steps: step i uses weight copy i % copies and set i % n_sets
     S = copies * int(np.ceil(n_sets / copies))
@@ -224,7 +229,8 @@ def main():
         gu, dn, sgu, sdn = weights[c]
         r = m.moe_route_topk(lg[j], k, bs[j], out=routes[j])
         starts[i].record(stream)
-        m.moe_nvfp4_decode(xs[j], r, gu, dn, sgu, sdn, workspace=ws, out=outs[j])
+        m.moe_nvfp4_decode(xs[j], r, gu, dn, sgu, sdn, workspace=ws, out=outs[j],
+                           schedule=args.schedule, dense_min_rows=args.dense_min_rows)
         ends[i].record(stream)
         decode_bytes.append(n_act[j] * expert_bytes(H, I) + (expert_bytes(H, I) if shared else 0)
                             + M * H * 4 + M * k * 8 + (E + 1 + E + 1) * 4 + M * k * 4)
@@ -253,7 +259,8 @@ def main():
                    "expert_inter": I, "weights": "nvfp4 e2m1 + e4m3/16 + f32",
                    "accumulate": "f32", "shared_expert": shared, "logit_bias": bias,
                    "weight_copies": copies, "logit_sets": n_sets, "graph_steps": S,
-                   "timing": "hip graph replay, events"},
+                   "timing": "hip graph replay, events",
+                   "schedule": args.schedule, "dense_min_rows": args.dense_min_rows},
         "rows_per_s": round(rows_per_s, 1),
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "bytes_per_step": round(mean_bytes),

@@ -170,10 +170,10 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
  * with FP32 accumulation and FP32 h. The slot sum runs in j order, then the
  * shared term, then the residual; the result is bit-reproducible from run to
  * run (no floating-point atomics).
- * Schedules: one launch (every tile item of gate_up and down in one grid,
- * exchanging h and y through the workspace; chosen while all of its blocks
- * fit on the GPU at once), or three launches (gate_up, down, combine; chosen
- * for larger grids). In the three-launch schedule, when H = 2048 and I = 512,
+ * Schedules: three launches (gate_up, down, combine; the default), or one
+ * launch (every tile item of gate_up and down in one grid, exchanging h and y
+ * through the workspace with flagged words). In the three-launch schedule,
+ * when H = 2048 and I = 512,
  * slots with at least dense_min_rows rows run on BF16 MFMA: weights exact in
  * BF16, x as stored, h as a hi + lo BF16 pair (relative error <= 2^-17).
  * Extra support-set conditions: H and I are each 32 * 2^j in [256, 2048], and

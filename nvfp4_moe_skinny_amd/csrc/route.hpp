@@ -7,7 +7,8 @@
 // by (logit descending, index ascending) gives. The weights are the softmax
 // over the selected logits.
 // Grouping is a stable counting sort: a pair's place inside its expert's run
-// is the number of earlier pairs routed to the same expert.
+// is the number of earlier pairs routed to the same expert (one wave, 64
+// pairs per step).
 #pragma once
 
 #include "common.hpp"
@@ -132,60 +133,93 @@ __device__ __forceinline__ void wave_scan256(const int (&v)[4], int lane, int (&
   total = __shfl(incl, 63, 64);
 }
 
-// Groups the P = M*k pairs by expert. Needs ids_lds[P] filled; uses counts_lds[256].
-// All threads of the block call it.
-__device__ __forceinline__ void group_pairs(const int32_t* ids_lds, int P, int E, int* counts_lds,
-                                            int* offs_lds, int32_t* __restrict__ counts,
-                                            int32_t* __restrict__ offsets,
-                                            int32_t* __restrict__ pairs,
-                                            int32_t* __restrict__ active,
-                                            int32_t* __restrict__ active_offsets,
-                                            int32_t* __restrict__ n_active) {
-  const int tid = threadIdx.x;
-  for (int e = tid; e < kRouteMaxE; e += blockDim.x) counts_lds[e] = 0;
-  __syncthreads();
-  for (int p = tid; p < P; p += blockDim.x) atomicAdd(&counts_lds[ids_lds[p]], 1);
-  __syncthreads();
-  if (tid < 64) {
-    const int lane = tid;
-    int c[4], f[4], cex[4], fex[4], ctot, ftot;
+// Lanes of this wave whose expert id equals this lane's (among `valid`
+// lanes), from one ballot per bit of the 8-bit id.
+__device__ __forceinline__ uint64_t match_id(int e, bool valid) {
+  uint64_t mask = __ballot(valid);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      c[j] = counts_lds[4 * lane + j];
-      f[j] = c[j] > 0 ? 1 : 0;
-    }
-    wave_scan256(c, lane, cex, ctot);
-    wave_scan256(f, lane, fex, ftot);
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t B = __ballot(bit);
+    mask &= bit ? B : ~B;
+  }
+  return valid ? mask : 0ull;
+}
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+// Groups the P = M*k pairs by expert with ONE wave (the calling wave; lane =
+// its lane id): a stable counting sort over batches of 64 pairs. Within a
+// batch, lanes holding the same expert find each other by ballots; a pair's
+// place is the expert's running offset plus the number of lower lanes with the
+// same expert, and the batch's lowest such lane advances the offset.
+// ids_lds[P] holds the expert of each pair; counts_lds / run_lds are 256-int
+// LDS scratch owned by this wave.
+__device__ __forceinline__ void group_pairs_wave(const int32_t* ids_lds, int P, int E, int lane,
+                                                 int* counts_lds, int* run_lds,
+                                                 int32_t* __restrict__ counts,
+                                                 int32_t* __restrict__ offsets,
+                                                 int32_t* __restrict__ pairs,
+                                                 int32_t* __restrict__ active,
+                                                 int32_t* __restrict__ active_offsets,
+                                                 int32_t* __restrict__ n_active) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * lane + j;
-      offs_lds[e] = cex[j];
-      if (e < E) {
-        counts[e] = c[j];
-        offsets[e] = cex[j];
-        if (f[j]) {  // active slots [0, ftot)
-          active[fex[j]] = e;
-          active_offsets[fex[j]] = cex[j];
-        }
-        if (e >= ftot) {  // unused slots [ftot, E)
-          active[e] = -1;
-          active_offsets[e] = ctot;
-        }
+  for (int j = 0; j < 4; ++j) counts_lds[4 * lane + j] = 0;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+  for (int p0 = 0; p0 < P; p0 += 64) {
+    const bool valid = p0 + lane < P;
+    const int e = valid ? ids_lds[p0 + lane] : 0;
+    const uint64_t same = match_id(e, valid);
+    if (valid && (same & lanes_below(lane)) == 0) counts_lds[e] += __popcll(same);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+  }
+  int c[4], f[4], cex[4], fex[4], ctot, ftot;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[j] = counts_lds[4 * lane + j];
+    f[j] = c[j] > 0 ? 1 : 0;
+  }
+  wave_scan256(c, lane, cex, ctot);
+  wave_scan256(f, lane, fex, ftot);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * lane + j;
+    run_lds[e] = cex[j];
+    if (e < E) {
+      counts[e] = c[j];
+      offsets[e] = cex[j];
+      if (f[j]) {  // active slots [0, ftot)
+        active[fex[j]] = e;
+        active_offsets[fex[j]] = cex[j];
+      }
+      if (e >= ftot) {  // unused slots [ftot, E)
+        active[e] = -1;
+        active_offsets[e] = ctot;
       }
     }
-    if (lane == 0) {
-      offsets[E] = ctot;
-      active_offsets[E] = ctot;
-      *n_active = ftot;
-    }
   }
-  __syncthreads();
-  // stable placement: rank of p among earlier pairs of the same expert
-  for (int p = tid; p < P; p += blockDim.x) {
-    const int e = ids_lds[p];
-    int rank = 0;
-    for (int q = 0; q < p; ++q) rank += (ids_lds[q] == e) ? 1 : 0;
-    pairs[offs_lds[e] + rank] = p;
+  if (lane == 0) {
+    offsets[E] = ctot;
+    active_offsets[E] = ctot;
+    *n_active = ftot;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+  for (int p0 = 0; p0 < P; p0 += 64) {
+    const bool valid = p0 + lane < P;
+    const int e = valid ? ids_lds[p0 + lane] : 0;
+    const uint64_t same = match_id(e, valid);
+    if (valid) {
+      const uint64_t below = same & lanes_below(lane);
+      pairs[run_lds[e] + __popcll(below)] = p0 + lane;
+      if (below == 0) run_lds[e] += __popcll(same);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -203,8 +237,9 @@ __global__ void __launch_bounds__(1024) route_group_kernel(
   for (int row = wave; row < M; row += kRouteWaves)
     route_row(logits, bias, E, k, row, lane, lp[wave], ids, w, ids_lds);
   __syncthreads();
-  group_pairs(ids_lds, M * k, E, counts_lds, offs_lds, counts, offsets, pairs, active,
-              active_offsets, n_active);
+  if (wave == 0)
+    group_pairs_wave(ids_lds, M * k, E, lane, counts_lds, offs_lds, counts, offsets, pairs,
+                     active, active_offsets, n_active);
 }
 
 // Larger M, first launch: one wave per row.
@@ -233,8 +268,9 @@ __global__ void __launch_bounds__(1024) group_kernel(const int32_t* __restrict__
   const int P = M * k;
   for (int p = threadIdx.x; p < P; p += blockDim.x) ids_lds[p] = ids[p];
   __syncthreads();
-  group_pairs(ids_lds, P, E, counts_lds, offs_lds, counts, offsets, pairs, active, active_offsets,
-              n_active);
+  if (threadIdx.x < 64)
+    group_pairs_wave(ids_lds, P, E, threadIdx.x, counts_lds, offs_lds, counts, offsets, pairs,
+                     active, active_offsets, n_active);
 }
 
 }  // namespace nvfp4moe

@@ -24,6 +24,13 @@ __device__ __forceinline__ int lane_pair(const MoeParams& p, const SlotInfo& s, 
   return s.shared ? p.M * p.k + r : p.pairs[s.row_begin + r];
 }
 
+// Slot of a tile item: the shared expert (if any) comes first, so that its
+// items, which carry every row, start with the first blocks instead of last.
+__device__ __forceinline__ int staged_slot(const MoeParams& p, int item_slot) {
+  if (!p.has_shared) return item_slot;
+  return item_slot == 0 ? p.routed_slots : item_slot - 1;
+}
+
 __device__ __forceinline__ const uint8_t* gate_matrix(const MoeParams& p, const SlotInfo& s) {
   return s.shared ? p.sgu : p.gu + (int64_t)s.e * p.gu_mat_bytes;
 }
@@ -33,16 +40,13 @@ __device__ __forceinline__ const uint8_t* down_matrix(const MoeParams& p, const 
 
 // ---- gate_up ------------------------------------------------------------------------------
 
-// VALU: R rows at a time, h as FP32 words.
+// VALU: h = silu(gate) * up for R loaded rows, as FP32 words.
 template <int LC, int R>
-__device__ __forceinline__ void staged_gate_rows(const MoeParams& p, const SlotInfo& s,
-                                                 const PairCache& c, const TileRegs& TG,
-                                                 const TileRegs& TU, int r0, int rows, int j,
-                                                 float g, int L) {
+__device__ __forceinline__ void staged_gate_math(const MoeParams& p, const TileRegs& TG,
+                                                 const TileRegs& TU, const uint4 (&xr)[R][4],
+                                                 const int (&pr)[R], int rows, int j, float g,
+                                                 int L) {
   const int lane = threadIdx.x;
-  int pr[R];
-  uint4 xr[R][4];
-  load_rows<R>(p, s, c, r0, rows, 32 * (lane % L), pr, xr);
   float ug[R], uu[R];
   {
     float part[R][8];
@@ -68,6 +72,17 @@ __device__ __forceinline__ void staged_gate_rows(const MoeParams& p, const SlotI
     for (int r = 0; r < R; ++r)
       if (r < rows) p.hp[(int64_t)pr[r] * p.I + i] = silu(ug[r] * g) * (uu[r] * g);
   }
+}
+
+template <int LC, int R>
+__device__ __forceinline__ void staged_gate_rows(const MoeParams& p, const SlotInfo& s,
+                                                 const PairCache& c, const TileRegs& TG,
+                                                 const TileRegs& TU, int r0, int rows, int j,
+                                                 float g, int L) {
+  int pr[R];
+  uint4 xr[R][4];
+  load_rows<R>(p, s, c, r0, rows, 32 * ((int)threadIdx.x % L), pr, xr);
+  staged_gate_math<LC, R>(p, TG, TU, xr, pr, rows, j, g, L);
 }
 
 // MFMA (H = 2048: a gate tile and an up tile hold 8 rows each, together one
@@ -128,9 +143,9 @@ __device__ __forceinline__ void staged_gate_dense(const MoeParams& p, const Slot
 }
 
 template <int LHC, int RMAX, bool DENSE>
-__global__ void __launch_bounds__(64) staged_gate_kernel(MoeParams p) {
+__global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_gate_kernel(MoeParams p) {
   const int lane = threadIdx.x;
-  const int slot = blockIdx.x / p.P, j = blockIdx.x % p.P;
+  const int slot = staged_slot(p, blockIdx.x / p.P), j = blockIdx.x % p.P;
   PairCache pc;
   load_pair_cache(p, lane, pc);
   SlotInfo s;
@@ -147,9 +162,20 @@ __global__ void __launch_bounds__(64) staged_gate_kernel(MoeParams p) {
   }
   const int L = LHC ? LHC : p.LH;
   TileRegs TG, TU;
-  load_tile_pair(tg, tu, lane, TG, TU);
+  // the first batch's activation rows are requested before the tiles, and
+  // its slabs are multiplied as they arrive (no wait for the whole tiles)
+  {
+    const int rows0 = s.rows < RMAX ? s.rows : RMAX;
+    int pr[RMAX];
+    uint4 xr[RMAX][4];
+    load_rows<RMAX>(p, s, pc, 0, rows0, 32 * (lane % L), pr, xr);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile_pair(tg, tu, lane, TG, TU);
+    __builtin_amdgcn_sched_barrier(0);
+    staged_gate_math<LHC, RMAX>(p, TG, TU, xr, pr, rows0, j, g, L);
+  }
 #pragma unroll 1
-  for (int r0 = 0; r0 < s.rows; r0 += RMAX) {
+  for (int r0 = RMAX; r0 < s.rows; r0 += RMAX) {
     opaque_tile(TG);
     opaque_tile(TU);
     const int rows = (s.rows - r0) < RMAX ? (s.rows - r0) : RMAX;
@@ -166,20 +192,25 @@ __global__ void __launch_bounds__(64) staged_gate_kernel(MoeParams p) {
 
 // ---- down ----------------------------------------------------------------------------------
 
-// VALU: R rows at a time from FP32 h, y as FP32 words.
-template <int LC, int R>
-__device__ __forceinline__ void staged_down_rows(const MoeParams& p, const SlotInfo& s,
-                                                 const PairCache& c, const TileRegs& T, int r0,
-                                                 int rows, int t, float g, int L) {
-  const int lane = threadIdx.x;
-  const int col0 = 32 * (lane % L);
-  int pr[R];
-  float hr[R][32];
+// VALU: h rows (FP32) of R pairs.
+template <int R>
+__device__ __forceinline__ void staged_load_h(const MoeParams& p, const SlotInfo& s,
+                                              const PairCache& c, int r0, int rows, int L,
+                                              int (&pr)[R], float (&hr)[R][32]) {
+  const int col0 = 32 * ((int)threadIdx.x % L);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     pr[r] = r < rows ? slot_pair(p, s, r0 + r, c) : 0;
     load_h_f32(p.hp, p.I, pr[r], r < rows, col0, hr[r]);
   }
+}
+
+// VALU: y for R loaded h rows, as FP32 words.
+template <int LC, int R>
+__device__ __forceinline__ void staged_down_math(const MoeParams& p, const TileRegs& T,
+                                                 const int (&pr)[R], const float (&hr)[R][32],
+                                                 int rows, int t, float g, int L) {
+  const int lane = threadIdx.x;
   float part[R][8];
   tile_dot_f32<R>(T, hr, part);
 #pragma unroll
@@ -190,6 +221,16 @@ __device__ __forceinline__ void staged_down_rows(const MoeParams& p, const SlotI
     for (int r = 0; r < R; ++r)
       if (r < rows) p.yp[(int64_t)pr[r] * p.H + n] = part[r][0] * g;
   }
+}
+
+template <int LC, int R>
+__device__ __forceinline__ void staged_down_rows(const MoeParams& p, const SlotInfo& s,
+                                                 const PairCache& c, const TileRegs& T, int r0,
+                                                 int rows, int t, float g, int L) {
+  int pr[R];
+  float hr[R][32];
+  staged_load_h<R>(p, s, c, r0, rows, L, pr, hr);
+  staged_down_math<LC, R>(p, T, pr, hr, rows, t, g, L);
 }
 
 // MFMA (I = 512: a down tile holds 32 rows, two 16-row blocks; K = 512 is 4
@@ -263,9 +304,9 @@ __device__ __forceinline__ void staged_down_dense(const MoeParams& p, const Slot
 }
 
 template <int LIC, int RMAX, bool DENSE>
-__global__ void __launch_bounds__(64) staged_down_kernel(MoeParams p) {
+__global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_down_kernel(MoeParams p) {
   const int lane = threadIdx.x;
-  const int slot = blockIdx.x / p.P, t = blockIdx.x % p.P;
+  const int slot = staged_slot(p, blockIdx.x / p.P), t = blockIdx.x % p.P;
   PairCache pc;
   load_pair_cache(p, lane, pc);
   SlotInfo s;
@@ -280,9 +321,18 @@ __global__ void __launch_bounds__(64) staged_down_kernel(MoeParams p) {
   }
   const int L = LIC ? LIC : p.LI;
   TileRegs T;
-  load_tile(tile, lane, T);
+  // h is complete (the gate_up launch has ended): the first batch's rows go
+  // out with the tile and its slabs are multiplied as they arrive
+  {
+    const int rows0 = s.rows < RMAX ? s.rows : RMAX;
+    int pr[RMAX];
+    float hr[RMAX][32];
+    load_tile(tile, lane, T);
+    staged_load_h<RMAX>(p, s, pc, 0, rows0, L, pr, hr);
+    staged_down_math<LIC, RMAX>(p, T, pr, hr, rows0, t, g, L);
+  }
 #pragma unroll 1
-  for (int r0 = 0; r0 < s.rows; r0 += RMAX) {
+  for (int r0 = RMAX; r0 < s.rows; r0 += RMAX) {
     opaque_tile(T);
     const int rows = (s.rows - r0) < RMAX ? (s.rows - r0) : RMAX;
     if (RMAX >= 8 && rows > 4)
