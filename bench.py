@@ -35,19 +35,24 @@ HBM_PEAK_GBS = 8000.0
 CPU_LAYERS = 12  # weight copies kept on the host for the CPU-baseline sample
 
 
+# the device code of one moe_nvfp4_decode call (all of its launches)
+DECODE_SOURCES = ("common.hpp", "tile.hpp", "dense.hpp", "moe.hpp", "staged.hpp", "api.hip")
+
+
 def kernel_source_hash():
-    """Hash of the decode kernel's sources, to tie recorded counters to the code."""
+    """Hash of the decode call's kernel sources, to tie recorded counters to the code."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("common.hpp", "tile.hpp", "moe.hpp"):
+    for f in DECODE_SOURCES:
         with open(os.path.join(ROOT, "nvfp4_moe_skinny_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def recorded_traffic():
-    """HBM bytes per decode launch from the committed FETCH_SIZE/WRITE_SIZE
-    summary, or None once the kernel has changed since it was taken."""
+    """HBM bytes per decode call (its gate_up, down and combine launches) from
+    the committed FETCH_SIZE/WRITE_SIZE summary, or None once the kernels have
+    changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "moe_decode_m4_counters.md")
     try:
         fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
@@ -266,7 +271,11 @@ def main():
         "bytes_per_step": round(mean_bytes),
         "touched_experts_mean": float(np.mean(n_act)),
         "eager_ms_per_step": round(eager_ms, 4),
-        "roofline": {"bound": "hbm", "kernel": "moe_nvfp4_decode",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("moe_nvfp4_decode (one call: moe_decode_kernel)"
+                                if args.schedule == 1 else
+                                "moe_nvfp4_decode (one call: staged_gate_kernel, "
+                                "staged_down_kernel, staged_combine_kernel)"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic() if args.workload == "m4" else None,
