@@ -96,9 +96,24 @@ int32_t launch_staged(const MoeParams& p, hipStream_t s) {
   return launched("moe_nvfp4_decode");
 }
 
+// One row per batch: gate_up with two waves per item (gate tile, up tile).
+template <int LH, int LI, bool DENSE>
+int32_t launch_staged_split(const MoeParams& p, hipStream_t s) {
+  const int grid = p.slots * p.P;
+  hipLaunchKernelGGL((staged_gate_split_kernel<LH, DENSE>), dim3(grid), dim3(128), 0, s, p);
+  hipLaunchKernelGGL((staged_down_kernel<LI, 1, DENSE>), dim3(grid), dim3(64), 0, s, p);
+  const int64_t outs = (int64_t)p.M * p.H;
+  hipLaunchKernelGGL(staged_combine_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s,
+                     p);
+  return launched("moe_nvfp4_decode");
+}
+
 // Rows per batch: gate_up 1, 2 or 4, down at most 2 (register budget); the
 // shapes without MFMA take one row at a time.
 int32_t launch_staged_rows(const MoeParams& p, bool specialised, int rmax, hipStream_t s) {
+  if (rmax == 1)
+    return specialised ? launch_staged_split<64, 16, true>(p, s)
+                       : launch_staged_split<0, 0, false>(p, s);
   if (!specialised) return launch_staged<0, 0, 1, 1, false>(p, s);
   switch (rmax) {
     case 1: return launch_staged<64, 16, 1, 1, true>(p, s);

@@ -190,6 +190,61 @@ __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_gate_kernel(MoeP
   }
 }
 
+// Gate_up with two waves per item (one row per batch): wave 0 streams the gate
+// tile, wave 1 the up tile, each half the bytes and half the arithmetic of a
+// one-wave item; wave 1 hands its reduced values to wave 0 through LDS.
+template <int LC>
+__device__ __forceinline__ float tile_row_value(const TileRegs& T, const uint4 (&xr)[1][4], int L) {
+  float part[1][8];
+  tile_dot_bf16<1>(T, xr, part);
+  reduce_slabs_rt<LC>(part[0], (int)threadIdx.x & 63, L);
+  return part[0][0];
+}
+
+template <int LHC, bool DENSE>
+__global__ void __launch_bounds__(128, 4) staged_gate_split_kernel(MoeParams p) {
+  __shared__ float up_lds[64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = staged_slot(p, blockIdx.x / p.P), j = blockIdx.x % p.P;
+  PairCache pc;
+  load_pair_cache(p, lane, pc);
+  SlotInfo s;
+  if (!slot_info(p, slot, s)) return;
+  const uint8_t* mat = gate_matrix(p, s);
+  const float g = s.shared ? p.sgu_g[0] : p.gu_g[s.e];
+  const uint8_t* tg = mat + (int64_t)j * kTileBytes;
+  const uint8_t* tu = mat + (int64_t)(j + p.P) * kTileBytes;
+  if constexpr (DENSE) {
+    if (s.rows >= p.dense_min_rows) {
+      if (wave == 0) staged_gate_dense<2>(p, s, tg, tu, j, g);
+      return;
+    }
+  }
+  const int L = LHC ? LHC : p.LH;
+  const bool writer = reduced_writer_rt(lane, L);
+  const int i = j * (16384 / p.H) + reduced_row(lane, L);
+  TileRegs T;
+#pragma unroll 1
+  for (int r = 0; r < s.rows; ++r) {
+    int pr[1];
+    uint4 xr[1][4];
+    if (r == 0) {
+      load_rows<1>(p, s, pc, 0, 1, 32 * (lane % L), pr, xr);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(wave == 0 ? tg : tu, lane, T);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      opaque_tile(T);
+      load_rows<1>(p, s, pc, r, 1, 32 * (lane % L), pr, xr);
+    }
+    const float v = tile_row_value<LHC>(T, xr, L);
+    if (wave == 1) up_lds[lane] = v;
+    __syncthreads();
+    if (wave == 0 && writer) p.hp[(int64_t)pr[0] * p.I + i] = silu(v * g) * (up_lds[lane] * g);
+    __syncthreads();
+  }
+}
+
 // ---- down ----------------------------------------------------------------------------------
 
 // VALU: h rows (FP32) of R pairs.
