@@ -14,6 +14,8 @@
 #include "pack.hpp"
 #include "route.hpp"
 
+static_assert(nvfp4moe::kMaxTopK == nvfp4moe::kRouteMaxK, "combine unrolls to the routing bound on k");
+
 using namespace nvfp4moe;
 
 namespace {

@@ -115,22 +115,31 @@ __device__ __forceinline__ void route_row(const float* __restrict__ logits,
   }
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP: shifts by 1, 2, 4 and 8
+// within each 16-lane row, then lane 15 of a row into the next row and lane
+// 31 into the upper two rows (lanes shifted in from outside a row add 0).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2, 3
+  return v;
+}
+
 // Inclusive scan over 256 entries held 4 per lane (lane l: entries 4l..4l+3)
 // by one wave; returns the exclusive prefix of each entry in ex[4].
 __device__ __forceinline__ void wave_scan256(const int (&v)[4], int lane, int (&ex)[4], int& total) {
   const int s0 = v[0], s1 = s0 + v[1], s2 = s1 + v[2], s3 = s2 + v[3];
-  int incl = s3;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
+  const int incl = wave_inclusive_scan(s3);
   const int base = incl - s3;
   ex[0] = base;
   ex[1] = base + s0;
   ex[2] = base + s1;
   ex[3] = base + s2;
-  total = __shfl(incl, 63, 64);
+  total = __builtin_amdgcn_readlane(incl, 63);
+  (void)lane;
 }
 
 // Lanes of this wave whose expert id equals this lane's (among `valid`

@@ -403,16 +403,33 @@ __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_down_kernel(MoeP
 
 // ---- combine -------------------------------------------------------------------------------
 
-// One thread per output (m, n): routed slots in j order, then shared, then residual.
+constexpr int kMaxTopK = 8;  // the library's bound on k (checked on the host)
+
+// One thread per output (m, n): routed slots in j order, then shared, then
+// residual. Every term's loads are issued before the first add (the loop over
+// k is unrolled to its maximum), so a thread waits one round trip, not k.
 __global__ void __launch_bounds__(256) staged_combine_kernel(MoeParams p) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)p.M * p.H) return;
   const int m = (int)(idx / p.H), n = (int)(idx % p.H);
+  float yv[kMaxTopK], wv[kMaxTopK];
+#pragma unroll
+  for (int t = 0; t < kMaxTopK; ++t) {
+    yv[t] = 0.0f;
+    wv[t] = 0.0f;
+    if (t < p.k) {
+      yv[t] = p.yp[((int64_t)m * p.k + t) * p.H + n];
+      wv[t] = p.w[m * p.k + t];
+    }
+  }
+  const float ys = p.has_shared ? p.yp[((int64_t)p.M * p.k + m) * p.H + n] : 0.0f;
+  const float res = p.residual ? bf16_to_f32(p.residual[(int64_t)m * p.H + n]) : 0.0f;
   float acc = 0.0f;
-  for (int t = 0; t < p.k; ++t)
-    acc += p.w[m * p.k + t] * p.yp[((int64_t)m * p.k + t) * p.H + n];
-  if (p.has_shared) acc += p.yp[((int64_t)p.M * p.k + m) * p.H + n];
-  if (p.residual) acc += bf16_to_f32(p.residual[(int64_t)m * p.H + n]);
+#pragma unroll
+  for (int t = 0; t < kMaxTopK; ++t)
+    if (t < p.k) acc += wv[t] * yv[t];
+  if (p.has_shared) acc += ys;
+  if (p.residual) acc += res;
   p.out[idx] = f32_to_bf16_rne(acc);
 }
 
