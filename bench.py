@@ -87,7 +87,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20000)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--workload", default="m4", choices=["m4", "m16", "m256"])
+    p.add_argument("--workload", default="m4", choices=["m4", "m16", "m256", "head32k", "head248k"])
     p.add_argument("--dense-min-rows", type=int, default=0,
                    help="rows from which a slot uses MFMA (0 = library default)")
     p.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2],
@@ -123,6 +123,8 @@ def main():
         return 2
     if args.calibrate_copy_mb:
         return calibrate_copy(args.calibrate_copy_mb)
+    if args.workload.startswith("head"):
+        return bench_head(args)
     import torch
 
     import nvfp4_moe_skinny_amd as m
@@ -292,6 +294,67 @@ def main():
         record["cpu_baseline"] = cpu_baseline(layers_host, logit_sets, x_host, copies, n_sets,
                                               args.cpu_seconds, shared, bias)
     print(json.dumps(record), flush=True)
+    return 0
+
+
+def bench_head(args):
+    """Large-N skinny GEMM: M = 6 rows times a [N][2048] NVFP4 head (N = 32768,
+    the draft head; N = 248000, the full head). Not the headline line: a
+    measurement of the same streaming product at a bandwidth-sized shape."""
+    import torch
+
+    import nvfp4_moe_skinny_amd as m
+    from synth import workloads as W
+    from tests.helpers import pack, to_dev_bf16
+
+    dev = torch.device("cuda:0")
+    N = 32768 if args.workload == "head32k" else 248000
+    M = 6
+    w_bytes = N * 2048 // 2 + N * 2048 // 16 + 4
+    copies = args.copies or int(np.ceil(1e9 / w_bytes)) + 1
+    ws, xs = [], []
+    for c in range(copies):
+        x, w = W.draft_head(seed=0, M=M, N=N, layer=c)
+        ws.append(pack(w, dev, m))
+        xs.append(to_dev_bf16(x, dev))
+        torch.cuda.synchronize()
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    S = copies * int(np.ceil(16 / copies))
+
+    def step(i):
+        m.nvfp4_skinny_gemm(xs[i % copies], ws[i % copies], out=outs[i % copies])
+
+    for i in range(max(args.warmup, S)):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(S):
+                step(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    replays = max(1, args.steps // S)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(replays):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / (replays * S)
+    step_bytes = w_bytes + M * 2048 * 2 + M * N * 2
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "NVFP4 skinny GEMM achieved HBM GB/s (large-N head)", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": replays * S, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"nvfp4_skinny_gemm_m{M}_k2048_n{N}", "M": M, "K": 2048, "N": N,
+                   "weight_copies": copies, "timing": "hip graph replay, events"},
+        "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes,
+    }), flush=True)
     return 0
 
 

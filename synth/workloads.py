@@ -117,6 +117,12 @@ def dense_skinny(seed=0, M=1, K=2048, N=512, g=1.0, wl=1, layer=0, t_codes=T_W_C
     return x, w
 
 
+def draft_head(seed=0, M=6, N=32768, layer=0):
+    """A large-N skinny projection: M BF16 rows (a token and its draft tokens)
+    times a [N][2048] NVFP4 head, tensor scale 2^-9 (unit-scale outputs)."""
+    return dense_skinny(seed, M=M, K=H, N=N, g=tensor_scale_for_k(H), wl=6, layer=layer)
+
+
 def decode_m4(seed=0):
     """One MoE block, 4 rows (one token plus three draft tokens verified together)."""
     return moe_layer(seed, wl=2, M=4)

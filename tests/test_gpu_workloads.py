@@ -31,6 +31,20 @@ def test_dense_single_matrix(m, gpu):
     assert tol_ratio(dev_bf16_to_f64(y), ref) <= 1.0
 
 
+@pytest.mark.parametrize("M,N", [(6, 32768), (3, 32773), (1, 248000)])
+def test_draft_head_sampled(m, gpu, M, N):
+    """Large-N skinny GEMM (draft head and full head shapes): every output of
+    a sample of rows of W (spread over the matrix, plus the first and last,
+    including the ragged last tile) against the oracle on those rows."""
+    x, w = W.draft_head(seed=1, M=M, N=N)
+    pw = pack(w, gpu, m)
+    y = dev_bf16_to_f64(m.nvfp4_skinny_gemm(to_dev_bf16(x, gpu), pw))
+    torch.cuda.synchronize()
+    cols = np.unique(np.concatenate([np.arange(0, N, 97), np.arange(N - 16, N), np.arange(16)]))
+    ref = oracle.gemm(x, w.codes[0][cols], w.scales[0][cols], float(w.g[0]))
+    assert tol_ratio(y[:, cols], ref) <= 1.0
+
+
 def _block(m, gpu, lay):
     d = upload_layer(lay, gpu, m)
     r = m.moe_route_topk(d["logits"], lay.k, d["bias"])
