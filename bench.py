@@ -87,7 +87,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20000)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--workload", default="m4", choices=["m4", "m16", "m256", "head32k", "head248k"])
+    p.add_argument("--workload", default="m4", choices=["m4", "m16", "m256", "head32k", "head248k", "fp8qkv",
+                                             "fp8o"])
+    p.add_argument("--rows", type=int, default=0, help="rows M of a skinny-GEMM workload")
     p.add_argument("--dense-min-rows", type=int, default=0,
                    help="rows from which a slot uses MFMA (0 = library default)")
     p.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2],
@@ -119,12 +121,14 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path runs on one GPU's share; see DESIGN.md for sharding)", file=sys.stderr)
+              "(the path runs on one GPU's share of a sharded model)", file=sys.stderr)
         return 2
     if args.calibrate_copy_mb:
         return calibrate_copy(args.calibrate_copy_mb)
     if args.workload.startswith("head"):
         return bench_head(args)
+    if args.workload.startswith("fp8"):
+        return bench_fp8(args)
     import torch
 
     import nvfp4_moe_skinny_amd as m
@@ -297,6 +301,76 @@ def main():
     return 0
 
 
+def time_graph(step, copies, args):
+    """Captures S = a multiple of copies (>= 16) calls step(0 .. S-1) in one
+    HIP graph and times its replays with events: (ms per call, calls timed)."""
+    import torch
+    S = copies * int(np.ceil(16 / copies))
+    for i in range(max(args.warmup, S)):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(S):
+                step(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    replays = max(1, args.steps // S)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(replays):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / (replays * S), replays * S
+
+
+def bench_fp8(args):
+    """FP8 E4M3 skinny product with one tensor scale (attention projections):
+    M rows (default 4) times [N][K] FP8 weights, K = 2048 -> N = 5120 (fp8qkv)
+    or K = 4096 -> N = 2048 (fp8o). The weights are one seeded matrix copied
+    to enough device buffers (>= 1 GB in all) that replays read HBM, not the
+    last-level cache. Not the headline line."""
+    import torch
+
+    import nvfp4_moe_skinny_amd as m
+    from synth import workloads as W
+    from tests.helpers import to_dev_bf16
+
+    dev = torch.device("cuda:0")
+    K, N = (2048, 5120) if args.workload == "fp8qkv" else (4096, 2048)
+    M = args.rows or 4
+    x, w, s = W.fp8_projection(seed=0, M=M, K=K, N=N)
+    copies = args.copies or int(np.ceil(1e9 / w.nbytes)) + 1
+    wd = torch.from_numpy(w).to(dev)
+    ws = [wd.clone() for _ in range(copies)]
+    xd = to_dev_bf16(x, dev)
+    sc = torch.tensor([s], dtype=torch.float32, device=dev)
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        m.fp8_skinny_gemm(xd, ws[i % copies], sc, out=outs[i % copies])
+
+    ms, n_steps = time_graph(step, copies, args)
+    step_bytes = w.nbytes + 4 + M * K * 2 + M * N * 2
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "FP8 skinny GEMM achieved HBM GB/s (attention projection)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": n_steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"fp8_skinny_gemm_m{M}_k{K}_n{N}", "M": M, "K": K, "N": N,
+                   "weights": "fp8 e4m3 + one f32 tensor scale", "weight_copies": copies,
+                   "timing": "hip graph replay, events"},
+        "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes,
+    }), flush=True)
+    return 0
+
+
 def bench_head(args):
     """Large-N skinny GEMM: M = 6 rows times a [N][2048] NVFP4 head (N = 32768,
     the draft head; N = 248000, the full head). Not the headline line: a
@@ -319,36 +393,16 @@ def bench_head(args):
         xs.append(to_dev_bf16(x, dev))
         torch.cuda.synchronize()
     outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
-    S = copies * int(np.ceil(16 / copies))
 
     def step(i):
         m.nvfp4_skinny_gemm(xs[i % copies], ws[i % copies], out=outs[i % copies])
 
-    for i in range(max(args.warmup, S)):
-        step(i)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(graph, stream=cap):
-            for i in range(S):
-                step(i)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    replays = max(1, args.steps // S)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(replays):
-        graph.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / (replays * S)
+    ms, n_steps = time_graph(step, copies, args)
     step_bytes = w_bytes + M * 2048 * 2 + M * N * 2
     gbs = step_bytes / (ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "NVFP4 skinny GEMM achieved HBM GB/s (large-N head)", "value": round(gbs, 2),
-        "unit": "GB/s", "n_gpus": 1, "steps": replays * S, "warmup": args.warmup,
+        "unit": "GB/s", "n_gpus": 1, "steps": n_steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"nvfp4_skinny_gemm_m{M}_k2048_n{N}", "M": M, "K": 2048, "N": N,

@@ -103,6 +103,21 @@ int32_t nvfp4_dequant_f32(const void* packed, int64_t G, int64_t N, int64_t K, i
 int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w_packed,
                           int64_t N, uint16_t* y, hipStream_t stream);
 
+/* ---- FP8 skinny product -------------------------------------------------------------
+ *
+ * y[M][N] = bf16_rne( (sum_k x[m][k] * W[n][k]) * scale[0] ), W an FP8 E4M3
+ * ("FN": bias 7, max 448, 0x7F / 0xFF NaN) matrix [N][K] stored row-major as
+ * bytes (used as stored: no packing step), one FP32 scale for the whole
+ * tensor (a device pointer, so that the call can be graph-captured), FP32
+ * accumulation. The attention projections of the pages' model are of this
+ * kind ([Elsa] "An FP8 fast path": a small-batch FP8 GEMM with one scale per
+ * tensor). x [M][K] and y [M][N] are raw BF16 bits; M >= 1 (taken in batches
+ * of 4 rows over the same weight registers), N >= 1, K in {1024, 2048, 4096}
+ * (else NVFP4MOE_ERR_UNSUPPORTED); x and W 16-byte aligned.
+ */
+int32_t fp8_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w_fp8,
+                        const float* scale, int64_t N, uint16_t* y, hipStream_t stream);
+
 /* ---- routing -------------------------------------------------------------------------
  *
  * Per row m: l'[e] = fl32(logits[m][e] + bias[e]) (bias may be NULL: l' =

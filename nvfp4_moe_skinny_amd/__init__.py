@@ -69,6 +69,8 @@ def _load():
     L.nvfp4_dequant_f32.argtypes = [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp]
     L.nvfp4_skinny_gemm.restype = _i32
     L.nvfp4_skinny_gemm.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _vp]
+    L.fp8_skinny_gemm.restype = _i32
+    L.fp8_skinny_gemm.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp]
     L.moe_route_topk.restype = _i32
     L.moe_route_topk.argtypes = [_vp, _vp, _i64, _i64, _i64] + [_vp] * 9
     L.moe_nvfp4_workspace_bytes.restype = _i64
@@ -81,6 +83,7 @@ def _load():
 lib = _load()
 
 EXPORTS = ["nvfp4moe_strerror", "nvfp4moe_last_error_detail", "nvfp4moe_version",
+           "fp8_skinny_gemm",
            "nvfp4_packed_bytes", "nvfp4_pack", "nvfp4_dequant_f32", "nvfp4_skinny_gemm",
            "moe_route_topk", "moe_nvfp4_workspace_bytes", "moe_nvfp4_decode"]
 
@@ -170,6 +173,23 @@ def nvfp4_skinny_gemm(x: torch.Tensor, w: PackedNVFP4, stream=None,
         out = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device)
     _check(lib.nvfp4_skinny_gemm(_ptr(x), M, K, _ptr(w.data), w.N, _ptr(out), _stream(stream)),
            "nvfp4_skinny_gemm")
+    return out
+
+
+def fp8_skinny_gemm(x: torch.Tensor, w_fp8: torch.Tensor, scale: torch.Tensor, stream=None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x bfloat16 [M][K], w_fp8 uint8 [N][K] (E4M3 codes), scale float32 [1]
+    -> bfloat16 [M][N] = (x W^T) * scale."""
+    if x.dtype != torch.bfloat16 or w_fp8.dtype != torch.uint8 or scale.dtype != torch.float32:
+        raise ValueError("need bfloat16 x, uint8 w_fp8, float32 scale")
+    M, K = x.shape
+    N = w_fp8.shape[0]
+    if w_fp8.shape[1] != K:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(lib.fp8_skinny_gemm(_ptr(x), M, K, _ptr(w_fp8), _ptr(scale), N, _ptr(out),
+                               _stream(stream)), "fp8_skinny_gemm")
     return out
 
 

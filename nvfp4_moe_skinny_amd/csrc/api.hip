@@ -8,6 +8,7 @@
 
 #include "nvfp4moe.h"
 
+#include "fp8.hpp"
 #include "gemm.hpp"
 #include "moe.hpp"
 #include "staged.hpp"
@@ -228,6 +229,35 @@ int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w
   if (!aligned(x, 16) || !aligned(w_packed, 16))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "x and w_packed must be 16-byte aligned");
   return dispatch_l<GemmLaunch>(K / 32, x, M, (const uint8_t*)w_packed, N, y, stream);
+}
+
+int32_t fp8_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w_fp8,
+                        const float* scale, int64_t N, uint16_t* y, hipStream_t stream) {
+  if (!x || !w_fp8 || !scale || !y) return fail(NVFP4MOE_ERR_NULL_ARG, "fp8_skinny_gemm: null");
+  if (M < 1 || N < 1) return fail(NVFP4MOE_ERR_BAD_SHAPE, "M and N must be >= 1");
+  if (K != 1024 && K != 2048 && K != 4096)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "K = %lld: need 1024, 2048 or 4096", (long long)K);
+  if (!aligned(x, 16) || !aligned(w_fp8, 16))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "x and w_fp8 must be 16-byte aligned");
+  const int64_t rpt = 8 / (K / 1024);
+  const int64_t tiles = (N + rpt - 1) / rpt;
+  if (tiles > ((int64_t)1 << 31) - 1) return fail(NVFP4MOE_ERR_UNSUPPORTED, "N too large");
+  const dim3 grid((unsigned)tiles);
+  switch (K) {
+    case 1024:
+      hipLaunchKernelGGL((fp8_skinny_gemm_kernel<1, 4>), grid, dim3(64), 0, stream, x, M, w_fp8,
+                         scale, N, y);
+      break;
+    case 2048:
+      hipLaunchKernelGGL((fp8_skinny_gemm_kernel<2, 4>), grid, dim3(64), 0, stream, x, M, w_fp8,
+                         scale, N, y);
+      break;
+    default:
+      hipLaunchKernelGGL((fp8_skinny_gemm_kernel<4, 4>), grid, dim3(64), 0, stream, x, M, w_fp8,
+                         scale, N, y);
+      break;
+  }
+  return launched("fp8_skinny_gemm");
 }
 
 int32_t moe_route_topk(const float* logits, const float* bias, int64_t M, int64_t E, int64_t k,

@@ -35,6 +35,8 @@ def lib():
         L.oracle_dequant_f32.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp]
         L.oracle_gemm.restype = None
         L.oracle_gemm.argtypes = [_vp, _i64, _i64, _vp, _vp, ctypes.c_float, _i64, _vp]
+        L.oracle_gemm_fp8.restype = None
+        L.oracle_gemm_fp8.argtypes = [_vp, _i64, _i64, _vp, ctypes.c_double, _i64, _vp]
         L.oracle_route_topk.restype = ctypes.c_int
         L.oracle_route_topk.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp]
         L.oracle_group_by_expert.restype = None
@@ -99,6 +101,18 @@ def gemm(x_bf16, codes, scales, g) -> np.ndarray:
     assert codes.shape[-1] * 2 == K
     y = np.empty((M, N), dtype=np.float64)
     lib().oracle_gemm(_p(x), M, K, _p(codes), _p(scales), float(np.float32(g)), N, _p(y))
+    return y
+
+
+def gemm_fp8(x_bf16, w_fp8, s) -> np.ndarray:
+    """x: uint16 [M][K]; w_fp8: uint8 E4M3 codes [N][K]; s: tensor scale.
+    Returns float64 [M][N]."""
+    x, w = _c(x_bf16, np.uint16), _c(w_fp8, np.uint8)
+    M, K = x.shape
+    N = w.shape[0]
+    assert w.shape[1] == K
+    y = np.empty((M, N), dtype=np.float64)
+    lib().oracle_gemm_fp8(_p(x), M, K, _p(w), float(s), N, _p(y))
     return y
 
 

@@ -109,6 +109,19 @@ void oracle_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes,
     }
 }
 
+/* y[m][n] = (sum_k x[m][k] * e4m3(w[n][k])) * s, float64: the FP8 skinny product
+ * with one scale per tensor (Elsa page, "An FP8 fast path"). */
+void oracle_gemm_fp8(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w, double s,
+                     int64_t N, double* y) {
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k)
+        acc += oracle_bf16(x[m * K + k]) * oracle_e4m3(w[n * K + k]);
+      y[m * N + n] = acc * s;
+    }
+}
+
 /* ---- routing ----------------------------------------------------------------- */
 
 /* Does expert a come before expert b? Larger l' first, NaN after everything,

@@ -12,7 +12,9 @@
  *     in 4-bit NVFP4; the element and scale encodings are the OCP MX FP4
  *     (E2M1) and OCP 8-bit E4M3 formats.
  *   - skinny products y = x W^T of a few BF16 rows with 4-bit weights (Elsa
- *     page, "Making decode faster", paragraph on skinny matrix multiplies);
+ *     page, "Making decode faster", paragraph on skinny matrix multiplies),
+ *     and with FP8 E4M3 weights under one scale per tensor ("An FP8 fast
+ *     path" on the same page);
  *   - top-k routing, grouping of (row, slot) pairs by expert, the expert
  *     feed-forward gate_up -> SiLU*up -> down, and the routing-weighted
  *     combine ("finalize" on the same page), plus an always-on shared expert
@@ -49,6 +51,11 @@ void oracle_dequant_f32(const uint8_t* codes, const uint8_t* scales, const float
 /* y[M][N] = sum_k x[m][k] * W[n][k], W = dequant of one matrix, float64. */
 void oracle_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes,
                  const uint8_t* scales, float g, int64_t N, double* y);
+
+/* y[M][N] = (sum_k x[m][k] * e4m3(w[n][k])) * s in float64; w FP8 E4M3 codes
+ * [N][K] row-major, one scale s for the tensor. */
+void oracle_gemm_fp8(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w, double s,
+                     int64_t N, double* y);
 
 /* Top-k routing per row: l' = fl32(l + bias) (l' = l without bias); experts
  * ordered by l' descending, ties to the lower index, NaN below -inf; ids =

@@ -18,7 +18,7 @@ from typing import Optional
 
 import numpy as np
 
-from . import key, normal_bf16, normal_f32, scale_codes_keys, uniform_bytes_keys, \
+from . import key, normal_bf16, normal_f32, scale_codes_keys, uniform_bytes, uniform_bytes_keys, \
     zipf_gumbel_logits
 
 # tensor identifiers inside a stream key
@@ -121,6 +121,20 @@ def draft_head(seed=0, M=6, N=32768, layer=0):
     """A large-N skinny projection: M BF16 rows (a token and its draft tokens)
     times a [N][2048] NVFP4 head, tensor scale 2^-9 (unit-scale outputs)."""
     return dense_skinny(seed, M=M, K=H, N=N, g=tensor_scale_for_k(H), wl=6, layer=layer)
+
+
+def fp8_projection(seed=0, M=4, K=2048, N=5120, layer=0):
+    """M BF16 rows and an FP8 E4M3 matrix [N][K] with one tensor scale: the
+    attention-projection product. Codes: random sign, exponent field 4..11,
+    random mantissa (values 2^-3 .. 30, never NaN); scale 2^round(-log2(
+    sqrt(K E[v^2]))) with E[v^2] = 2.1484 * 42.66 for this code distribution,
+    so that outputs are of unit scale."""
+    x = normal_bf16(key(seed, 7, layer, T_X, 0), (M, K))
+    b = uniform_bytes(key(seed, 7, layer, T_W_CODES, 0), (N, K))
+    sign = uniform_bytes(key(seed, 7, layer, T_W_SCALES, 0), (N, K)) & 0x80
+    codes = (sign | ((4 + ((b >> 3) & 7)) << 3) | (b & 7)).astype(np.uint8)
+    s = 2.0 ** round(-np.log2(np.sqrt(K * 2.1484375 * 42.666)))
+    return x, codes, float(s)
 
 
 def decode_m4(seed=0):

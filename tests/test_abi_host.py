@@ -61,6 +61,13 @@ def test_validation_errors_before_launch(m):
     assert L.nvfp4_skinny_gemm(fake, 1, 4096, fake, 8, fake, None) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert L.nvfp4_skinny_gemm(fake + 2, 1, 64, fake, 8, fake, None) == \
         m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned x
+    assert L.fp8_skinny_gemm(None, 1, 2048, fake, fake, 8, fake, None) == m.NVFP4MOE_ERR_NULL_ARG
+    assert L.fp8_skinny_gemm(fake, 0, 2048, fake, fake, 8, fake, None) == m.NVFP4MOE_ERR_BAD_SHAPE
+    assert L.fp8_skinny_gemm(fake, 1, 2048, fake, fake, 0, fake, None) == m.NVFP4MOE_ERR_BAD_SHAPE
+    assert L.fp8_skinny_gemm(fake, 1, 512, fake, fake, 8, fake, None) == \
+        m.NVFP4MOE_ERR_UNSUPPORTED  # K not 1024, 2048 or 4096
+    assert L.fp8_skinny_gemm(fake, 1, 2048, fake + 8, fake, 8, fake, None) == \
+        m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned weights
     r = [fake] * 8
     assert L.moe_route_topk(None, None, 4, 256, 8, *r, None) == m.NVFP4MOE_ERR_NULL_ARG
     assert L.moe_route_topk(fake, None, 4, 257, 8, *r, None) == m.NVFP4MOE_ERR_UNSUPPORTED

@@ -198,6 +198,61 @@ def test_gemm_special_cases():
     assert (oracle.gemm(x, codes, scales, 0.75) * 2 == oracle.gemm(x, codes, scales, 1.5)).all()
 
 
+# ---- FP8 skinny product (Elsa page, "An FP8 fast path") ------------------------------
+
+@pytest.mark.parametrize("M,K,N,sexp", [(1, 16, 1, 0), (2, 48, 5, -9), (3, 64, 7, 4)])
+def test_gemm_fp8_equals_exact_rational_sum(M, K, N, sexp):
+    """Every finite E4M3 code (incl. subnormals and negatives) times BF16 values
+    in [2^-8, 2^8): each product and partial sum is a dyadic rational float64
+    holds, so the oracle must equal the exact sum, decoded with torch's own
+    float8_e4m3fn, bit for bit."""
+    rng = np.random.default_rng(7000 + M * 100 + K + N)
+    x = _bf16_bits_in_range(rng, (M, K))
+    w = rng.choice(FINITE_E4M3, (N, K)).astype(np.uint8)
+    s = 2.0 ** sexp
+    xf = [[Fraction(float(v)) for v in row] for row in bf16_to_f64(x)]
+    wv = torch_e4m3(w)
+    got = oracle.gemm_fp8(x, w, s)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(xf[m][k] * Fraction(float(wv[n, k])) for k in range(K)) * Fraction(s)
+            assert got[m, n] == float(exact) and Fraction(got[m, n]) == exact, (m, n)
+
+
+def test_gemm_fp8_special_cases():
+    M, K, N = 3, 64, 5
+    x = synth.normal_bf16(synth.key(2), (M, K))
+    xd = bf16_to_f64(x)
+    # one non-zero weight in row 2, column 41: 0xC3 = -(1 + 3/8) * 2^1
+    w = np.zeros((N, K), np.uint8)
+    w[2, 41] = 0xC3
+    y = oracle.gemm_fp8(x, w, 0.125)
+    assert (y[:, [0, 1, 3, 4]] == 0).all()
+    assert (y[:, 2] == xd[:, 41] * -2.75 * 0.125).all()
+    # unit rows of x read back the decoded weights exactly (every finite code)
+    K2 = 256
+    eye = np.zeros((4, K2), np.uint16)
+    cols = [0, 17, 130, 255]
+    for r, c in enumerate(cols):
+        eye[r, c] = 0x3F80  # 1.0
+    w = np.zeros((254, K2), np.uint8)
+    for r, c in enumerate(cols):
+        w[:, c] = FINITE_E4M3
+    y = oracle.gemm_fp8(eye, w, 1.0)
+    ref = torch_e4m3(FINITE_E4M3.astype(np.uint8))
+    for r in range(4):
+        assert (y[r] == ref).all()
+    # 0x80 is -0 and adds nothing; scaling s scales y exactly
+    rng = np.random.default_rng(5)
+    w = rng.choice(FINITE_E4M3, (N, K)).astype(np.uint8)
+    wz = w.copy()
+    wz[:, ::3] = 0x80
+    wz0 = w.copy()
+    wz0[:, ::3] = 0
+    assert (oracle.gemm_fp8(x, wz, 1.0) == oracle.gemm_fp8(x, wz0, 1.0)).all()
+    assert (oracle.gemm_fp8(x, w, 0.75) * 2 == oracle.gemm_fp8(x, w, 1.5)).all()
+
+
 # ---- routing -------------------------------------------------------------------------
 
 def _brute_route(logits, k, bias=None):
