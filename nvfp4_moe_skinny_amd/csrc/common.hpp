@@ -94,13 +94,70 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
 
 // ---- cross-lane exchange ------------------------------------------------------------
 
-__device__ __forceinline__ float xor_shuffle(float v, int d) { return __shfl_xor(v, d, 64); }
+// DPP controls (gfx9 encoding). Those named kDppXor<m> read lane l ^ m.
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;  // in a 16-lane row, lane i + 8 mod 16 = i ^ 8
+constexpr int kDppHalfMirror = 0x141;  // in 8 lanes, lane 7 - i = i ^ 7
+
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, int ctrl) {
+  switch (ctrl) {
+    case kDppQuadXor1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor1, 0xF, 0xF, false);
+    case kDppQuadXor2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor2, 0xF, 0xF, false);
+    case kDppRowRor4: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor4, 0xF, 0xF, false);
+    case kDppHalfMirror: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppHalfMirror, 0xF, 0xF, false);
+    default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor8, 0xF, 0xF, false);
+  }
+}
+
+// The value of lane l ^ 32 (every lane of the wave active). v_permlane32_swap
+// exchanges the upper half of its first operand with the lower half of its
+// second; with both operands v, result 1 holds the upper half's values in the
+// lower lanes and result 0 the lower half's in the upper lanes.
+__device__ __forceinline__ float partner32(float v, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+// Halving exchange at distance d (a power of two <= 32; the whole wave
+// active, d uniform): a lane whose bit log2(d) is clear returns
+// a + a(partner), a lane whose bit is set b + b(partner). The partner
+// differs from the lane in bit log2(d) and in no higher bit: l ^ d, except
+// l ^ 7 for d = 4 (DPP has no xor-4 pattern; the half-row mirror is one).
+// Instead of LDS permutes: v_permlane32_swap / v_permlane16_swap for d = 32 /
+// 16 (one swap moves a's upper half and b's lower half at once) and DPP
+// operands below. Both orders of the two addends give the same sum.
+__device__ __forceinline__ float halve(float a, float b, int d, int lane) {
+  if (d == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if (d == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const bool upper = (lane & d) != 0;
+  const float send = upper ? a : b;
+  const float keep = upper ? b : a;
+  const int ctrl = d == 8 ? kDppRowRor8 : (d == 4 ? kDppHalfMirror : (d == 2 ? kDppQuadXor2
+                                                                           : kDppQuadXor1));
+  return keep + __uint_as_float(dpp_u32(__float_as_uint(send), ctrl));
+}
+
+// v + v(partner) in every lane, same pairing as halve().
+__device__ __forceinline__ float fold(float v, int d, int lane) { return halve(v, v, d, lane); }
 
 // Segmented reduction of per-slab partial sums over the L lanes that share a
 // row. In: v[8] per lane (slab 0..7). Out: v[0 .. 8/min(L,8)) hold full sums;
 // value j of lane l belongs to slab reduced_slab<L>(l) + j. Halving exchanges
 // first (each lane keeps half of its values and receives the partner's
-// matching half), then plain butterflies once one value is left.
+// matching half), then plain butterflies once one value is left; a lane's
+// half is chosen by its own bit log2(d), so the partner pattern of halve()
+// leaves this mapping as it is for xor partners.
 template <int L>
 __device__ __forceinline__ void reduce_slabs(float (&v)[8], int lane) {
   constexpr int kHalvings = (L >= 8) ? 3 : (L == 4 ? 2 : (L == 2 ? 1 : 0));
@@ -108,21 +165,17 @@ __device__ __forceinline__ void reduce_slabs(float (&v)[8], int lane) {
 #pragma unroll
   for (int t = 0; t < kHalvings; ++t) {
     const int d = L >> (t + 1);
-    const bool upper = (lane & d) != 0;
     const int half = count >> 1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (j < half) {
-        const float a = v[j], b = v[j + half];
-        const float send = upper ? a : b;
-        const float keep = upper ? b : a;
-        v[j] = keep + xor_shuffle(send, d);
+        v[j] = halve(v[j], v[j + half], d, lane);
       }
     }
     count = half;
   }
 #pragma unroll
-  for (int d = (L >= 8 ? L / 16 : 0); d >= 1; d >>= 1) v[0] += xor_shuffle(v[0], d);
+  for (int d = (L >= 8 ? L / 16 : 0); d >= 1; d >>= 1) v[0] = fold(v[0], d, lane);
 }
 
 template <int L>

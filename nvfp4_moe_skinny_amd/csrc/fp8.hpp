@@ -37,21 +37,15 @@ __device__ __forceinline__ void reduce_rows64(float (&v)[8], int lane) {
 #pragma unroll
   for (int t = 0; t < kHalvings; ++t) {
     const int d = 32 >> t;
-    const bool upper = (lane & d) != 0;
     const int half = count >> 1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (j < half) {
-        const float a = v[j], b = v[j + half];
-        const float send = upper ? a : b;
-        const float keep = upper ? b : a;
-        v[j] = keep + __shfl_xor(send, d, 64);
-      }
+      if (j < half) v[j] = halve(v[j], v[j + half], d, lane);
     }
     count = half;
   }
 #pragma unroll
-  for (int d = 32 >> kHalvings; d >= 1; d >>= 1) v[0] += __shfl_xor(v[0], d, 64);
+  for (int d = 32 >> kHalvings; d >= 1; d >>= 1) v[0] = fold(v[0], d, lane);
 }
 
 // One wave per tile of 8 / S rows; rows of x in batches of up to R.

@@ -203,20 +203,14 @@ __device__ __forceinline__ void reduce_slabs_rt(float (&v)[8], int lane, int Lrt
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       const int d = Lrt >> (t + 1);
-      const bool upper = (lane & d) != 0;
       const int half = count >> 1;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (j < half) {
-          const float a = v[j], b = v[j + half];
-          const float send = upper ? a : b;
-          const float keep = upper ? b : a;
-          v[j] = keep + xor_shuffle(send, d);
-        }
+        if (j < half) v[j] = halve(v[j], v[j + half], d, lane);
       }
       count = half;
     }
-    for (int d = Lrt / 16; d >= 1; d >>= 1) v[0] += xor_shuffle(v[0], d);
+    for (int d = Lrt / 16; d >= 1; d >>= 1) v[0] = fold(v[0], d, lane);
   }
 }
 

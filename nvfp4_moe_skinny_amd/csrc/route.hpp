@@ -30,21 +30,6 @@ __device__ __forceinline__ uint32_t route_ord(float l) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// DPP controls (gfx9 encoding)
-constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int kDppRowRor4 = 0x124;
-constexpr int kDppRowRor8 = 0x128;
-
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, int ctrl) {
-  switch (ctrl) {
-    case kDppQuadXor1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor1, 0xF, 0xF, false);
-    case kDppQuadXor2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor2, 0xF, 0xF, false);
-    case kDppRowRor4: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor4, 0xF, 0xF, false);
-    default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor8, 0xF, 0xF, false);
-  }
-}
-
 // Maximum over the wave, returned uniform: DPP within each 16-lane row, then
 // the four row results through readlane.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

@@ -132,7 +132,7 @@ __device__ __forceinline__ void staged_gate_dense(const MoeParams& p, const Slot
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = acc[b][r];
-        const float u = xor_shuffle(v, 32);
+        const float u = partner32(v, lane);
         if (lane < 32 && pr[b] >= 0) {
           const int i = j * 8 + 4 * grp + r;
           hw[(int64_t)pr[b] * p.I + i] = pack_hilo(silu(v * g) * (u * g));
