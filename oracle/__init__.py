@@ -37,6 +37,8 @@ def lib():
         L.oracle_gemm.argtypes = [_vp, _i64, _i64, _vp, _vp, ctypes.c_float, _i64, _vp]
         L.oracle_gemm_fp8.restype = None
         L.oracle_gemm_fp8.argtypes = [_vp, _i64, _i64, _vp, ctypes.c_double, _i64, _vp]
+        L.oracle_router_logits.restype = None
+        L.oracle_router_logits.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp]
         L.oracle_route_topk.restype = ctypes.c_int
         L.oracle_route_topk.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp]
         L.oracle_group_by_expert.restype = None
@@ -114,6 +116,18 @@ def gemm_fp8(x_bf16, w_fp8, s) -> np.ndarray:
     y = np.empty((M, N), dtype=np.float64)
     lib().oracle_gemm_fp8(_p(x), M, K, _p(w), float(s), N, _p(y))
     return y
+
+
+def router_logits(x_bf16, w_router_bf16) -> np.ndarray:
+    """x: uint16 [M][H]; w_router: uint16 [E][H] (BF16 bits). Returns float64
+    [M][E] = x W_r^T."""
+    x, wr = _c(x_bf16, np.uint16), _c(w_router_bf16, np.uint16)
+    M, H = x.shape
+    E = wr.shape[0]
+    assert wr.shape[1] == H
+    out = np.empty((M, E), dtype=np.float64)
+    lib().oracle_router_logits(_p(x), M, H, _p(wr), E, _p(out))
+    return out
 
 
 def route_topk(logits, k, bias=None):

@@ -122,6 +122,19 @@ void oracle_gemm_fp8(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w, 
     }
 }
 
+/* logits[m][e] = sum_h x[m][h] * w_r[e][h] in float64: the router projection in
+ * front of top-k routing of the mixture-of-experts model (Elsa page, "The card
+ * and the model"). x and w_r are BF16 bit patterns; w_r is [E][H]. */
+void oracle_router_logits(const uint16_t* x, int64_t M, int64_t H, const uint16_t* w_r, int64_t E,
+                          double* logits) {
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int64_t h = 0; h < H; ++h) acc += oracle_bf16(x[m * H + h]) * oracle_bf16(w_r[e * H + h]);
+      logits[m * E + e] = acc;
+    }
+}
+
 /* ---- routing ----------------------------------------------------------------- */
 
 /* Does expert a come before expert b? Larger l' first, NaN after everything,

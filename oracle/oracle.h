@@ -15,6 +15,8 @@
  *     page, "Making decode faster", paragraph on skinny matrix multiplies),
  *     and with FP8 E4M3 weights under one scale per tensor ("An FP8 fast
  *     path" on the same page);
+ *   - the router projection (logits = x W_r^T, BF16 weights) in front of
+ *     top-k routing ("The card and the model": a mixture-of-experts model);
  *   - top-k routing, grouping of (row, slot) pairs by expert, the expert
  *     feed-forward gate_up -> SiLU*up -> down, and the routing-weighted
  *     combine ("finalize" on the same page), plus an always-on shared expert
@@ -56,6 +58,11 @@ void oracle_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes,
  * [N][K] row-major, one scale s for the tensor. */
 void oracle_gemm_fp8(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w, double s,
                      int64_t N, double* y);
+
+/* Router projection: logits[M][E] = x W_r^T in float64; x BF16 [M][H], w_r
+ * BF16 [E][H]. */
+void oracle_router_logits(const uint16_t* x, int64_t M, int64_t H, const uint16_t* w_r, int64_t E,
+                          double* logits);
 
 /* Top-k routing per row: l' = fl32(l + bias) (l' = l without bias); experts
  * ordered by l' descending, ties to the lower index, NaN below -inf; ids =

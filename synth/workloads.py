@@ -26,6 +26,7 @@ T_X, T_LOGITS, T_BIAS = 1, 2, 3
 T_GU_CODES, T_GU_SCALES, T_DN_CODES, T_DN_SCALES = 4, 5, 6, 7
 T_SH_GU_CODES, T_SH_GU_SCALES, T_SH_DN_CODES, T_SH_DN_SCALES = 8, 9, 10, 11
 T_P_CODES, T_P_SCALES, T_PERM, T_W_CODES, T_W_SCALES = 12, 13, 14, 15, 16
+T_ROUTER = 17
 
 H, I, E, TOPK = 2048, 512, 256, 8
 G_K2048 = 2.0 ** -9
@@ -135,6 +136,12 @@ def fp8_projection(seed=0, M=4, K=2048, N=5120, layer=0):
     codes = (sign | ((4 + ((b >> 3) & 7)) << 3) | (b & 7)).astype(np.uint8)
     s = 2.0 ** round(-np.log2(np.sqrt(K * 2.1484375 * 42.666)))
     return x, codes, float(s)
+
+
+def router_weights(seed=0, wl=2, layer=0, E_=E, H_=H):
+    """BF16 router matrix [E][H], entries N(0, 1/H): for rows of unit RMS the
+    logits x W_r^T are about N(0, 1), the logit scale of the other workloads."""
+    return normal_bf16(key(seed, wl, layer, T_ROUTER, 0), (E_, H_), 0.0, 1.0 / np.sqrt(H_))
 
 
 def decode_m4(seed=0):

@@ -198,6 +198,44 @@ def test_gemm_special_cases():
     assert (oracle.gemm(x, codes, scales, 0.75) * 2 == oracle.gemm(x, codes, scales, 1.5)).all()
 
 
+# ---- router projection ----------------------------------------------------------------
+
+@pytest.mark.parametrize("M,H,E", [(1, 16, 3), (3, 64, 9), (2, 96, 5)])
+def test_router_logits_equal_exact_rational_sum(M, H, E):
+    """BF16 x BF16 products of values in [2^-8, 2^8) and their sums are dyadic
+    rationals float64 holds exactly: the oracle must equal the exact sum."""
+    rng = np.random.default_rng(900 + M * 10 + H + E)
+    x = _bf16_bits_in_range(rng, (M, H))
+    wr = _bf16_bits_in_range(rng, (E, H))
+    xf = [[Fraction(float(v)) for v in row] for row in bf16_to_f64(x)]
+    wf = [[Fraction(float(v)) for v in row] for row in bf16_to_f64(wr)]
+    got = oracle.router_logits(x, wr)
+    for m in range(M):
+        for e in range(E):
+            exact = sum(xf[m][h] * wf[e][h] for h in range(H))
+            assert got[m, e] == float(exact) and Fraction(got[m, e]) == exact, (m, e)
+
+
+def test_router_logits_special_cases():
+    M, H, E = 3, 128, 6
+    x = synth.normal_bf16(synth.key(4), (M, H))
+    xd = bf16_to_f64(x)
+    # row e of W_r one-hot at column c_e (value 2^-e): logits pick x's columns
+    wr = np.zeros((E, H), np.uint16)
+    cols = [0, 5, 64, 100, 127, 31]
+    for e, c in enumerate(cols):
+        wr[e, c] = (127 - e) << 7  # 2^-e
+    got = oracle.router_logits(x, wr)
+    for e, c in enumerate(cols):
+        assert (got[:, e] == xd[:, c] * 2.0 ** -e).all()
+    # swapping rows of W_r swaps the logit columns; negating x negates them
+    wr = synth.normal_bf16(synth.key(5), (E, H))
+    a = oracle.router_logits(x, wr)
+    b = oracle.router_logits(x, wr[::-1].copy())
+    assert (b == a[:, ::-1]).all()
+    assert (oracle.router_logits(x ^ np.uint16(0x8000), wr) == -a).all()
+
+
 # ---- FP8 skinny product (Elsa page, "An FP8 fast path") ------------------------------
 
 @pytest.mark.parametrize("M,K,N,sexp", [(1, 16, 1, 0), (2, 48, 5, -9), (3, 64, 7, 4)])
