@@ -140,6 +140,21 @@ int32_t moe_route_topk(const float* logits, const float* bias, int64_t M, int64_
                        int32_t* active, int32_t* active_offsets, int32_t* n_active,
                        hipStream_t stream);
 
+/* Router projection, then the routing above: logits[m][e] = sum_h x[m][h] *
+ * w_router[e][h] with FP32 accumulation and FP32 result, written to the
+ * caller's logits buffer [M][E] (an output: it is also what the selection
+ * reads), then exactly moe_route_topk(logits, bias, ...). The pages' model is
+ * a routed mixture of experts ([Elsa] "The card and the model"); its router
+ * is neither an NVFP4 expert nor an FP8 projection, so w_router is BF16 [E][H]
+ * (raw bits) and x is BF16 [M][H]. H in {512, 1024, 2048, 4096} (else
+ * NVFP4MOE_ERR_UNSUPPORTED); x and w_router 16-byte aligned; the limits on M,
+ * E and k are those of moe_route_topk. Two or three launches on `stream`. */
+int32_t moe_route_project_topk(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                               int64_t M, int64_t E, int64_t k, int64_t H, float* logits,
+                               int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                               int32_t* pairs, int32_t* active, int32_t* active_offsets,
+                               int32_t* n_active, hipStream_t stream);
+
 /* ---- MoE block -------------------------------------------------------------------------- */
 
 typedef struct moe_nvfp4_args {

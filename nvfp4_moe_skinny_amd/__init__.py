@@ -73,6 +73,8 @@ def _load():
     L.fp8_skinny_gemm.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp]
     L.moe_route_topk.restype = _i32
     L.moe_route_topk.argtypes = [_vp, _vp, _i64, _i64, _i64] + [_vp] * 9
+    L.moe_route_project_topk.restype = _i32
+    L.moe_route_project_topk.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64] + [_vp] * 10
     L.moe_nvfp4_workspace_bytes.restype = _i64
     L.moe_nvfp4_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32]
     L.moe_nvfp4_decode.restype = _i32
@@ -85,7 +87,7 @@ lib = _load()
 EXPORTS = ["nvfp4moe_strerror", "nvfp4moe_last_error_detail", "nvfp4moe_version",
            "fp8_skinny_gemm",
            "nvfp4_packed_bytes", "nvfp4_pack", "nvfp4_dequant_f32", "nvfp4_skinny_gemm",
-           "moe_route_topk", "moe_nvfp4_workspace_bytes", "moe_nvfp4_decode"]
+           "moe_route_topk", "moe_route_project_topk", "moe_nvfp4_workspace_bytes", "moe_nvfp4_decode"]
 
 
 def strerror(status: int) -> str:
@@ -227,6 +229,31 @@ def moe_route_topk(logits: torch.Tensor, k: int, bias: Optional[torch.Tensor] = 
                               _ptr(r.active_offsets), _ptr(r.n_active), _stream(stream)),
            "moe_route_topk")
     return r
+
+
+def moe_route_project_topk(x: torch.Tensor, w_router: torch.Tensor, k: int,
+                           bias: Optional[torch.Tensor] = None, stream=None,
+                           out: Optional[Routing] = None,
+                           logits: Optional[torch.Tensor] = None):
+    """x bfloat16 [M][H], w_router bfloat16 [E][H] (+ bias float32 [E]) ->
+    (logits float32 [M][E], Routing): the router projection, then top-k."""
+    if x.dtype != torch.bfloat16 or w_router.dtype != torch.bfloat16:
+        raise ValueError("x and w_router must be bfloat16")
+    if bias is not None and bias.dtype != torch.float32:
+        raise ValueError("bias must be float32")
+    M, H = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise ValueError("shape mismatch")
+    r = routing_buffers(M, E, k, x.device) if out is None else out
+    if logits is None:
+        logits = torch.empty((M, E), dtype=torch.float32, device=x.device)
+    _check(lib.moe_route_project_topk(_ptr(x), _ptr(w_router), _ptr(bias), M, E, k, H,
+                                      _ptr(logits), _ptr(r.ids), _ptr(r.w), _ptr(r.counts),
+                                      _ptr(r.offsets), _ptr(r.pairs), _ptr(r.active),
+                                      _ptr(r.active_offsets), _ptr(r.n_active), _stream(stream)),
+           "moe_route_project_topk")
+    return logits, r
 
 
 # ---- MoE block ---------------------------------------------------------------------------

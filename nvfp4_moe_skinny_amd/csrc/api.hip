@@ -14,6 +14,7 @@
 #include "staged.hpp"
 #include "pack.hpp"
 #include "route.hpp"
+#include "router.hpp"
 
 static_assert(nvfp4moe::kMaxTopK == nvfp4moe::kRouteMaxK, "combine unrolls to the routing bound on k");
 
@@ -169,6 +170,46 @@ bool valid_moe_dim(int64_t v) { return valid_k(v) && v >= 256; }
 
 }  // namespace
 
+namespace {
+
+int32_t check_route(const float* logits, int64_t M, int64_t E, int64_t k, int32_t* ids, float* w,
+                    int32_t* counts, int32_t* offsets, int32_t* pairs, int32_t* active,
+                    int32_t* active_offsets, int32_t* n_active) {
+  if (!logits || !ids || !w || !counts || !offsets || !pairs || !active || !active_offsets ||
+      !n_active)
+    return fail(NVFP4MOE_ERR_NULL_ARG, "routing: null");
+  if (M < 1 || E < 1 || k < 1) return fail(NVFP4MOE_ERR_BAD_SHAPE, "M, E, k must be >= 1");
+  if (E > kRouteMaxE) return fail(NVFP4MOE_ERR_UNSUPPORTED, "E = %lld > 256", (long long)E);
+  if (k > kRouteMaxK || k > E)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "k = %lld: need k <= min(8, E)", (long long)k);
+  if (M * k > kGroupMaxPairs)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "M * k = %lld > %d", (long long)(M * k),
+                kGroupMaxPairs);
+  return ok();
+}
+
+// Top-k selection and grouping of validated logits.
+int32_t launch_route(const float* logits, const float* bias, int64_t M, int64_t E, int64_t k,
+                     int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* pairs,
+                     int32_t* active, int32_t* active_offsets, int32_t* n_active,
+                     hipStream_t stream) {
+  if (M <= kRouteSingleBlockRows) {
+    hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(1024), 0, stream, logits, bias, (int)M,
+                       (int)E, (int)k, ids, w, counts, offsets, pairs, active, active_offsets,
+                       n_active);
+    return launched("moe_route_topk");
+  }
+  hipLaunchKernelGGL(route_rows_kernel, dim3(grid_for(M, kRouteWaves, 1 << 20)), dim3(1024), 0,
+                     stream, logits, bias, (int)M, (int)E, (int)k, ids, w);
+  const int32_t st = launched("moe_route_topk rows");
+  if (st != NVFP4MOE_OK) return st;
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, ids, (int)M, (int)E, (int)k,
+                     counts, offsets, pairs, active, active_offsets, n_active);
+  return launched("moe_route_topk group");
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* nvfp4moe_strerror(int32_t status) {
@@ -260,33 +301,55 @@ int32_t fp8_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
   return launched("fp8_skinny_gemm");
 }
 
+
 int32_t moe_route_topk(const float* logits, const float* bias, int64_t M, int64_t E, int64_t k,
                        int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* pairs,
                        int32_t* active, int32_t* active_offsets, int32_t* n_active,
                        hipStream_t stream) {
-  if (!logits || !ids || !w || !counts || !offsets || !pairs || !active || !active_offsets ||
-      !n_active)
-    return fail(NVFP4MOE_ERR_NULL_ARG, "moe_route_topk: null");
-  if (M < 1 || E < 1 || k < 1) return fail(NVFP4MOE_ERR_BAD_SHAPE, "M, E, k must be >= 1");
-  if (E > kRouteMaxE) return fail(NVFP4MOE_ERR_UNSUPPORTED, "E = %lld > 256", (long long)E);
-  if (k > kRouteMaxK || k > E)
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "k = %lld: need k <= min(8, E)", (long long)k);
-  if (M * k > kGroupMaxPairs)
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "M * k = %lld > %d", (long long)(M * k),
-                kGroupMaxPairs);
-  if (M <= kRouteSingleBlockRows) {
-    hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(1024), 0, stream, logits, bias, (int)M,
-                       (int)E, (int)k, ids, w, counts, offsets, pairs, active, active_offsets,
-                       n_active);
-    return launched("moe_route_topk");
-  }
-  hipLaunchKernelGGL(route_rows_kernel, dim3(grid_for(M, kRouteWaves, 1 << 20)), dim3(1024), 0,
-                     stream, logits, bias, (int)M, (int)E, (int)k, ids, w);
-  const int32_t st = launched("moe_route_topk rows");
+  const int32_t st = check_route(logits, M, E, k, ids, w, counts, offsets, pairs, active,
+                                 active_offsets, n_active);
   if (st != NVFP4MOE_OK) return st;
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, ids, (int)M, (int)E, (int)k,
-                     counts, offsets, pairs, active, active_offsets, n_active);
-  return launched("moe_route_topk group");
+  return launch_route(logits, bias, M, E, k, ids, w, counts, offsets, pairs, active,
+                      active_offsets, n_active, stream);
+}
+
+int32_t moe_route_project_topk(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                               int64_t M, int64_t E, int64_t k, int64_t H, float* logits,
+                               int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                               int32_t* pairs, int32_t* active, int32_t* active_offsets,
+                               int32_t* n_active, hipStream_t stream) {
+  if (!x || !w_router) return fail(NVFP4MOE_ERR_NULL_ARG, "moe_route_project_topk: null");
+  int32_t st = check_route(logits, M, E, k, ids, w, counts, offsets, pairs, active,
+                           active_offsets, n_active);
+  if (st != NVFP4MOE_OK) return st;
+  if (H != 512 && H != 1024 && H != 2048 && H != 4096)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H = %lld: need 512, 1024, 2048 or 4096",
+                (long long)H);
+  if (!aligned(x, 16) || !aligned(w_router, 16))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "x and w_router must be 16-byte aligned");
+  const dim3 grid((unsigned)E), block(256);
+  switch (H) {
+    case 512:
+      hipLaunchKernelGGL(router_logits_kernel<2>, grid, block, 0, stream, x, M, w_router, (int)E,
+                         logits);
+      break;
+    case 1024:
+      hipLaunchKernelGGL(router_logits_kernel<4>, grid, block, 0, stream, x, M, w_router, (int)E,
+                         logits);
+      break;
+    case 2048:
+      hipLaunchKernelGGL(router_logits_kernel<8>, grid, block, 0, stream, x, M, w_router, (int)E,
+                         logits);
+      break;
+    default:
+      hipLaunchKernelGGL(router_logits_kernel<16>, grid, block, 0, stream, x, M, w_router, (int)E,
+                         logits);
+      break;
+  }
+  st = launched("moe_route_project_topk logits");
+  if (st != NVFP4MOE_OK) return st;
+  return launch_route(logits, bias, M, E, k, ids, w, counts, offsets, pairs, active,
+                      active_offsets, n_active, stream);
 }
 
 int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, int64_t I,

@@ -151,6 +151,28 @@ __device__ __forceinline__ float halve(float a, float b, int d, int lane) {
 // v + v(partner) in every lane, same pairing as halve().
 __device__ __forceinline__ float fold(float v, int d, int lane) { return halve(v, v, d, lane); }
 
+// Sum of v[0 .. RPT) over the 64 lanes, each row separately: halving
+// exchanges (a lane keeps half of its values, receives the partner's matching
+// half), then plain butterflies. After: v[0] of lane l holds the full sum of
+// row (l >> (6 - log2 RPT)) (all lanes of that group hold it).
+template <int RPT>
+__device__ __forceinline__ void reduce_rows64(float (&v)[8], int lane) {
+  constexpr int kHalvings = RPT == 8 ? 3 : (RPT == 4 ? 2 : (RPT == 2 ? 1 : 0));
+  int count = RPT;
+#pragma unroll
+  for (int t = 0; t < kHalvings; ++t) {
+    const int d = 32 >> t;
+    const int half = count >> 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < half) v[j] = halve(v[j], v[j + half], d, lane);
+    }
+    count = half;
+  }
+#pragma unroll
+  for (int d = 32 >> kHalvings; d >= 1; d >>= 1) v[0] = fold(v[0], d, lane);
+}
+
 // Segmented reduction of per-slab partial sums over the L lanes that share a
 // row. In: v[8] per lane (slab 0..7). Out: v[0 .. 8/min(L,8)) hold full sums;
 // value j of lane l belongs to slab reduced_slab<L>(l) + j. Halving exchanges

@@ -26,28 +26,6 @@ __device__ __forceinline__ bf16x2 fp8_pair_bf16(uint32_t w, bool hi_word) {
                  : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
 }
 
-// Sum of v[0 .. RPT) over the 64 lanes, each row separately: halving
-// exchanges (a lane keeps half of its values, receives the partner's matching
-// half), then plain butterflies. After: v[0] of lane l holds the full sum of
-// row (l >> (6 - log2 RPT)) (all lanes of that group hold it).
-template <int RPT>
-__device__ __forceinline__ void reduce_rows64(float (&v)[8], int lane) {
-  constexpr int kHalvings = RPT == 8 ? 3 : (RPT == 4 ? 2 : (RPT == 2 ? 1 : 0));
-  int count = RPT;
-#pragma unroll
-  for (int t = 0; t < kHalvings; ++t) {
-    const int d = 32 >> t;
-    const int half = count >> 1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < half) v[j] = halve(v[j], v[j + half], d, lane);
-    }
-    count = half;
-  }
-#pragma unroll
-  for (int d = 32 >> kHalvings; d >= 1; d >>= 1) v[0] = fold(v[0], d, lane);
-}
-
 // One wave per tile of 8 / S rows; rows of x in batches of up to R.
 template <int S, int RMAX>
 __global__ void __launch_bounds__(64) fp8_skinny_gemm_kernel(const uint16_t* __restrict__ x,

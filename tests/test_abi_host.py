@@ -76,6 +76,19 @@ def test_validation_errors_before_launch(m):
     assert L.moe_route_topk(fake, None, 0, 256, 8, *r, None) == m.NVFP4MOE_ERR_BAD_SHAPE
     assert L.moe_route_topk(fake, None, 2000, 256, 8, *r, None) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert "k" in m.last_error_detail() or "M" in m.last_error_detail()
+    rp = [fake] * 9
+    assert L.moe_route_project_topk(None, fake, None, 4, 256, 8, 2048, fake, *rp, None) == \
+        m.NVFP4MOE_ERR_NULL_ARG
+    assert L.moe_route_project_topk(fake, fake, None, 4, 256, 8, 2048, None, *rp, None) == \
+        m.NVFP4MOE_ERR_NULL_ARG  # logits buffer
+    assert L.moe_route_project_topk(fake, fake, None, 0, 256, 8, 2048, fake, *rp, None) == \
+        m.NVFP4MOE_ERR_BAD_SHAPE
+    assert L.moe_route_project_topk(fake, fake, None, 4, 256, 8, 256, fake, *rp, None) == \
+        m.NVFP4MOE_ERR_UNSUPPORTED  # H
+    assert L.moe_route_project_topk(fake, fake, None, 4, 257, 8, 2048, fake, *rp, None) == \
+        m.NVFP4MOE_ERR_UNSUPPORTED  # E
+    assert L.moe_route_project_topk(fake + 4, fake, None, 4, 256, 8, 2048, fake, *rp, None) == \
+        m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned x
 
 
 def _args(m, **kw):
