@@ -37,6 +37,12 @@ def lib():
         L.oracle_gemm.argtypes = [_vp, _i64, _i64, _vp, _vp, ctypes.c_float, _i64, _vp]
         L.oracle_gemm_fp8.restype = None
         L.oracle_gemm_fp8.argtypes = [_vp, _i64, _i64, _vp, ctypes.c_double, _i64, _vp]
+        L.oracle_quantize_nvfp4.restype = None
+        L.oracle_quantize_nvfp4.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
+        L.oracle_e4m3_rne.restype = ctypes.c_uint32
+        L.oracle_e4m3_rne.argtypes = [ctypes.c_float]
+        L.oracle_e2m1_rne.restype = ctypes.c_uint32
+        L.oracle_e2m1_rne.argtypes = [ctypes.c_float]
         L.oracle_router_logits.restype = None
         L.oracle_router_logits.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp]
         L.oracle_route_topk.restype = ctypes.c_int
@@ -116,6 +122,29 @@ def gemm_fp8(x_bf16, w_fp8, s) -> np.ndarray:
     y = np.empty((M, N), dtype=np.float64)
     lib().oracle_gemm_fp8(_p(x), M, K, _p(w), float(s), N, _p(y))
     return y
+
+
+def quantize_nvfp4(x_bf16):
+    """x: uint16 BF16 bits [G][N][K] (or [N][K]) -> (codes uint8 [G][N][K/2],
+    scales uint8 [G][N][K/16], g float32 [G]) by the amax recipe of oracle.cpp."""
+    x = _c(x_bf16, np.uint16)
+    if x.ndim == 2:
+        x = x[None]
+    G, N, K = x.shape
+    assert K % 16 == 0
+    codes = np.empty((G, N, K // 2), np.uint8)
+    scales = np.empty((G, N, K // 16), np.uint8)
+    g = np.empty(G, np.float32)
+    lib().oracle_quantize_nvfp4(_p(x), G, N, K, _p(codes), _p(scales), _p(g))
+    return codes, scales, g
+
+
+def e4m3_rne(t: float) -> int:
+    return int(lib().oracle_e4m3_rne(t))
+
+
+def e2m1_rne(v: float) -> int:
+    return int(lib().oracle_e2m1_rne(v))
 
 
 def router_logits(x_bf16, w_router_bf16) -> np.ndarray:

@@ -135,6 +135,87 @@ void oracle_router_logits(const uint16_t* x, int64_t M, int64_t H, const uint16_
     }
 }
 
+/* ---- quantization: BF16 -> canonical NVFP4 ----------------------------------------
+ * The pages say only that a BF16 head was turned into NVFP4 with NVIDIA's
+ * model optimizer (Elsa page, "Files": the lm_head quantization script) and
+ * give no recipe. The reading used here is the plain amax one, every division
+ * and product in FP32 (the precision the GPU kernel decides in):
+ *   g   = fl32(amax / 2688) over the whole matrix (2688 = 6 * 448: the largest
+ *         E2M1 magnitude times the largest E4M3 value), 1 if amax = 0;
+ *   s_b = E4M3 nearest to fl32(amax_b / fl32(6 g)), ties to the even code,
+ *         448 above 448 (amax_b over the 16 elements of block b along K);
+ *   q   = sign of x, magnitude the E2M1 nearest to fl32(|x| / fl32(s_b g)),
+ *         ties to the even code, 6 above 6; magnitude 0 when s_b g = 0.
+ * The nearest-value searches below scan the value tables directly. */
+
+/* Nearest non-negative finite E4M3 code to t >= 0, ties to the even code. */
+uint32_t oracle_e4m3_rne(float t) {
+  if (t >= 448.0f) return 0x7Eu;  // saturate (a distance search loses ties far out)
+  uint32_t best = 0;
+  double bd = std::numeric_limits<double>::infinity();
+  for (uint32_t c = 0; c <= 0x7E; ++c) {
+    const double d = std::fabs(oracle_e4m3(c) - (double)t);
+    if (d < bd || (d == bd && (c & 1u) == 0)) {
+      best = c;
+      bd = d;
+    }
+  }
+  return best;
+}
+
+/* Nearest E2M1 magnitude code (0..7) to v >= 0, ties to the even code. */
+uint32_t oracle_e2m1_rne(float v) {
+  if (v >= 6.0f) return 7u;  // saturate
+  uint32_t best = 0;
+  double bd = std::numeric_limits<double>::infinity();
+  for (uint32_t c = 0; c < 8; ++c) {
+    const double d = std::fabs(oracle_e2m1(c) - (double)v);
+    if (d < bd || (d == bd && (c & 1u) == 0)) {
+      best = c;
+      bd = d;
+    }
+  }
+  return best;
+}
+
+static inline float bf16_f32(uint16_t bits) {
+  const uint32_t u = (uint32_t)bits << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+void oracle_quantize_nvfp4(const uint16_t* x, int64_t G, int64_t N, int64_t K, uint8_t* codes,
+                           uint8_t* scales, float* g) {
+  for (int64_t gi = 0; gi < G; ++gi) {
+    const uint16_t* xm = x + gi * N * K;
+    float amax = 0.0f;
+    for (int64_t i = 0; i < N * K; ++i) amax = std::max(amax, std::fabs(bf16_f32(xm[i])));
+    const float gv = amax > 0.0f ? amax / 2688.0f : 1.0f;
+    g[gi] = gv;
+    const float six_g = 6.0f * gv;
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t b = 0; b < K / 16; ++b) {
+        const uint16_t* xb = xm + n * K + b * 16;
+        float amax_b = 0.0f;
+        for (int i = 0; i < 16; ++i) amax_b = std::max(amax_b, std::fabs(bf16_f32(xb[i])));
+        const uint32_t sc = oracle_e4m3_rne(amax_b / six_g);
+        scales[(gi * N + n) * (K / 16) + b] = (uint8_t)sc;
+        const float sg = (float)oracle_e4m3(sc) * gv;
+        for (int i = 0; i < 16; ++i) {
+          const float v = bf16_f32(xb[i]);
+          const uint32_t mag = sg > 0.0f ? oracle_e2m1_rne(std::fabs(v) / sg) : 0u;
+          const uint32_t q = (std::signbit(v) ? 8u : 0u) | mag;
+          uint8_t& byte = codes[(gi * N + n) * (K / 2) + (b * 16 + i) / 2];
+          if (i % 2 == 0)
+            byte = (uint8_t)q;
+          else
+            byte = (uint8_t)(byte | (q << 4));
+        }
+      }
+  }
+}
+
 /* ---- routing ----------------------------------------------------------------- */
 
 /* Does expert a come before expert b? Larger l' first, NaN after everything,

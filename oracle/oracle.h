@@ -15,6 +15,8 @@
  *     page, "Making decode faster", paragraph on skinny matrix multiplies),
  *     and with FP8 E4M3 weights under one scale per tensor ("An FP8 fast
  *     path" on the same page);
+ *   - quantization of BF16 matrices to NVFP4 (amax recipe: the pages name
+ *     only the tool that did it, in the "Files" list of the Elsa page);
  *   - the router projection (logits = x W_r^T, BF16 weights) in front of
  *     top-k routing ("The card and the model": a mixture-of-experts model);
  *   - top-k routing, grouping of (row, slot) pairs by expert, the expert
@@ -58,6 +60,14 @@ void oracle_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes,
  * [N][K] row-major, one scale s for the tensor. */
 void oracle_gemm_fp8(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w, double s,
                      int64_t N, double* y);
+
+/* BF16 [G][N][K] -> canonical NVFP4 (codes [G][N][K/2], scales [G][N][K/16],
+ * g [G]) by the amax recipe documented in oracle.cpp; K % 16 == 0. Finite
+ * inputs only (non-finite inputs: parity unpinned). */
+void oracle_quantize_nvfp4(const uint16_t* x, int64_t G, int64_t N, int64_t K, uint8_t* codes,
+                           uint8_t* scales, float* g);
+uint32_t oracle_e4m3_rne(float t);  /* nearest finite E4M3 code to t >= 0, ties to even */
+uint32_t oracle_e2m1_rne(float v);  /* nearest E2M1 magnitude code to v >= 0, ties to even */
 
 /* Router projection: logits[M][E] = x W_r^T in float64; x BF16 [M][H], w_r
  * BF16 [E][H]. */

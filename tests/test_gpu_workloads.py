@@ -84,10 +84,14 @@ def test_prefill_m256_zipf(m, gpu):
 
 
 @pytest.mark.parametrize("check_layers", [(0, 1, 20, 39)])
-def test_stack_40_layers_teacher_forced(m, gpu, check_layers):
+@pytest.mark.parametrize("router", [False, True])
+def test_stack_40_layers_teacher_forced(m, gpu, check_layers, router):
     """40 MoE blocks (routed + shared expert + residual) and a dense 2048->64
     projection per layer, run as a chain on the GPU. Checked layers are
-    recomputed by the oracle from the GPU's own BF16 input of that layer."""
+    recomputed by the oracle from the GPU's own BF16 input of that layer.
+    router=True: the logits come from each layer's own BF16 router matrix
+    applied to that layer's input on the GPU (routing follows the chain);
+    they are held to the tolerance, and the oracle routes the GPU's logits."""
     x_host = W.stack_x0()
     x = to_dev_bf16(x_host, gpu)
     worst = 0.0
@@ -95,12 +99,21 @@ def test_stack_40_layers_teacher_forced(m, gpu, check_layers):
         lay = W.stack_layer(l, x=x_host)
         d = upload_layer(lay, gpu, m)
         pw = pack(lay.extra["proj"], gpu, m)
-        r = m.moe_route_topk(d["logits"], lay.k)
+        if router:
+            wr = W.router_weights(seed=0, wl=4, layer=l)
+            logits, r = m.moe_route_project_topk(x, to_dev_bf16(wr, gpu), lay.k)
+        else:
+            r = m.moe_route_topk(d["logits"], lay.k)
         proj = m.nvfp4_skinny_gemm(x, pw)
         x_next = m.moe_nvfp4_decode(x, r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=x)
         torch.cuda.synchronize()
         if l in check_layers:
-            ids, w = oracle.route_topk(lay.logits, lay.k)
+            if router:
+                lg = logits.cpu().numpy()
+                worst = max(worst, tol_ratio(lg.astype(np.float64), oracle.router_logits(x_host, wr)))
+                ids, w = oracle.route_topk(lg, lay.k)
+            else:
+                ids, w = oracle.route_topk(lay.logits, lay.k)
             check_routing_exact(r, ids, w, lay.E)
             ref = oracle.moe_block_touched(lay, ids, w, residual=x_host)
             worst = max(worst, tol_ratio(dev_bf16_to_f64(x_next), ref))

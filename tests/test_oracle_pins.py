@@ -198,6 +198,118 @@ def test_gemm_special_cases():
     assert (oracle.gemm(x, codes, scales, 0.75) * 2 == oracle.gemm(x, codes, scales, 1.5)).all()
 
 
+# ---- quantization BF16 -> NVFP4 (amax recipe) --------------------------------------------
+
+def _f32(v):
+    return float(np.float32(v))
+
+
+def test_e4m3_rne_matches_torch():
+    """The oracle's nearest-code search against torch's own float32 ->
+    float8_e4m3fn conversion (round to nearest even) on every E4M3 value, every
+    midpoint between neighbours and the floats just either side of each."""
+    vals = sorted({oracle.e4m3(c) for c in range(0x7F)})
+    ts = set(vals)
+    for a, b in zip(vals, vals[1:]):
+        mid = np.float32((a + b) / 2)
+        ts.update([float(mid), float(np.nextafter(mid, np.float32(0))),
+                   float(np.nextafter(mid, np.float32(1e9)))])
+    rng = np.random.default_rng(3)
+    ts.update(float(v) for v in (2.0 ** rng.uniform(-12, 8.8, 2000)).astype(np.float32))
+    ts = np.array(sorted(t for t in ts if t <= 448.0), np.float32)
+    ref = torch.from_numpy(ts).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_rne(float(t)) for t in ts], np.uint8)
+    assert (got == ref).all()
+    assert oracle.e4m3_rne(449.0) == 0x7E and oracle.e4m3_rne(1e30) == 0x7E  # saturates
+
+
+def test_e2m1_rne_closed_form():
+    """Thresholds of round-to-nearest-even on {0, .5, 1, 1.5, 2, 3, 4, 6}:
+    midpoints go to the even code, everything above 5 to 6."""
+    table = [(0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6)]
+    for mid, code in table:
+        assert oracle.e2m1_rne(mid) == code, mid
+        lo, hi = np.nextafter(np.float32(mid), np.float32(0)), np.nextafter(np.float32(mid),
+                                                                             np.float32(9))
+        below = [c for c in range(8) if E2M1_TABLE[c] < mid][-1]
+        above = [c for c in range(8) if E2M1_TABLE[c] > mid][0]
+        assert oracle.e2m1_rne(float(lo)) == below and oracle.e2m1_rne(float(hi)) == above
+    for c in range(8):
+        assert oracle.e2m1_rne(E2M1_TABLE[c]) == c
+    assert oracle.e2m1_rne(6.5) == 7 and oracle.e2m1_rne(1e30) == 7
+
+
+def _nvfp4_with_full_blocks(rng, G, N, K, gexp):
+    """Codes with a +-6 in every 16-block, every finite positive scale code
+    in use, one 448 scale per matrix, g = 2^gexp: every value is a BF16 value
+    and each block's amax is exactly 6 s_b g."""
+    codes = rng.integers(0, 16, (G, N, K))
+    blocks = codes.reshape(G, N, K // 16, 16)
+    pos = rng.integers(0, 16, (G, N, K // 16))
+    np.put_along_axis(blocks, pos[..., None], (7 | (rng.integers(0, 2, pos.shape) << 3))[..., None],
+                      axis=-1)
+    codes = blocks.reshape(G, N, K)
+    scales = rng.integers(1, 0x7F, (G, N, K // 16)).astype(np.uint8)
+    scales[:, 0, 0] = 0x7E
+    g = np.full(G, 2.0 ** gexp, np.float32)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, scales, g
+
+
+@pytest.mark.parametrize("G,N,K,gexp", [(1, 4, 32, 0), (2, 3, 64, -12), (3, 5, 128, -7)])
+def test_quantize_inverts_exact_dequant(G, N, K, gexp):
+    """x = dequant(c, s, g) is exact in BF16 and its blocks meet the recipe's
+    fixed point (g = amax / 2688, s_b = amax_b / 6g, q = x / s_b g exactly),
+    so quantizing x must give back c, s and g bit for bit (a wrong nibble
+    order, block index or sign shows)."""
+    rng = np.random.default_rng(G * 100 + N + K)
+    codes, scales, g = _nvfp4_with_full_blocks(rng, G, N, K, gexp)
+    x = oracle.dequant(codes, scales, g)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    assert (xb.to(torch.float64).numpy() == x).all()
+    bits = xb.view(torch.int16).numpy().view(np.uint16)
+    qc, qs, qg = oracle.quantize_nvfp4(bits)
+    assert (qg == g).all()
+    assert (qs == scales).all()
+    assert (qc == codes).all()
+
+
+def test_quantize_special_cases():
+    K = 32
+    one = 0x3F80
+    # all zeros (either sign): g = 1, scales 0, codes carry the sign only
+    x = np.zeros((1, 2, K), np.uint16)
+    x[0, 1, 3] = 0x8000
+    c, s, g = oracle.quantize_nvfp4(x)
+    assert g[0] == 1.0 and (s == 0).all()
+    assert c[0, 1, 1] == 0x80 and (np.delete(c.ravel(), 17) == 0).all()
+    # g from the tensor amax; a block whose t rounds down saturates at 6
+    x = np.zeros((1, 1, K), np.uint16)
+    x[0, 0, 0] = 0x4528           # 2688: g = 1
+    xv = 6.0 * 1.0625 * 1.0      # block 1: t = 1.0625 (a tie) -> s = 1.0
+    x[0, 0, 16] = torch.tensor(xv, dtype=torch.bfloat16).view(torch.int16).item() & 0xFFFF
+    x[0, 0, 17] = one             # 1.0 / 1.0 -> code 2
+    c, s, g = oracle.quantize_nvfp4(x)
+    assert g[0] == 1.0 and s[0, 0, 0] == 0x7E and s[0, 0, 1] == 0x38
+    assert c[0, 0, 8] == (7 | (2 << 4))   # 6.375 -> 6 (saturated), 1.0 -> 1.0
+    # each value lands on the nearest point of its block's grid +-{0..6} s_b g
+    # (up to the FP32 rounding of x / s_b g at a midpoint); blocks whose scale
+    # rounded down saturate at 6 s_b g
+    xs = synth.normal_bf16(synth.key(6), (2, 8, 256), 0.0, 3.0)
+    xs[0, 2, 40] = 0x4400          # an outlier (512)
+    c, s, g = oracle.quantize_nvfp4(xs)
+    deq = oracle.dequant(c, s, g)
+    xd = bf16_to_f64(xs)
+    sg = np.repeat(torch_e4m3(s), 16, axis=-1) * g[:, None, None]
+    grid = np.array([E2M1_TABLE[c] for c in range(8)])
+    nearest = np.min(np.abs(np.abs(xd)[..., None] - grid * sg[..., None]), axis=-1)
+    err = np.abs(deq - xd)
+    sat = np.abs(xd) > 6 * sg
+    assert (err[~sat] <= nearest[~sat] + 1e-6 * np.abs(xd[~sat])).all()
+    assert (np.abs(deq[sat]) == 6 * sg[sat]).all()
+    assert (np.sign(deq) * np.sign(xd) >= 0).all()
+
+
 # ---- router projection ----------------------------------------------------------------
 
 @pytest.mark.parametrize("M,H,E", [(1, 16, 3), (3, 64, 9), (2, 96, 5)])
