@@ -93,6 +93,25 @@ int32_t nvfp4_pack(const uint8_t* codes, const uint8_t* scales, const float* g, 
 int32_t nvfp4_dequant_f32(const void* packed, int64_t G, int64_t N, int64_t K, int32_t apply_g,
                           int32_t path, float* out, hipStream_t stream);
 
+/* ---- quantization ------------------------------------------------------------------
+ *
+ * BF16 matrices x [G][N][K] (raw bits) -> canonical NVFP4: codes [G][N][K/2]
+ * (element 2b in the low nibble of byte b), E4M3 scales [G][N][K/16], FP32
+ * tensor scales g [G]; nvfp4_pack then gives the library layout. The pages
+ * name only the tool that quantized a BF16 head ([Elsa] "Files", the lm_head
+ * quantization script), not its recipe; this is the plain amax recipe, every
+ * division and product in FP32:
+ *   g[i] = amax_i / 2688 (6 * 448), or 1 when matrix i is all zeros;
+ *   scale of a 16-block = E4M3 nearest to amax_b / (6 g), ties to the even
+ *     code, saturating at 448;
+ *   code = sign(x) | E2M1 nearest to |x| / (scale * g), ties to the even
+ *     code, saturating at 6; magnitude 0 where scale * g = 0.
+ * Finite inputs (non-finite inputs give unspecified codes). g is used as
+ * scratch for the per-matrix maxima between the launches (four on `stream`).
+ * K % 16 == 0, G <= 65535; x 16-byte, codes 8-byte, g 4-byte aligned. */
+int32_t nvfp4_quantize(const uint16_t* x, int64_t G, int64_t N, int64_t K, uint8_t* codes,
+                       uint8_t* scales, float* g, hipStream_t stream);
+
 /* ---- dense skinny product ----------------------------------------------------------
  *
  * y[M][N] = bf16_rne( sum_k x[m][k] * W[n][k] ), one packed matrix (G = 1),

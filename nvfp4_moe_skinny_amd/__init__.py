@@ -65,6 +65,8 @@ def _load():
     L.nvfp4_packed_bytes.argtypes = [_i64, _i64, _i64]
     L.nvfp4_pack.restype = _i32
     L.nvfp4_pack.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]
+    L.nvfp4_quantize.restype = _i32
+    L.nvfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
     L.nvfp4_dequant_f32.restype = _i32
     L.nvfp4_dequant_f32.argtypes = [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp]
     L.nvfp4_skinny_gemm.restype = _i32
@@ -86,7 +88,7 @@ lib = _load()
 
 EXPORTS = ["nvfp4moe_strerror", "nvfp4moe_last_error_detail", "nvfp4moe_version",
            "fp8_skinny_gemm",
-           "nvfp4_packed_bytes", "nvfp4_pack", "nvfp4_dequant_f32", "nvfp4_skinny_gemm",
+           "nvfp4_packed_bytes", "nvfp4_pack", "nvfp4_quantize", "nvfp4_dequant_f32", "nvfp4_skinny_gemm",
            "moe_route_topk", "moe_route_project_topk", "moe_nvfp4_workspace_bytes", "moe_nvfp4_decode"]
 
 
@@ -153,6 +155,23 @@ def nvfp4_pack(codes: torch.Tensor, scales: torch.Tensor, g: torch.Tensor, strea
     _check(lib.nvfp4_pack(_ptr(codes), _ptr(scales), _ptr(g), G, N, K, _ptr(out),
                           _stream(stream)), "nvfp4_pack")
     return PackedNVFP4(out, G, N, K)
+
+
+def nvfp4_quantize(x: torch.Tensor, stream=None):
+    """x bfloat16 [G][N][K] (or [N][K]) -> canonical NVFP4 (codes uint8
+    [G][N][K/2], scales uint8 [G][N][K/16], g float32 [G]) on x's device."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    if x.dim() == 2:
+        x = x.unsqueeze(0)
+    x = x.contiguous()
+    G, N, K = x.shape
+    codes = torch.empty((G, N, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((G, N, K // 16), dtype=torch.uint8, device=x.device)
+    g = torch.empty(G, dtype=torch.float32, device=x.device)
+    _check(lib.nvfp4_quantize(_ptr(x), G, N, K, _ptr(codes), _ptr(scales), _ptr(g),
+                              _stream(stream)), "nvfp4_quantize")
+    return codes, scales, g
 
 
 def nvfp4_dequant_f32(w: PackedNVFP4, apply_g: bool = True, path: int = 0,

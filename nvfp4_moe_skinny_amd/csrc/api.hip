@@ -2,6 +2,7 @@
 //
 // Every call validates on the host, launches on the caller's stream and
 // returns; nothing is allocated, synchronised or read back.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -13,6 +14,7 @@
 #include "moe.hpp"
 #include "staged.hpp"
 #include "pack.hpp"
+#include "quant.hpp"
 #include "route.hpp"
 #include "router.hpp"
 
@@ -259,6 +261,33 @@ int32_t nvfp4_dequant_f32(const void* packed, int64_t G, int64_t N, int64_t K, i
   hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(chunks, 256, 1 << 16)), dim3(256), 0, stream,
                      (const uint8_t*)packed, G, N, K, (int)apply_g, (int)path, out);
   return launched("nvfp4_dequant_f32");
+}
+
+int32_t nvfp4_quantize(const uint16_t* x, int64_t G, int64_t N, int64_t K, uint8_t* codes,
+                       uint8_t* scales, float* g, hipStream_t stream) {
+  if (!x || !codes || !scales || !g) return fail(NVFP4MOE_ERR_NULL_ARG, "nvfp4_quantize: null");
+  if (G < 1 || N < 1 || K < 16) return fail(NVFP4MOE_ERR_BAD_SHAPE, "G, N >= 1 and K >= 16");
+  if (K % 16 != 0) return fail(NVFP4MOE_ERR_UNSUPPORTED, "K = %lld: need K %% 16 == 0", (long long)K);
+  if (G > 65535) return fail(NVFP4MOE_ERR_UNSUPPORTED, "G = %lld > 65535", (long long)G);
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(g, 4))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "x 16-byte, codes 8-byte, g 4-byte aligned");
+  const int64_t per = N * (K / 16);  // 16-element blocks per matrix
+  const int64_t total = per * G;
+  if ((total + kQuantThreads - 1) / kQuantThreads > ((int64_t)1 << 31) - 1)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "tensor too large");
+  uint32_t* amax = reinterpret_cast<uint32_t*>(g);
+  hipLaunchKernelGGL(quant_clear_kernel, dim3((unsigned)((G + kQuantThreads - 1) / kQuantThreads)),
+                     dim3(kQuantThreads), 0, stream, amax, G);
+  const int64_t bx = std::min<int64_t>((per + kQuantThreads - 1) / kQuantThreads,
+                                       kQuantMaxBlocksPerMatrix);
+  hipLaunchKernelGGL(quant_amax_kernel, dim3((unsigned)bx, (unsigned)G), dim3(kQuantThreads), 0,
+                     stream, x, per, amax);
+  hipLaunchKernelGGL(quant_blocks_kernel,
+                     dim3((unsigned)((total + kQuantThreads - 1) / kQuantThreads)),
+                     dim3(kQuantThreads), 0, stream, x, per, G, amax, codes, scales);
+  hipLaunchKernelGGL(quant_finish_kernel, dim3((unsigned)((G + kQuantThreads - 1) / kQuantThreads)),
+                     dim3(kQuantThreads), 0, stream, g, G);
+  return launched("nvfp4_quantize");
 }
 
 int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w_packed,

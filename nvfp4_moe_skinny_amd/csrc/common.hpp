@@ -111,6 +111,20 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v, int ctrl) {
   }
 }
 
+// Maximum over the wave, returned uniform: DPP within each 16-lane row, then
+// the four row results through readlane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32(v, kDppQuadXor1));
+  v = max(v, dpp_u32(v, kDppQuadXor2));
+  v = max(v, dpp_u32(v, kDppRowRor4));
+  v = max(v, dpp_u32(v, kDppRowRor8));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+
 // The value of lane l ^ 32 (every lane of the wave active). v_permlane32_swap
 // exchanges the upper half of its first operand with the lower half of its
 // second; with both operands v, result 1 holds the upper half's values in the

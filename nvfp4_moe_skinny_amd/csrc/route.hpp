@@ -30,20 +30,6 @@ __device__ __forceinline__ uint32_t route_ord(float l) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Maximum over the wave, returned uniform: DPP within each 16-lane row, then
-// the four row results through readlane.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32(v, kDppQuadXor1));
-  v = max(v, dpp_u32(v, kDppQuadXor2));
-  v = max(v, dpp_u32(v, kDppRowRor4));
-  v = max(v, dpp_u32(v, kDppRowRor8));
-  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-  return max(max(a, b), max(c, d));
-}
-
 // Sum of lanes 0..15 (the others may hold anything), returned uniform.
 __device__ __forceinline__ float row0_sum(float v) {
   v += __uint_as_float(dpp_u32(__float_as_uint(v), kDppQuadXor1));

@@ -76,6 +76,12 @@ def test_validation_errors_before_launch(m):
     assert L.moe_route_topk(fake, None, 0, 256, 8, *r, None) == m.NVFP4MOE_ERR_BAD_SHAPE
     assert L.moe_route_topk(fake, None, 2000, 256, 8, *r, None) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert "k" in m.last_error_detail() or "M" in m.last_error_detail()
+    assert L.nvfp4_quantize(None, 1, 8, 32, fake, fake, fake, None) == m.NVFP4MOE_ERR_NULL_ARG
+    assert L.nvfp4_quantize(fake, 0, 8, 32, fake, fake, fake, None) == m.NVFP4MOE_ERR_BAD_SHAPE
+    assert L.nvfp4_quantize(fake, 1, 8, 40, fake, fake, fake, None) == \
+        m.NVFP4MOE_ERR_UNSUPPORTED  # K % 16
+    assert L.nvfp4_quantize(fake + 8, 1, 8, 32, fake, fake, fake, None) == \
+        m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned x
     rp = [fake] * 9
     assert L.moe_route_project_topk(None, fake, None, 4, 256, 8, 2048, fake, *rp, None) == \
         m.NVFP4MOE_ERR_NULL_ARG
