@@ -82,17 +82,27 @@ def step_bytes(M, E, k, H, I, n_active, shared, bias):
     return b
 
 
+def decode_kernels(schedule, M):
+    """The launches of one decode call under the library's schedule choice."""
+    if schedule == 1:
+        return "moe_nvfp4_decode (one call: moe_decode_kernel)"
+    gate = "staged_gate_split_kernel" if M <= 16 else "staged_gate_kernel"
+    if schedule == 3 or (schedule == 0 and M <= 8):
+        return f"moe_nvfp4_decode (one call: {gate}, token_down_combine_kernel)"
+    return f"moe_nvfp4_decode (one call: {gate}, staged_down_kernel, staged_combine_kernel)"
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="m4", choices=["m4", "m16", "m256", "head32k", "head248k", "fp8qkv",
-                                             "fp8o"])
+                                             "fp8o", "router", "quant"])
     p.add_argument("--rows", type=int, default=0, help="rows M of a skinny-GEMM workload")
     p.add_argument("--dense-min-rows", type=int, default=0,
                    help="rows from which a slot uses MFMA (0 = library default)")
-    p.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2],
+    p.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2, 3],
                    help="0 = library choice, 1 = one launch, 2 = three launches")
     p.add_argument("--copies", type=int, default=0, help="weight sets cycled (0: >= 1 GB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -129,6 +139,10 @@ def main():
         return bench_head(args)
     if args.workload.startswith("fp8"):
         return bench_fp8(args)
+    if args.workload == "router":
+        return bench_router(args)
+    if args.workload == "quant":
+        return bench_quant(args)
     import torch
 
     import nvfp4_moe_skinny_amd as m
@@ -278,10 +292,7 @@ def main():
         "touched_experts_mean": float(np.mean(n_act)),
         "eager_ms_per_step": round(eager_ms, 4),
         "roofline": {"bound": "hbm",
-                     "kernel": ("moe_nvfp4_decode (one call: moe_decode_kernel)"
-                                if args.schedule == 1 else
-                                "moe_nvfp4_decode (one call: staged_gate_kernel, "
-                                "staged_down_kernel, staged_combine_kernel)"),
+                     "kernel": decode_kernels(args.schedule, M),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic() if args.workload == "m4" else None,
@@ -366,6 +377,96 @@ def bench_fp8(args):
         "config": {"workload": f"fp8_skinny_gemm_m{M}_k{K}_n{N}", "M": M, "K": K, "N": N,
                    "weights": "fp8 e4m3 + one f32 tensor scale", "weight_copies": copies,
                    "timing": "hip graph replay, events"},
+        "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes,
+    }), flush=True)
+    return 0
+
+
+def bench_router(args):
+    """Router projection + top-k + grouping (moe_route_project_topk): M rows
+    (default 4) of BF16 x [M][2048] times a BF16 router [256][2048], k = 8.
+    Router copies cycled so the 1 MB matrix comes from HBM. Not the headline."""
+    import torch
+
+    import nvfp4_moe_skinny_amd as m
+    from synth import workloads as W
+    from tests.helpers import to_dev_bf16
+
+    dev = torch.device("cuda:0")
+    M, E, H, k = args.rows or 4, 256, 2048, 8
+    x = to_dev_bf16(W.normal_bf16(W.key(0, 9, 0, W.T_X, 0), (M, H)), dev)
+    wr = to_dev_bf16(W.router_weights(seed=0, wl=9), dev)
+    copies = args.copies or 300
+    wrs = [wr.clone() for _ in range(copies)]
+    bufs = [m.routing_buffers(M, E, k, dev) for _ in range(copies)]
+    logits = [torch.empty((M, E), dtype=torch.float32, device=dev) for _ in range(copies)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        j = i % copies
+        m.moe_route_project_topk(x, wrs[j], k, out=bufs[j], logits=logits[j])
+
+    ms, n_steps = time_graph(step, copies, args)
+    step_bytes = E * H * 2 + M * H * 2 + M * E * 4 * 2 + M * k * 8
+    print(json.dumps({
+        "metric": "router projection + top-k latency", "value": round(ms * 1e3, 3),
+        "unit": "us", "n_gpus": 1, "steps": n_steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"route_project_m{M}_e{E}_h{H}_k{k}", "M": M, "E": E, "H": H,
+                   "top_k": k, "router_copies": copies, "timing": "hip graph replay, events"},
+        "achieved_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 2), "bytes_per_step": step_bytes,
+    }), flush=True)
+    return 0
+
+
+def bench_quant(args):
+    """Device quantizer (nvfp4_quantize) over one layer's gate_up expert set,
+    BF16 [256][1024][2048] (1 GiB in, 0.28 GiB out). 32 seeded matrices are
+    generated on the host and tiled to 256 on the device. Not the headline."""
+    import torch
+
+    import nvfp4_moe_skinny_amd as m
+    from synth import workloads as W
+    from tests.helpers import to_dev_bf16
+
+    dev = torch.device("cuda:0")
+    G, N, K = 256, 1024, 2048
+    base = to_dev_bf16(W.normal_bf16(W.key(0, 8, 0, W.T_X, 0), (32, N, K), 0.0, 0.02), dev)
+    x = base.repeat(G // 32, 1, 1).contiguous()
+    del base
+    codes = torch.empty((G, N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((G, N, K // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty(G, dtype=torch.float32, device=dev)
+    L = m.lib
+    ptrs = (x.data_ptr(), codes.data_ptr(), scales.data_ptr(), g.data_ptr())
+
+    def call():
+        st = L.nvfp4_quantize(ptrs[0], G, N, K, ptrs[1], ptrs[2], ptrs[3],
+                              torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"nvfp4_quantize: {st}")
+
+    for _ in range(max(2, min(args.warmup, 5))):
+        call()
+    torch.cuda.synchronize()
+    n = max(3, min(args.steps, 20))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(n):
+        call()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / n
+    step_bytes = G * N * K * 2 + G * N * (K // 2 + K // 16) + G * 4  # x once (two passes read it twice)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "NVFP4 quantizer achieved HBM GB/s", "value": round(gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"nvfp4_quantize_g{G}_n{N}_k{K}", "G": G, "N": N, "K": K,
+                   "timing": "eager launches, events"},
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes,
     }), flush=True)
     return 0

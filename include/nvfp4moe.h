@@ -196,7 +196,8 @@ typedef struct moe_nvfp4_args {
   int64_t M, E, k, H, I;
   int64_t dense_min_rows;     /* three-launch schedule: slots with at least this many rows
                                  use BF16 MFMA (0 = library default, 16; above M = never) */
-  int32_t schedule;           /* 0 = library choice, 1 = one launch, 2 = three launches */
+  int32_t schedule;           /* 0 = library choice, 1 = one launch, 2 = three launches,
+                                 3 = two launches (per-row down + combine) */
 } moe_nvfp4_args;
 
 /* Workspace bytes for moe_nvfp4_decode: a control block of counters, then h
@@ -219,16 +220,25 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
  * with FP32 accumulation and FP32 h. The slot sum runs in j order, then the
  * shared term, then the residual; the result is bit-reproducible from run to
  * run (no floating-point atomics).
- * Schedules: three launches (gate_up, down, combine; the default), or one
- * launch (every tile item of gate_up and down in one grid, exchanging h and y
- * through the workspace with flagged words). In the three-launch schedule,
+ * Schedules: three launches (gate_up, down, combine), two launches (gate_up,
+ * then one block per (row, down tile) that runs the row's k pairs (+ the
+ * shared expert) on that tile and sums them in place: no y round trip and no
+ * combine launch, at the cost of reading a tile once per pair instead of once
+ * per expert, which with few rows is nearly the same set), or one launch
+ * (every tile item of gate_up and down in one grid, exchanging h and y
+ * through the workspace with flagged words). The library's choice (0) is two
+ * launches for M <= 8 when M < dense_min_rows or the shape has no MFMA path,
+ * else three; schedule 3 asks for two launches and returns
+ * NVFP4MOE_ERR_UNSUPPORTED unless M < dense_min_rows or the shape has no
+ * MFMA path (the per-row kernel needs FP32 h for every pair). In the
+ * two- and three-launch schedules,
  * when H = 2048 and I = 512,
  * slots with at least dense_min_rows rows run on BF16 MFMA: weights exact in
  * BF16, x as stored, h as a hi + lo BF16 pair (relative error <= 2^-17).
  * Extra support-set conditions: H and I are each 32 * 2^j in [256, 2048], and
  * I is a multiple of 16384 / H (gate and up halves start on a tile boundary).
  * Returns NVFP4MOE_ERR_WORKSPACE if the workspace is too small and
- * NVFP4MOE_ERR_BAD_SHAPE for a schedule other than 0, 1 or 2. */
+ * NVFP4MOE_ERR_BAD_SHAPE for a schedule other than 0, 1, 2 or 3. */
 int32_t moe_nvfp4_decode(const moe_nvfp4_args* args, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -47,7 +47,7 @@ class MoeArgs(ctypes.Structure):
     ]
 
 # moe_nvfp4_args.schedule
-SCHEDULE_AUTO, SCHEDULE_ONE_LAUNCH, SCHEDULE_THREE_LAUNCHES = 0, 1, 2
+SCHEDULE_AUTO, SCHEDULE_ONE_LAUNCH, SCHEDULE_THREE_LAUNCHES, SCHEDULE_TWO_LAUNCHES = 0, 1, 2, 3
 
 
 def _load():
@@ -304,7 +304,8 @@ def moe_nvfp4_decode(x: torch.Tensor, routing: Routing, w_gate_up: PackedNVFP4,
                      out: Optional[torch.Tensor] = None, schedule: int = SCHEDULE_AUTO,
                      dense_min_rows: int = 0) -> torch.Tensor:
     """x bfloat16 [M][H] -> bfloat16 [M][H] (routed experts + shared + residual).
-    schedule: SCHEDULE_AUTO / SCHEDULE_ONE_LAUNCH / SCHEDULE_THREE_LAUNCHES;
+    schedule: SCHEDULE_AUTO / SCHEDULE_ONE_LAUNCH / SCHEDULE_THREE_LAUNCHES /
+    SCHEDULE_TWO_LAUNCHES;
     dense_min_rows: rows from which a slot uses MFMA (0 = library default)."""
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bfloat16")

@@ -104,9 +104,14 @@ int32_t launch_staged(const MoeParams& p, hipStream_t s) {
 
 // One row per batch: gate_up with two waves per item (gate tile, up tile).
 template <int LH, int LI, bool DENSE>
-int32_t launch_staged_split(const MoeParams& p, hipStream_t s) {
+int32_t launch_staged_split(const MoeParams& p, bool token_major, hipStream_t s) {
   const int grid = p.slots * p.P;
   hipLaunchKernelGGL((staged_gate_split_kernel<LH, DENSE>), dim3(grid), dim3(128), 0, s, p);
+  if (token_major) {
+    hipLaunchKernelGGL((token_down_combine_kernel<LI>), dim3(p.M * p.P),
+                       dim3((p.k + p.has_shared) * 64), 0, s, p);
+    return launched("moe_nvfp4_decode");
+  }
   hipLaunchKernelGGL((staged_down_kernel<LI, 1, DENSE>), dim3(grid), dim3(64), 0, s, p);
   const int64_t outs = (int64_t)p.M * p.H;
   hipLaunchKernelGGL(staged_combine_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s,
@@ -116,10 +121,11 @@ int32_t launch_staged_split(const MoeParams& p, hipStream_t s) {
 
 // Rows per batch: gate_up 1, 2 or 4, down at most 2 (register budget); the
 // shapes without MFMA take one row at a time.
-int32_t launch_staged_rows(const MoeParams& p, bool specialised, int rmax, hipStream_t s) {
-  if (rmax == 1)
-    return specialised ? launch_staged_split<64, 16, true>(p, s)
-                       : launch_staged_split<0, 0, false>(p, s);
+int32_t launch_staged_rows(const MoeParams& p, bool specialised, int rmax, bool token_major,
+                           hipStream_t s) {
+  if (rmax == 1 || token_major)
+    return specialised ? launch_staged_split<64, 16, true>(p, token_major, s)
+                       : launch_staged_split<0, 0, false>(p, token_major, s);
   if (!specialised) return launch_staged<0, 0, 1, 1, false>(p, s);
   switch (rmax) {
     case 1: return launch_staged<64, 16, 1, 1, true>(p, s);
@@ -393,7 +399,7 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
 
 int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
   if (!a) return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_decode: args is null");
-  if (!a->x || !a->w || !a->offsets || !a->pairs || !a->active || !a->active_offsets ||
+  if (!a->x || !a->ids || !a->w || !a->offsets || !a->pairs || !a->active || !a->active_offsets ||
       !a->n_active ||
       !a->w_gate_up || !a->w_down || !a->out || !a->workspace)
     return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_decode: a required pointer is null");
@@ -410,8 +416,9 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "I = %lld must be a multiple of 16384 / H = %lld",
                 (long long)I, (long long)rows_per_tile(H));
   if (M * k + M > (int64_t)1 << 24) return fail(NVFP4MOE_ERR_UNSUPPORTED, "M too large");
-  if (a->schedule < 0 || a->schedule > 2)
-    return fail(NVFP4MOE_ERR_BAD_SHAPE, "schedule must be 0, 1 or 2 (got %d)", (int)a->schedule);
+  if (a->schedule < 0 || a->schedule > 3)
+    return fail(NVFP4MOE_ERR_BAD_SHAPE, "schedule must be 0, 1, 2 or 3 (got %d)",
+                (int)a->schedule);
   const bool shared = a->shared_gate_up != nullptr;
   const WsLayout ws = ws_layout(M, E, k, H, I, shared);
   if (a->workspace_bytes < ws.total)
@@ -426,6 +433,7 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
   MoeParams p;
   std::memset(&p, 0, sizeof(p));
   p.x = a->x;
+  p.ids = a->ids;
   p.w = a->w;
   p.offsets = a->offsets;
   p.pairs = a->pairs;
@@ -475,10 +483,18 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
   // the staged kernels are at least as fast as the one-launch exchange
   const bool staged = a->schedule != 1;
   if (staged) {
+    // per-row down + combine needs FP32 h for every pair: no slot (the shared
+    // one has M rows) may take the MFMA gate_up path
+    const bool valu_h = M < p.dense_min_rows || !specialised;
+    if (a->schedule == 3 && !valu_h)
+      return fail(NVFP4MOE_ERR_UNSUPPORTED,
+                  "schedule 3 needs M < dense_min_rows (FP32 h for every pair)");
+    const bool token_major =
+        a->schedule == 3 || (a->schedule == 0 && valu_h && M <= kTokenMajorMaxRows);
     // one row per batch keeps these kernels at three waves per SIMD; slots
     // with many rows go to MFMA (specialised shapes) or take more batches
     const int rmax_s = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    return launch_staged_rows(p, specialised, rmax_s, stream);
+    return launch_staged_rows(p, specialised, rmax_s, token_major, stream);
   }
   p.spin_limit = 1u << 22;
   int rmax = rows_per_batch(M);

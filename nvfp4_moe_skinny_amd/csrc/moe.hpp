@@ -46,6 +46,7 @@ namespace nvfp4moe {
 
 struct MoeParams {
   const uint16_t* x;
+  const int32_t* ids;
   const float* w;
   const int32_t* offsets;
   const int32_t* pairs;

@@ -433,4 +433,55 @@ __global__ void __launch_bounds__(256) staged_combine_kernel(MoeParams p) {
   p.out[idx] = f32_to_bf16_rne(acc);
 }
 
+
+// ---- down + combine per row (few rows) --------------------------------------------------
+
+// Row counts up to this take the two-launch path below by default.
+constexpr int kTokenMajorMaxRows = 8;
+
+// One block per (row m, down tile t), one wave per slot j of the row (plus one
+// for the shared expert): wave j multiplies its pair's h row with tile t of
+// expert ids[m][j], then the block adds the tile's outputs in j order (+ the
+// shared term) (+ residual) and writes them as BF16, with the same arithmetic
+// as staged_combine_kernel. With a few rows nearly every pair has its own
+// expert, so reading a tile per pair rather than per expert costs almost no
+// extra bytes, and y never leaves the chip (no combine launch). h must be
+// FP32 words: every slot took the VALU gate_up path.
+template <int LIC>
+__global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel(MoeParams p) {
+  __shared__ float ys[kMaxTopK + 1][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = blockIdx.x / p.P, t = blockIdx.x % p.P;
+  const int L = LIC ? LIC : p.LI;
+  const int rpt = 16384 / p.I;  // output rows of a down tile
+  {
+    const bool sh = wave == p.k;  // the shared expert's wave (only with has_shared)
+    const int pair = sh ? p.M * p.k + m : m * p.k + wave;
+    const int e = sh ? 0 : p.ids[pair];
+    const uint8_t* tile =
+        (sh ? p.sdn : p.dn + (int64_t)e * p.dn_mat_bytes) + (int64_t)t * kTileBytes;
+    const float g = sh ? p.sdn_g[0] : p.dn_g[e];
+    TileRegs T;
+    float hr[1][32];
+    load_tile(tile, lane, T);
+    load_h_f32(p.hp, p.I, pair, true, 32 * (lane % L), hr[0]);
+    float part[1][8];
+    tile_dot_f32<1>(T, hr, part);
+    reduce_slabs_rt<LIC>(part[0], lane, L);
+    if (reduced_writer_rt(lane, L)) ys[wave][reduced_row(lane, L)] = part[0][0] * g;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < rpt) {
+    const int r = threadIdx.x;
+    const int64_t o = (int64_t)m * p.H + t * rpt + r;
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < p.k) acc += p.w[m * p.k + j] * ys[j][r];
+    if (p.has_shared) acc += ys[p.k][r];
+    if (p.residual) acc += bf16_to_f32(p.residual[o]);
+    p.out[o] = f32_to_bf16_rne(acc);
+  }
+}
+
 }  // namespace nvfp4moe

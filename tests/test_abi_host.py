@@ -128,7 +128,10 @@ def test_decode_validation(m):
     assert dec(_args(m, workspace_bytes=need - 1)) == m.NVFP4MOE_ERR_WORKSPACE
     assert "workspace" in m.last_error_detail()
     assert dec(_args(m, x=4096 + 8)) == m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned
-    assert dec(_args(m, schedule=3)) == m.NVFP4MOE_ERR_BAD_SHAPE
+    assert dec(_args(m, schedule=4)) == m.NVFP4MOE_ERR_BAD_SHAPE
+    # two launches need FP32 h for every pair: no MFMA slot (M < dense_min_rows)
+    assert dec(_args(m, schedule=3, dense_min_rows=4)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert dec(_args(m, ids=None)) == m.NVFP4MOE_ERR_NULL_ARG
     assert dec(_args(m, schedule=-1)) == m.NVFP4MOE_ERR_BAD_SHAPE
     # h [M*k][I] + y [M*k][H] as 8-byte (value, flag) words, then as 4-byte words
     assert need >= 4 * 8 * (512 + 2048) * (8 + 4)

@@ -18,7 +18,7 @@ def m(gpu):
 
 
 @pytest.mark.parametrize("M,shared,schedule", [(4, False, 1), (16, True, 1), (16, True, 2),
-                                               (4, False, 2)])
+                                               (4, False, 2), (4, False, 3), (8, True, 3)])
 def test_graph_replay_matches_eager(m, gpu, M, shared, schedule):
     lays = [moe_layer(seed=s, wl=400, layer=s, M=M, E_=64, H_=2048, I_=512, k=8, bias=shared,
                       shared=shared) for s in range(3)]

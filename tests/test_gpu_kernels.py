@@ -129,7 +129,7 @@ def _run_block(m, gpu, lay, residual=None, **kw):
     return r, dev_bf16_to_f64(out)
 
 
-@pytest.mark.parametrize("schedule", [1, 2])
+@pytest.mark.parametrize("schedule", [1, 2, 3])
 @pytest.mark.parametrize("M,E,H,I,k,shared,resid", [
     (1, 16, 256, 256, 4, False, False), (3, 16, 256, 256, 4, True, False),
     (8, 16, 256, 512, 4, False, True), (17, 16, 512, 256, 4, True, True),
@@ -140,7 +140,9 @@ def _run_block(m, gpu, lay, residual=None, **kw):
 def test_moe_block_small(m, gpu, M, E, H, I, k, shared, resid, schedule):
     lay = moe_layer(seed=M + E, wl=200, M=M, E_=E, H_=H, I_=I, k=k, shared=shared)
     residual = synth.normal_bf16(synth.key(5, 201, M), (M, H)) if resid else None
-    r, out = _run_block(m, gpu, lay, residual, schedule=schedule)
+    # the two-launch schedule takes any M once no slot uses MFMA
+    kw = dict(dense_min_rows=M + 1) if schedule == 3 else {}
+    r, out = _run_block(m, gpu, lay, residual, schedule=schedule, **kw)
     ids, w = oracle.route_topk(lay.logits, k, lay.bias)
     check_routing_exact(r, ids, w, E)
     ref = oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down, lay.shared_gate_up,
