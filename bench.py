@@ -36,7 +36,8 @@ CPU_LAYERS = 12  # weight copies kept on the host for the CPU-baseline sample
 
 
 # the device code of one moe_nvfp4_decode call (all of its launches)
-DECODE_SOURCES = ("common.hpp", "tile.hpp", "dense.hpp", "moe.hpp", "staged.hpp", "api.hip")
+DECODE_SOURCES = ("common.hpp", "tile.hpp", "dense.hpp", "moe.hpp", "staged.hpp", "route.hpp",
+                  "fused.hpp", "api.hip")
 
 
 def kernel_source_hash():
@@ -72,13 +73,14 @@ def expert_bytes(H, I):
     return gu + dn
 
 
-def step_bytes(M, E, k, H, I, n_active, shared, bias):
+def step_bytes(M, E, k, H, I, n_active, shared, bias, grouped=True):
     b = n_active * expert_bytes(H, I) + (expert_bytes(H, I) if shared else 0)
     b += M * H * 2 * 2          # x in, out
     b += M * E * 4              # logits
     b += E * 4 if bias else 0   # logit bias
     b += M * k * (4 + 4) * 2    # ids, w written then read
-    b += (E + E + 1 + E + 1) * 4 + M * k * 4 * 2  # counts, offsets, active, n_active, pairs
+    if grouped:                 # counts, offsets, active, n_active, pairs
+        b += (E + E + 1 + E + 1) * 4 + M * k * 4 * 2
     return b
 
 
@@ -104,6 +106,9 @@ def parse():
                    help="rows from which a slot uses MFMA (0 = library default)")
     p.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2, 3],
                    help="0 = library choice, 1 = one launch, 2 = three launches")
+    p.add_argument("--path", default="auto", choices=["auto", "separate", "fused"],
+                   help="separate: moe_route_topk + moe_nvfp4_decode; fused: "
+                        "moe_nvfp4_route_decode (few rows); auto: fused for M <= 8")
     p.add_argument("--copies", type=int, default=0, help="weight sets cycled (0: >= 1 GB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -198,13 +203,26 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    # one step of the hot path: (weight copy c, logits/x set j)
-    def step(i):
+    fused = args.path == "fused" or (args.path == "auto" and args.schedule == 0 and M <= 8)
+
+    # one decode call: routed experts + shared + combine (fused: with the routing)
+    def decode_call(i):
         c, j = i % copies, i % n_sets
         gu, dn, sgu, sdn = weights[c]
-        r = m.moe_route_topk(lg[j], k, bs[j], out=routes[j])
-        m.moe_nvfp4_decode(xs[j], r, gu, dn, sgu, sdn, workspace=ws, out=outs[j],
-                           schedule=args.schedule, dense_min_rows=args.dense_min_rows)
+        if fused:
+            m.moe_nvfp4_route_decode(xs[j], lg[j], k, gu, dn, bs[j], sgu, sdn, workspace=ws,
+                                     out=outs[j], ids=routes[j].ids, w=routes[j].w,
+                                     dense_min_rows=args.dense_min_rows)
+        else:
+            m.moe_nvfp4_decode(xs[j], routes[j], gu, dn, sgu, sdn, workspace=ws, out=outs[j],
+                               schedule=args.schedule, dense_min_rows=args.dense_min_rows)
+
+    # one step of the hot path: (weight copy c, logits/x set j)
+    def step(i):
+        j = i % n_sets
+        if not fused:
+            m.moe_route_topk(lg[j], k, bs[j], out=routes[j])
+        decode_call(i)
 
     # the graph holds S steps: step i uses weight copy i % copies and set i % n_sets
     S = copies * int(np.ceil(n_sets / copies))
@@ -238,8 +256,9 @@ def main():
     ms_per_step = gpu_ms / steps
 
     # bytes from each step's actual routing (read back after the timed region)
-    n_act = np.array([int(routes[j].n_active.item()) for j in range(n_sets)])
-    bytes_per_set = np.array([step_bytes(M, E, k, H, I, int(na), shared, bias) for na in n_act])
+    n_act = np.array([len(np.unique(routes[j].ids.cpu().numpy())) for j in range(n_sets)])
+    bytes_per_set = np.array([step_bytes(M, E, k, H, I, int(na), shared, bias, not fused)
+                              for na in n_act])
     mean_bytes = float(np.mean([bytes_per_set[i % n_sets] for i in range(S)]))
     gbs = mean_bytes / (ms_per_step * 1e-3) / 1e9
     rows_per_s = M / (ms_per_step * 1e-3)
@@ -250,15 +269,18 @@ def main():
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.eager_calls)]
     decode_bytes = []
     for i in range(args.eager_calls):
-        c, j = i % copies, i % n_sets
-        gu, dn, sgu, sdn = weights[c]
-        r = m.moe_route_topk(lg[j], k, bs[j], out=routes[j])
+        j = i % n_sets
+        if not fused:
+            m.moe_route_topk(lg[j], k, bs[j], out=routes[j])
         starts[i].record(stream)
-        m.moe_nvfp4_decode(xs[j], r, gu, dn, sgu, sdn, workspace=ws, out=outs[j],
-                           schedule=args.schedule, dense_min_rows=args.dense_min_rows)
+        decode_call(i)
         ends[i].record(stream)
-        decode_bytes.append(n_act[j] * expert_bytes(H, I) + (expert_bytes(H, I) if shared else 0)
-                            + M * H * 4 + M * k * 8 + (E + 1 + E + 1) * 4 + M * k * 4)
+        b = n_act[j] * expert_bytes(H, I) + (expert_bytes(H, I) if shared else 0) + M * H * 4
+        if fused:  # logits (+ bias) in, ids and w out
+            b += M * E * 4 + (E * 4 if bias else 0) + M * k * 8
+        else:      # ids, w and the grouping arrays in
+            b += M * k * 8 + (E + 1 + E + 1) * 4 + M * k * 4
+        decode_bytes.append(b)
     torch.cuda.synchronize()
     dec_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])[20:]
     dec_bytes = float(np.mean(decode_bytes[20:]))
@@ -285,14 +307,18 @@ def main():
                    "accumulate": "f32", "shared_expert": shared, "logit_bias": bias,
                    "weight_copies": copies, "logit_sets": n_sets, "graph_steps": S,
                    "timing": "hip graph replay, events",
-                   "schedule": args.schedule, "dense_min_rows": args.dense_min_rows},
+                   "schedule": args.schedule, "dense_min_rows": args.dense_min_rows,
+                   "path": "moe_nvfp4_route_decode" if fused
+                           else "moe_route_topk + moe_nvfp4_decode"},
         "rows_per_s": round(rows_per_s, 1),
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "bytes_per_step": round(mean_bytes),
         "touched_experts_mean": float(np.mean(n_act)),
         "eager_ms_per_step": round(eager_ms, 4),
         "roofline": {"bound": "hbm",
-                     "kernel": decode_kernels(args.schedule, M),
+                     "kernel": ("moe_nvfp4_route_decode (one call: fused_route_gate_kernel, "
+                                "token_down_combine_kernel)" if fused
+                                else decode_kernels(args.schedule, M)),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic() if args.workload == "m4" else None,

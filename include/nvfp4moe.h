@@ -241,6 +241,23 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
  * NVFP4MOE_ERR_BAD_SHAPE for a schedule other than 0, 1, 2 or 3. */
 int32_t moe_nvfp4_decode(const moe_nvfp4_args* args, hipStream_t stream);
 
+/* moe_route_topk (top-k and weights only, no grouping) and moe_nvfp4_decode
+ * in one call of two launches, for few rows: the routing is done inside the
+ * gate_up launch, one block per (pair, tile) selecting its row's experts with
+ * the same per-row routine as moe_route_topk (so ids and w are bit-identical
+ * to it), and the down launch sums each row's pairs in place (schedule 3 of
+ * moe_nvfp4_decode). logits [M][E] FP32 and bias [E] FP32 (or NULL) as in
+ * moe_route_topk. In args, ids [M][k] and w [M][k] are OUTPUTS (written with
+ * the routing; the const of the struct fields is cast away), the grouping
+ * arrays (offsets, pairs, active, active_offsets, n_active) and schedule are
+ * not used; everything else is as for moe_nvfp4_decode, the output
+ * bit-identical to moe_route_topk + moe_nvfp4_decode with schedule 3.
+ * Reading a weight tile per pair rather than per expert suits small M (up to
+ * about 8); NVFP4MOE_ERR_UNSUPPORTED when H = 2048, I = 512 and M >=
+ * dense_min_rows. */
+int32_t moe_nvfp4_route_decode(const moe_nvfp4_args* args, const float* logits, const float* bias,
+                               hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

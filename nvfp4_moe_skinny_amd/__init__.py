@@ -81,6 +81,8 @@ def _load():
     L.moe_nvfp4_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32]
     L.moe_nvfp4_decode.restype = _i32
     L.moe_nvfp4_decode.argtypes = [ctypes.POINTER(MoeArgs), _vp]
+    L.moe_nvfp4_route_decode.restype = _i32
+    L.moe_nvfp4_route_decode.argtypes = [ctypes.POINTER(MoeArgs), _vp, _vp, _vp]
     return L
 
 
@@ -89,7 +91,8 @@ lib = _load()
 EXPORTS = ["nvfp4moe_strerror", "nvfp4moe_last_error_detail", "nvfp4moe_version",
            "fp8_skinny_gemm",
            "nvfp4_packed_bytes", "nvfp4_pack", "nvfp4_quantize", "nvfp4_dequant_f32", "nvfp4_skinny_gemm",
-           "moe_route_topk", "moe_route_project_topk", "moe_nvfp4_workspace_bytes", "moe_nvfp4_decode"]
+           "moe_route_topk", "moe_route_project_topk", "moe_nvfp4_workspace_bytes", "moe_nvfp4_decode",
+           "moe_nvfp4_route_decode"]
 
 
 def strerror(status: int) -> str:
@@ -334,3 +337,50 @@ def moe_nvfp4_decode(x: torch.Tensor, routing: Routing, w_gate_up: PackedNVFP4,
     a.dense_min_rows, a.schedule = dense_min_rows, schedule
     _check(lib.moe_nvfp4_decode(ctypes.byref(a), _stream(stream)), "moe_nvfp4_decode")
     return out
+
+
+def moe_nvfp4_route_decode(x: torch.Tensor, logits: torch.Tensor, k: int,
+                           w_gate_up: PackedNVFP4, w_down: PackedNVFP4,
+                           bias: Optional[torch.Tensor] = None,
+                           shared_gate_up: Optional[PackedNVFP4] = None,
+                           shared_down: Optional[PackedNVFP4] = None,
+                           residual: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None,
+                           out: Optional[torch.Tensor] = None,
+                           ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
+                           dense_min_rows: int = 0):
+    """Routing (top-k + weights) and the MoE block in two launches, for few
+    rows: x bfloat16 [M][H], logits float32 [M][E] (+ bias float32 [E]) ->
+    (out bfloat16 [M][H], ids int32 [M][k], w float32 [M][k])."""
+    if x.dtype != torch.bfloat16 or logits.dtype != torch.float32:
+        raise ValueError("x must be bfloat16 and logits float32")
+    if bias is not None and bias.dtype != torch.float32:
+        raise ValueError("bias must be float32")
+    M, H = x.shape
+    E, I = w_gate_up.G, w_down.K
+    if w_gate_up.N != 2 * I or w_gate_up.K != H or w_down.N != H or w_down.G != E:
+        raise ValueError("expert weight shapes do not match x")
+    if tuple(logits.shape) != (M, E):
+        raise ValueError("logits must be [M][E]")
+    has_shared = shared_gate_up is not None
+    if workspace is None:
+        workspace = moe_workspace(M, E, k, H, I, has_shared, x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    if ids is None:
+        ids = torch.empty((M, k), dtype=torch.int32, device=x.device)
+    if w is None:
+        w = torch.empty((M, k), dtype=torch.float32, device=x.device)
+    a = MoeArgs()
+    a.x, a.ids, a.w = _ptr(x), _ptr(ids), _ptr(w)
+    a.w_gate_up, a.w_down = _ptr(w_gate_up.data), _ptr(w_down.data)
+    a.shared_gate_up = _ptr(shared_gate_up.data) if has_shared else None
+    a.shared_down = _ptr(shared_down.data) if has_shared else None
+    a.residual = _ptr(residual)
+    a.out = _ptr(out)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    a.M, a.E, a.k, a.H, a.I = M, E, k, H, I
+    a.dense_min_rows, a.schedule = dense_min_rows, SCHEDULE_AUTO
+    _check(lib.moe_nvfp4_route_decode(ctypes.byref(a), _ptr(logits), _ptr(bias),
+                                      _stream(stream)), "moe_nvfp4_route_decode")
+    return out, ids, w

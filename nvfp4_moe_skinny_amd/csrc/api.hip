@@ -10,6 +10,7 @@
 #include "nvfp4moe.h"
 
 #include "fp8.hpp"
+#include "fused.hpp"
 #include "gemm.hpp"
 #include "moe.hpp"
 #include "staged.hpp"
@@ -218,6 +219,95 @@ int32_t launch_route(const float* logits, const float* bias, int64_t M, int64_t 
 
 }  // namespace
 
+namespace {
+
+// Validates the arguments and fills p. routed: the routing arrays come from
+// moe_route_topk (moe_nvfp4_decode); otherwise only ids and w, which the call
+// writes (moe_nvfp4_route_decode).
+int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p) {
+  if (!a) return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_decode: args is null");
+  if (!a->x || !a->ids || !a->w || !a->w_gate_up || !a->w_down || !a->out || !a->workspace ||
+      (routed && (!a->offsets || !a->pairs || !a->active || !a->active_offsets || !a->n_active)))
+    return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_decode: a required pointer is null");
+  if ((a->shared_gate_up == nullptr) != (a->shared_down == nullptr))
+    return fail(NVFP4MOE_ERR_NULL_ARG, "shared_gate_up and shared_down go together");
+  const int64_t M = a->M, E = a->E, k = a->k, H = a->H, I = a->I;
+  if (M < 1 || E < 1 || k < 1 || H < 1 || I < 1)
+    return fail(NVFP4MOE_ERR_BAD_SHAPE, "M, E, k, H, I must be >= 1");
+  if (E > kRouteMaxE || k > kRouteMaxK || k > E)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "need E <= 256 and k <= min(8, E)");
+  if (!valid_moe_dim(H) || !valid_moe_dim(I))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be 32 * 2^j in [256, 2048]");
+  if (I % rows_per_tile(H) != 0)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "I = %lld must be a multiple of 16384 / H = %lld",
+                (long long)I, (long long)rows_per_tile(H));
+  if (M * k + M > (int64_t)1 << 24) return fail(NVFP4MOE_ERR_UNSUPPORTED, "M too large");
+  if (a->schedule < 0 || a->schedule > 3)
+    return fail(NVFP4MOE_ERR_BAD_SHAPE, "schedule must be 0, 1, 2 or 3 (got %d)",
+                (int)a->schedule);
+  const bool shared = a->shared_gate_up != nullptr;
+  const WsLayout ws = ws_layout(M, E, k, H, I, shared);
+  if (a->workspace_bytes < ws.total)
+    return fail(NVFP4MOE_ERR_WORKSPACE, "workspace %lld < %lld bytes",
+                (long long)a->workspace_bytes, (long long)ws.total);
+  if (!aligned(a->x, 16) || !aligned(a->w_gate_up, 16) || !aligned(a->w_down, 16) ||
+      !aligned(a->workspace, 256) || (shared && (!aligned(a->shared_gate_up, 16) ||
+                                                 !aligned(a->shared_down, 16))))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED,
+                "x and weights need 16-byte, workspace 256-byte alignment");
+
+  std::memset(&p, 0, sizeof(p));
+  p.x = a->x;
+  p.ids = a->ids;
+  p.w = a->w;
+  p.offsets = a->offsets;
+  p.pairs = a->pairs;
+  p.active = a->active;
+  p.active_offsets = a->active_offsets;
+  p.n_active = a->n_active;
+  p.gu = (const uint8_t*)a->w_gate_up;
+  p.dn = (const uint8_t*)a->w_down;
+  p.sgu = (const uint8_t*)a->shared_gate_up;
+  p.sdn = (const uint8_t*)a->shared_down;
+  p.residual = a->residual;
+  p.out = a->out;
+  uint8_t* wsb = (uint8_t*)a->workspace;
+  p.ctl = (uint32_t*)(wsb + ws.ctl_off);
+  p.cnt_ds = (uint32_t*)(wsb + ws.cnt_ds_off);
+  p.cnt_dn = (uint32_t*)(wsb + ws.cnt_dn_off);
+  p.h = (uint64_t*)(wsb + ws.h_off);
+  p.y = (uint64_t*)(wsb + ws.y_off);
+  p.M = (int)M;
+  p.E = (int)E;
+  p.k = (int)k;
+  p.H = (int)H;
+  p.I = (int)I;
+  p.LH = (int)(H / 32);
+  p.LI = (int)(I / 32);
+  p.routed_slots = (int)(E < M * k ? E : M * k);
+  p.has_shared = shared ? 1 : 0;
+  p.slots = p.routed_slots + p.has_shared;
+  p.gu_mat_bytes = matrix_bytes(2 * I, H);
+  p.dn_mat_bytes = matrix_bytes(H, I);
+  p.gu_g = (const float*)(p.gu + gscale_offset(E, 2 * I, H));
+  p.dn_g = (const float*)(p.dn + gscale_offset(E, H, I));
+  if (shared) {
+    p.sgu_g = (const float*)(p.sgu + gscale_offset(1, 2 * I, H));
+    p.sdn_g = (const float*)(p.sdn + gscale_offset(1, H, I));
+  }
+  p.P = (int)(I / rows_per_tile(H));  // == tiles_per_matrix(H, I) == H * I / 16384
+  p.total_blocks = (p.slots + 1) * p.P;
+  p.pair_regs = M * k <= 128 ? (int)((M * k + 63) / 64) : 0;
+  p.hp = (float*)(wsb + ws.hp_off);
+  p.yp = (float*)(wsb + ws.yp_off);
+  p.dense_min_rows = a->dense_min_rows > 0
+                         ? (int)(a->dense_min_rows < (int64_t)1 << 30 ? a->dense_min_rows : 1 << 30)
+                         : kDenseRowsDefault;
+  return ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* nvfp4moe_strerror(int32_t status) {
@@ -398,86 +488,10 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
 }
 
 int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
-  if (!a) return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_decode: args is null");
-  if (!a->x || !a->ids || !a->w || !a->offsets || !a->pairs || !a->active || !a->active_offsets ||
-      !a->n_active ||
-      !a->w_gate_up || !a->w_down || !a->out || !a->workspace)
-    return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_decode: a required pointer is null");
-  if ((a->shared_gate_up == nullptr) != (a->shared_down == nullptr))
-    return fail(NVFP4MOE_ERR_NULL_ARG, "shared_gate_up and shared_down go together");
-  const int64_t M = a->M, E = a->E, k = a->k, H = a->H, I = a->I;
-  if (M < 1 || E < 1 || k < 1 || H < 1 || I < 1)
-    return fail(NVFP4MOE_ERR_BAD_SHAPE, "M, E, k, H, I must be >= 1");
-  if (E > kRouteMaxE || k > kRouteMaxK || k > E)
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "need E <= 256 and k <= min(8, E)");
-  if (!valid_moe_dim(H) || !valid_moe_dim(I))
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be 32 * 2^j in [256, 2048]");
-  if (I % rows_per_tile(H) != 0)
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "I = %lld must be a multiple of 16384 / H = %lld",
-                (long long)I, (long long)rows_per_tile(H));
-  if (M * k + M > (int64_t)1 << 24) return fail(NVFP4MOE_ERR_UNSUPPORTED, "M too large");
-  if (a->schedule < 0 || a->schedule > 3)
-    return fail(NVFP4MOE_ERR_BAD_SHAPE, "schedule must be 0, 1, 2 or 3 (got %d)",
-                (int)a->schedule);
-  const bool shared = a->shared_gate_up != nullptr;
-  const WsLayout ws = ws_layout(M, E, k, H, I, shared);
-  if (a->workspace_bytes < ws.total)
-    return fail(NVFP4MOE_ERR_WORKSPACE, "workspace %lld < %lld bytes",
-                (long long)a->workspace_bytes, (long long)ws.total);
-  if (!aligned(a->x, 16) || !aligned(a->w_gate_up, 16) || !aligned(a->w_down, 16) ||
-      !aligned(a->workspace, 256) || (shared && (!aligned(a->shared_gate_up, 16) ||
-                                                 !aligned(a->shared_down, 16))))
-    return fail(NVFP4MOE_ERR_UNSUPPORTED,
-                "x and weights need 16-byte, workspace 256-byte alignment");
-
   MoeParams p;
-  std::memset(&p, 0, sizeof(p));
-  p.x = a->x;
-  p.ids = a->ids;
-  p.w = a->w;
-  p.offsets = a->offsets;
-  p.pairs = a->pairs;
-  p.active = a->active;
-  p.active_offsets = a->active_offsets;
-  p.n_active = a->n_active;
-  p.gu = (const uint8_t*)a->w_gate_up;
-  p.dn = (const uint8_t*)a->w_down;
-  p.sgu = (const uint8_t*)a->shared_gate_up;
-  p.sdn = (const uint8_t*)a->shared_down;
-  p.residual = a->residual;
-  p.out = a->out;
-  uint8_t* wsb = (uint8_t*)a->workspace;
-  p.ctl = (uint32_t*)(wsb + ws.ctl_off);
-  p.cnt_ds = (uint32_t*)(wsb + ws.cnt_ds_off);
-  p.cnt_dn = (uint32_t*)(wsb + ws.cnt_dn_off);
-  p.h = (uint64_t*)(wsb + ws.h_off);
-  p.y = (uint64_t*)(wsb + ws.y_off);
-  p.M = (int)M;
-  p.E = (int)E;
-  p.k = (int)k;
-  p.H = (int)H;
-  p.I = (int)I;
-  p.LH = (int)(H / 32);
-  p.LI = (int)(I / 32);
-  p.routed_slots = (int)(E < M * k ? E : M * k);
-  p.has_shared = shared ? 1 : 0;
-  p.slots = p.routed_slots + p.has_shared;
-  p.gu_mat_bytes = matrix_bytes(2 * I, H);
-  p.dn_mat_bytes = matrix_bytes(H, I);
-  p.gu_g = (const float*)(p.gu + gscale_offset(E, 2 * I, H));
-  p.dn_g = (const float*)(p.dn + gscale_offset(E, H, I));
-  if (shared) {
-    p.sgu_g = (const float*)(p.sgu + gscale_offset(1, 2 * I, H));
-    p.sdn_g = (const float*)(p.sdn + gscale_offset(1, H, I));
-  }
-  p.P = (int)(I / rows_per_tile(H));  // == tiles_per_matrix(H, I) == H * I / 16384
-  p.total_blocks = (p.slots + 1) * p.P;
-  p.pair_regs = M * k <= 128 ? (int)((M * k + 63) / 64) : 0;
-  p.hp = (float*)(wsb + ws.hp_off);
-  p.yp = (float*)(wsb + ws.yp_off);
-  p.dense_min_rows = a->dense_min_rows > 0
-                         ? (int)(a->dense_min_rows < (int64_t)1 << 30 ? a->dense_min_rows : 1 << 30)
-                         : kDenseRowsDefault;
+  const int32_t st = prepare_decode(a, true, p);
+  if (st != NVFP4MOE_OK) return st;
+  const int64_t M = a->M, H = a->H, I = a->I;
   const bool specialised = H == 2048 && I == 512;
   // three launches unless one is asked for: measured at M = 4, 16 and 256,
   // the staged kernels are at least as fast as the one-launch exchange
@@ -501,6 +515,37 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
   while (rmax > 1 && (int64_t)rmax * I * 4 > 48 * 1024) rmax /= 2;  // LDS for staged h rows
   if (H == 2048 && I == 512) return launch_decode_rows<64, 16>(p, rmax, stream);
   return launch_decode_rows<0, 0>(p, rmax, stream);
+}
+
+int32_t moe_nvfp4_route_decode(const moe_nvfp4_args* a, const float* logits, const float* bias,
+                               hipStream_t stream) {
+  if (!logits) return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_route_decode: logits is null");
+  MoeParams p;
+  const int32_t st = prepare_decode(a, false, p);
+  if (st != NVFP4MOE_OK) return st;
+  const int64_t M = a->M, H = a->H, I = a->I;
+  const bool specialised = H == 2048 && I == 512;
+  if (specialised && M >= p.dense_min_rows)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED,
+                "moe_nvfp4_route_decode needs M < dense_min_rows (FP32 h for every pair)");
+  const int grid = (int)((M * a->k + (p.has_shared ? M : 0)) * p.P);
+  int32_t* ids = const_cast<int32_t*>(a->ids);
+  float* w = const_cast<float*>(a->w);
+  if (specialised)
+    hipLaunchKernelGGL(fused_route_gate_kernel<64>, dim3(grid), dim3(128), 0, stream, p, logits,
+                       bias, ids, w);
+  else
+    hipLaunchKernelGGL(fused_route_gate_kernel<0>, dim3(grid), dim3(128), 0, stream, p, logits,
+                       bias, ids, w);
+  const int32_t st2 = launched("moe_nvfp4_route_decode gate_up");
+  if (st2 != NVFP4MOE_OK) return st2;
+  if (specialised)
+    hipLaunchKernelGGL(token_down_combine_kernel<16>, dim3(p.M * p.P),
+                       dim3((p.k + p.has_shared) * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(token_down_combine_kernel<0>, dim3(p.M * p.P),
+                       dim3((p.k + p.has_shared) * 64), 0, stream, p);
+  return launched("moe_nvfp4_route_decode");
 }
 
 }  // extern "C"

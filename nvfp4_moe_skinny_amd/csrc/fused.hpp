@@ -1,0 +1,60 @@
+// fused.hpp - routing folded into gate_up for few rows (two launches from the
+// logits to the output, with token_down_combine_kernel).
+//
+// One block per (item, gate tile j); items are the pairs m*k + jj (row m, slot
+// jj), then the shared expert's rows. Both waves of a routed item select the
+// top k of row m themselves (the same per-row routine as moe_route_topk, so
+// the same experts and weights bit for bit) while the row of x is already on
+// its way; wave 0 then streams gate tile j of expert ids[m][jj], wave 1 the up
+// tile, as in staged_gate_split_kernel. The items of tile 0 store ids and w
+// for the down launch. With few rows nearly every pair has its own expert, so
+// a tile per pair costs almost no extra bytes, and no grouping is needed.
+#pragma once
+
+#include "route.hpp"
+#include "staged.hpp"
+
+namespace nvfp4moe {
+
+template <int LHC>
+__global__ void __launch_bounds__(128, 4) fused_route_gate_kernel(MoeParams p,
+                                                                  const float* __restrict__ logits,
+                                                                  const float* __restrict__ bias,
+                                                                  int32_t* __restrict__ ids,
+                                                                  float* __restrict__ w) {
+  __shared__ float up_lds[64];
+  __shared__ float lp[2][kRouteMaxE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int item = blockIdx.x / p.P, j = blockIdx.x % p.P;
+  const int npairs = p.M * p.k;
+  const bool sh = item >= npairs;
+  const int m = sh ? item - npairs : item / p.k;
+  const int L = LHC ? LHC : p.LH;
+  uint4 xr[1][4];
+  load_x_bf16(p.x, p.H, m, true, 32 * (lane % L), xr[0]);
+  int e = 0;
+  if (!sh) {
+    int my_id;
+    float my_w;
+    route_row_core(logits, bias, p.E, p.k, m, lane, lp[wave], my_id, my_w);
+    const int jj = item - m * p.k;
+    e = __builtin_amdgcn_readlane(my_id, jj);
+    if (j == 0 && wave == 0 && lane == jj) {
+      ids[item] = my_id;
+      w[item] = my_w;
+    }
+  }
+  const uint8_t* mat = sh ? p.sgu : p.gu + (int64_t)e * p.gu_mat_bytes;
+  const float g = sh ? p.sgu_g[0] : p.gu_g[e];
+  TileRegs T;
+  load_tile(mat + (int64_t)(wave == 0 ? j : j + p.P) * kTileBytes, lane, T);
+  const float v = tile_row_value<LHC>(T, xr, L);
+  if (wave == 1) up_lds[lane] = v;
+  __syncthreads();
+  if (wave == 0 && reduced_writer_rt(lane, L)) {
+    const int i = j * (16384 / p.H) + reduced_row(lane, L);
+    p.hp[(int64_t)item * p.I + i] = silu(v * g) * (up_lds[lane] * g);
+  }
+}
+
+}  // namespace nvfp4moe

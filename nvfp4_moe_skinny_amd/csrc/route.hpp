@@ -39,13 +39,14 @@ __device__ __forceinline__ float row0_sum(float v) {
   return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
 }
 
-// Routes one row with one wave: ids and weights to global memory and to
-// ids_lds (if not null). Each round takes the largest remaining key; among
-// equal keys the ballots pick the lowest expert index (e = lane + 64 s).
-__device__ __forceinline__ void route_row(const float* __restrict__ logits,
-                                          const float* __restrict__ bias, int E, int k, int row,
-                                          int lane, float* lp, int32_t* __restrict__ ids,
-                                          float* __restrict__ w, int32_t* ids_lds) {
+// Routes one row with one wave (the whole wave active): lane j < k returns
+// the j-th selected expert in my_id and its weight in my_w. Each round takes
+// the largest remaining key; among equal keys the ballots pick the lowest
+// expert index (e = lane + 64 s). lp: E floats of LDS owned by the wave.
+__device__ __forceinline__ void route_row_core(const float* __restrict__ logits,
+                                               const float* __restrict__ bias, int E, int k,
+                                               int row, int lane, float* lp, int& my_id_out,
+                                               float& my_w) {
   uint32_t ord[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -79,9 +80,22 @@ __device__ __forceinline__ void route_row(const float* __restrict__ logits,
   const float top = lp[__builtin_amdgcn_readfirstlane(my_id)];
   const float ex = lane < k ? expf(lp[my_id] - top) : 0.0f;
   const float z = row0_sum(ex);
+  my_id_out = my_id;
+  my_w = ex / z;
+}
+
+// Routes one row with one wave: ids and weights to global memory and to
+// ids_lds (if not null).
+__device__ __forceinline__ void route_row(const float* __restrict__ logits,
+                                          const float* __restrict__ bias, int E, int k, int row,
+                                          int lane, float* lp, int32_t* __restrict__ ids,
+                                          float* __restrict__ w, int32_t* ids_lds) {
+  int my_id;
+  float my_w;
+  route_row_core(logits, bias, E, k, row, lane, lp, my_id, my_w);
   if (lane < k) {
     ids[(int64_t)row * k + lane] = my_id;
-    w[(int64_t)row * k + lane] = ex / z;
+    w[(int64_t)row * k + lane] = my_w;
     if (ids_lds) ids_lds[row * k + lane] = my_id;
   }
 }

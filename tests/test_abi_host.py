@@ -132,6 +132,13 @@ def test_decode_validation(m):
     # two launches need FP32 h for every pair: no MFMA slot (M < dense_min_rows)
     assert dec(_args(m, schedule=3, dense_min_rows=4)) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert dec(_args(m, ids=None)) == m.NVFP4MOE_ERR_NULL_ARG
+    # routing folded in: grouping arrays not needed; logits required; M < dense_min_rows
+    rd = lambda a, lg=4096: L.moe_nvfp4_route_decode(ctypes.byref(a), lg, None, None)
+    assert rd(_args(m), lg=None) == m.NVFP4MOE_ERR_NULL_ARG
+    assert rd(_args(m, w=None)) == m.NVFP4MOE_ERR_NULL_ARG
+    assert rd(_args(m, M=16)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert rd(_args(m, M=4, dense_min_rows=3)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert rd(_args(m, workspace_bytes=1)) == m.NVFP4MOE_ERR_WORKSPACE
     assert dec(_args(m, schedule=-1)) == m.NVFP4MOE_ERR_BAD_SHAPE
     # h [M*k][I] + y [M*k][H] as 8-byte (value, flag) words, then as 4-byte words
     assert need >= 4 * 8 * (512 + 2048) * (8 + 4)

@@ -18,7 +18,8 @@ def m(gpu):
 
 
 @pytest.mark.parametrize("M,shared,schedule", [(4, False, 1), (16, True, 1), (16, True, 2),
-                                               (4, False, 2), (4, False, 3), (8, True, 3)])
+                                               (4, False, 2), (4, False, 3), (8, True, 3),
+                                               (4, False, "fused"), (8, True, "fused")])
 def test_graph_replay_matches_eager(m, gpu, M, shared, schedule):
     lays = [moe_layer(seed=s, wl=400, layer=s, M=M, E_=64, H_=2048, I_=512, k=8, bias=shared,
                       shared=shared) for s in range(3)]
@@ -30,6 +31,11 @@ def test_graph_replay_matches_eager(m, gpu, M, shared, schedule):
 
     def step(i):
         d = devs[i]
+        if schedule == "fused":  # routing inside the decode call (ids / w written)
+            m.moe_nvfp4_route_decode(d["x"], d["logits"], 8, d["gu"], d["dn"], d["bias"], d["sgu"],
+                                     d["sdn"], residual=d["x"], workspace=ws, out=outs[i],
+                                     ids=routes[i].ids, w=routes[i].w)
+            return
         r = m.moe_route_topk(d["logits"], 8, d["bias"], out=routes[i])
         m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=d["x"],
                            workspace=ws, out=outs[i], schedule=schedule)

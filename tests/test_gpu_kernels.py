@@ -150,6 +150,37 @@ def test_moe_block_small(m, gpu, M, E, H, I, k, shared, resid, schedule):
     assert tol_ratio(out, ref) <= 1.0
 
 
+@pytest.mark.parametrize("M,E,H,I,k,shared,resid,bias", [
+    (1, 256, 2048, 512, 8, False, False, False), (4, 256, 2048, 512, 8, False, False, True),
+    (8, 256, 2048, 512, 8, True, True, True), (3, 16, 256, 256, 4, True, False, False),
+    (5, 8, 512, 512, 8, True, False, False), (2, 32, 1024, 256, 2, False, True, False),
+    (12, 64, 2048, 512, 8, True, False, True), (6, 4, 2048, 512, 1, True, True, False)])
+def test_moe_route_decode_fused(m, gpu, M, E, H, I, k, shared, resid, bias):
+    """Routing inside the gate_up launch: ids and w bit-identical to the oracle's
+    routing, the output within tolerance of the oracle and bit-identical to
+    moe_route_topk + moe_nvfp4_decode with the two-launch schedule."""
+    lay = moe_layer(seed=M + 3 * E, wl=205, M=M, E_=E, H_=H, I_=I, k=k, bias=bias, shared=shared)
+    residual = synth.normal_bf16(synth.key(5, 206, M), (M, H)) if resid else None
+    d = upload_layer(lay, gpu, m)
+    res = None if residual is None else to_dev_bf16(residual, gpu)
+    dmr = 13 if M == 12 else 0
+    out, ids_d, w_d = m.moe_nvfp4_route_decode(d["x"], d["logits"], k, d["gu"], d["dn"], d["bias"],
+                                               d["sgu"], d["sdn"], residual=res,
+                                               dense_min_rows=dmr)
+    r = m.moe_route_topk(d["logits"], k, d["bias"])
+    out2 = m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=res,
+                              schedule=3, dense_min_rows=dmr)
+    torch.cuda.synchronize()
+    ids, w = oracle.route_topk(lay.logits, k, lay.bias)
+    assert (ids_d.cpu().numpy() == ids).all()
+    assert np.max(np.abs(w_d.cpu().numpy().astype(np.float64) - w)) <= 1e-6
+    assert torch.equal(w_d.view(torch.int32), r.w.view(torch.int32))
+    ref = oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down, lay.shared_gate_up,
+                           lay.shared_down, residual)
+    assert tol_ratio(dev_bf16_to_f64(out), ref) <= 1.0
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
 @pytest.mark.parametrize("M,E,k,shared,resid,dense_min_rows", [
     (6, 4, 1, True, True, 1),      # every slot on MFMA, most blocks with one row
     (17, 8, 8, True, False, 16),   # each expert holds all 17 rows: a 1-row second block
