@@ -125,6 +125,20 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(a, b), max(c, d));
 }
 
+// Maximum over the wave in every lane, VALU only: DPP within 16-lane rows,
+// then v_permlane16_swap / v_permlane32_swap of v with itself, whose two
+// results hold the partner rows' values (their maximum is the pair's).
+__device__ __forceinline__ uint32_t wave_max_u32_all(uint32_t v) {
+  v = max(v, dpp_u32(v, kDppQuadXor1));
+  v = max(v, dpp_u32(v, kDppQuadXor2));
+  v = max(v, dpp_u32(v, kDppRowRor4));
+  v = max(v, dpp_u32(v, kDppRowRor8));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((uint32_t)a[0], (uint32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)b[0], (uint32_t)b[1]);
+}
+
 // The value of lane l ^ 32 (every lane of the wave active). v_permlane32_swap
 // exchanges the upper half of its first operand with the lower half of its
 // second; with both operands v, result 1 holds the upper half's values in the

@@ -36,8 +36,11 @@ __global__ void __launch_bounds__(128, 4) fused_route_gate_kernel(MoeParams p,
   if (!sh) {
     int my_id;
     float my_w;
-    route_row_core(logits, bias, p.E, p.k, m, lane, lp[wave], my_id, my_w);
     const int jj = item - m * p.k;
+    // the items of tile 0 store ids and w (all k rounds, softmax); the others
+    // need only the first jj + 1 experts
+    route_row_core(logits, bias, p.E, p.k, m, lane, lp[wave], my_id, my_w,
+                   j == 0 ? kRouteMaxK : jj + 1, j == 0);
     e = __builtin_amdgcn_readlane(my_id, jj);
     if (j == 0 && wave == 0 && lane == jj) {
       ids[item] = my_id;

@@ -46,41 +46,47 @@ __device__ __forceinline__ float row0_sum(float v) {
 __device__ __forceinline__ void route_row_core(const float* __restrict__ logits,
                                                const float* __restrict__ bias, int E, int k,
                                                int row, int lane, float* lp, int& my_id_out,
-                                               float& my_w) {
+                                               float& my_w, int rounds = kRouteMaxK,
+                                               bool weights = true) {
+  // every load first (one round trip), then the keys
+  float lv[4], bv[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int e = lane + 64 * s;
+    const int ec = e < E ? e : E - 1;  // in bounds; masked below
+    lv[s] = logits[(int64_t)row * E + ec];
+    bv[s] = bias ? bias[ec] : 0.0f;
+  }
   uint32_t ord[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int e = lane + 64 * s;
-    if (e < E) {
-      float l = logits[(int64_t)row * E + e];
-      if (bias) l = l + bias[e];
-      lp[e] = l;
-      ord[s] = route_ord(l);
-    } else {
-      ord[s] = 0u;
-    }
+    const float l = bias ? lv[s] + bv[s] : lv[s];
+    if (e < E) lp[e] = l;
+    ord[s] = e < E ? route_ord(l) : 0u;
   }
   int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    const uint32_t best = wave_max_u32(max(max(ord[0], ord[1]), max(ord[2], ord[3])));
-    int e = 0;
+  const int nr = rounds < k ? rounds : k;  // the first nr experts only (weights need all k)
+  for (int j = 0; j < nr; ++j) {
+    const uint32_t best = wave_max_u32_all(max(max(ord[0], ord[1]), max(ord[2], ord[3])));
+    const uint64_t b0 = __ballot(ord[0] == best), b1 = __ballot(ord[1] == best);
+    const uint64_t b2 = __ballot(ord[2] == best), b3 = __ballot(ord[3] == best);
+    const int e = b0 ? (int)__builtin_ctzll(b0)
+                     : b1 ? 64 + (int)__builtin_ctzll(b1)
+                          : b2 ? 128 + (int)__builtin_ctzll(b2) : 192 + (int)__builtin_ctzll(b3);
+    const bool mine = lane == (e & 63);
+    const int se = e >> 6;
 #pragma unroll
-    for (int s = 3; s >= 0; --s) {
-      const uint64_t b = __ballot(ord[s] == best);
-      if (b) e = 64 * s + (int)__builtin_ctzll(b);
-    }
-    if (lane == (e & 63)) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (s == (e >> 6)) ord[s] = 0u;
-    }
-    if (lane == j) my_id = e;
+    for (int s = 0; s < 4; ++s) ord[s] = (mine && se == s) ? 0u : ord[s];
+    my_id = lane == j ? e : my_id;
   }
+  my_id_out = my_id;
+  my_w = 0.0f;
+  if (!weights) return;
   __builtin_amdgcn_wave_barrier();
   const float top = lp[__builtin_amdgcn_readfirstlane(my_id)];
   const float ex = lane < k ? expf(lp[my_id] - top) : 0.0f;
   const float z = row0_sum(ex);
-  my_id_out = my_id;
   my_w = ex / z;
 }
 
