@@ -98,9 +98,9 @@ int32_t nvfp4_dequant_f32(const void* packed, int64_t G, int64_t N, int64_t K, i
  * BF16 matrices x [G][N][K] (raw bits) -> canonical NVFP4: codes [G][N][K/2]
  * (element 2b in the low nibble of byte b), E4M3 scales [G][N][K/16], FP32
  * tensor scales g [G]; nvfp4_pack then gives the library layout. The pages
- * name only the tool that quantized a BF16 head ([Elsa] "Files", the lm_head
- * quantization script), not its recipe; this is the plain amax recipe, every
- * division and product in FP32:
+ * name only the tool that quantized a BF16 head (the Qwen3.8-27B NVFP4 lm_head
+ * recipe page, "Files": its lm_head quantization script), not its recipe;
+ * this is the plain amax recipe, every division and product in FP32:
  *   g[i] = amax_i / 2688 (6 * 448), or 1 when matrix i is all zeros;
  *   scale of a 16-block = E4M3 nearest to amax_b / (6 g), ties to the even
  *     code, saturating at 448;
@@ -129,7 +129,7 @@ int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w
  * bytes (used as stored: no packing step), one FP32 scale for the whole
  * tensor (a device pointer, so that the call can be graph-captured), FP32
  * accumulation. The attention projections of the pages' model are of this
- * kind ([Elsa] "An FP8 fast path": a small-batch FP8 GEMM with one scale per
+ * kind (Elsa page, "An FP8 fast path": a small-batch FP8 GEMM with one scale per
  * tensor). x [M][K] and y [M][N] are raw BF16 bits; M >= 1 (taken in batches
  * of 4 rows over the same weight registers), N >= 1, K in {1024, 2048, 4096}
  * (else NVFP4MOE_ERR_UNSUPPORTED); x and W 16-byte aligned.
@@ -163,7 +163,7 @@ int32_t moe_route_topk(const float* logits, const float* bias, int64_t M, int64_
  * w_router[e][h] with FP32 accumulation and FP32 result, written to the
  * caller's logits buffer [M][E] (an output: it is also what the selection
  * reads), then exactly moe_route_topk(logits, bias, ...). The pages' model is
- * a routed mixture of experts ([Elsa] "The card and the model"); its router
+ * a routed mixture of experts (Elsa page, "The card and the model"); its router
  * is neither an NVFP4 expert nor an FP8 projection, so w_router is BF16 [E][H]
  * (raw bits) and x is BF16 [M][H]. H in {512, 1024, 2048, 4096} (else
  * NVFP4MOE_ERR_UNSUPPORTED); x and w_router 16-byte aligned; the limits on M,

@@ -1,9 +1,9 @@
 // quant.hpp - BF16 matrices -> canonical NVFP4 (E2M1 codes, one E4M3 scale per
 // 16 elements along K, one FP32 scale per matrix) on the device.
 //
-// The pages name only the tool that quantized a BF16 head to NVFP4 (the Elsa
-// page's "Files" list); the recipe here is the plain amax one, with every
-// division and product in FP32:
+// The pages name only the tool that quantized a BF16 head to NVFP4 (the
+// "Files" list of the Qwen3.8-27B NVFP4 lm_head recipe page); the recipe
+// here is the plain amax one, with every division and product in FP32:
 //   g   = amax / 2688 over the matrix (6 * 448: the largest E2M1 magnitude
 //         times the largest E4M3 value), 1 if amax = 0;
 //   s_b = E4M3 round-to-nearest-even of amax_b / (6 g), saturating at 448;

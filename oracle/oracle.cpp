@@ -137,7 +137,8 @@ void oracle_router_logits(const uint16_t* x, int64_t M, int64_t H, const uint16_
 
 /* ---- quantization: BF16 -> canonical NVFP4 ----------------------------------------
  * The pages say only that a BF16 head was turned into NVFP4 with NVIDIA's
- * model optimizer (Elsa page, "Files": the lm_head quantization script) and
+ * model optimizer (the Qwen3.8-27B NVFP4 lm_head recipe page, "Files": its
+ * lm_head quantization script) and
  * give no recipe. The reading used here is the plain amax one, every division
  * and product in FP32 (the precision the GPU kernel decides in):
  *   g   = fl32(amax / 2688) over the whole matrix (2688 = 6 * 448: the largest

@@ -16,7 +16,8 @@
  *     and with FP8 E4M3 weights under one scale per tensor ("An FP8 fast
  *     path" on the same page);
  *   - quantization of BF16 matrices to NVFP4 (amax recipe: the pages name
- *     only the tool that did it, in the "Files" list of the Elsa page);
+ *     only the tool that did it, in the "Files" list of the Qwen3.8-27B NVFP4
+ *     lm_head recipe page);
  *   - the router projection (logits = x W_r^T, BF16 weights) in front of
  *     top-k routing ("The card and the model": a mixture-of-experts model);
  *   - top-k routing, grouping of (row, slot) pairs by expert, the expert
