@@ -164,9 +164,12 @@ def test_moe_route_decode_fused(m, gpu, M, E, H, I, k, shared, resid, bias):
     d = upload_layer(lay, gpu, m)
     res = None if residual is None else to_dev_bf16(residual, gpu)
     dmr = 13 if M == 12 else 0
-    out, ids_d, w_d = m.moe_nvfp4_route_decode(d["x"], d["logits"], k, d["gu"], d["dn"], d["bias"],
-                                               d["sgu"], d["sdn"], residual=res,
-                                               dense_min_rows=dmr)
+    ws = m.moe_workspace(M, E, k, H, I, shared, gpu)
+    call = lambda: m.moe_nvfp4_route_decode(d["x"], d["logits"], k, d["gu"], d["dn"], d["bias"],
+                                            d["sgu"], d["sdn"], residual=res, workspace=ws,
+                                            dense_min_rows=dmr)
+    out, ids_d, w_d = call()
+    again, _, _ = call()  # the same workspace again
     r = m.moe_route_topk(d["logits"], k, d["bias"])
     out2 = m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=res,
                               schedule=3, dense_min_rows=dmr)
@@ -179,6 +182,8 @@ def test_moe_route_decode_fused(m, gpu, M, E, H, I, k, shared, resid, bias):
                            lay.shared_down, residual)
     assert tol_ratio(dev_bf16_to_f64(out), ref) <= 1.0
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(again.view(torch.int16), out2.view(torch.int16))
+    assert m.workspace_error_flag(ws) == 0
 
 
 @pytest.mark.parametrize("M,E,k,shared,resid,dense_min_rows", [
