@@ -112,7 +112,7 @@ def parse():
     p.add_argument("--copies", type=int, default=0, help="weight sets cycled (0: >= 1 GB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--eager-calls", type=int, default=400)
+    p.add_argument("--eager-calls", type=int, default=400, help=">= 2")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="only run a plain device copy of this many MB (counter calibration)")
     return p.parse_args()
@@ -282,8 +282,9 @@ def main():
             b += M * k * 8 + (E + 1 + E + 1) * 4 + M * k * 4
         decode_bytes.append(b)
     torch.cuda.synchronize()
-    dec_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])[20:]
-    dec_bytes = float(np.mean(decode_bytes[20:]))
+    skip = min(20, args.eager_calls // 2)  # warm calls only
+    dec_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])[skip:]
+    dec_bytes = float(np.mean(decode_bytes[skip:]))
     dec_avg_ms = float(dec_ms.mean())
     eager_call_us = dec_avg_ms * 1e3
     if fused:

@@ -253,7 +253,13 @@ __global__ void __launch_bounds__(1024) route_rows_kernel(const float* __restric
   if (row < M) route_row(logits, bias, E, k, row, lane, lp[wave], ids, w, nullptr);
 }
 
-// Larger M, second launch: group all pairs in one block (P <= kGroupMaxPairs).
+// Larger M, second launch: group all pairs in one block (P <= kGroupMaxPairs)
+// with all 16 waves: the same stable counting sort, with the pairs cut into
+// 16 consecutive chunks. Each wave counts its chunk per expert; a thread per
+// expert turns the 16 counts into the chunks' starting places within the
+// expert's run (a prefix over the waves, so earlier chunks come first); wave 0
+// scans the totals into offsets and slots; then every wave places its chunk,
+// batch by batch, as the one-wave sort does.
 constexpr int kGroupMaxPairs = 8192;
 __global__ void __launch_bounds__(1024) group_kernel(const int32_t* __restrict__ ids, int M, int E,
                                                      int k, int32_t* __restrict__ counts,
@@ -263,14 +269,90 @@ __global__ void __launch_bounds__(1024) group_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ active_offsets,
                                                      int32_t* __restrict__ n_active) {
   __shared__ int32_t ids_lds[kGroupMaxPairs];
-  __shared__ int counts_lds[kRouteMaxE];
-  __shared__ int offs_lds[kRouteMaxE];
+  __shared__ int wcnt[kRouteWaves][kRouteMaxE];  // counts, then run positions, per wave
+  __shared__ int total[kRouteMaxE];
+  __shared__ int start[kRouteMaxE];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int P = M * k;
+  const int chunk = ((P + kRouteWaves - 1) / kRouteWaves + 63) / 64 * 64;
+  const int p_begin = wave * chunk;
+  const int p_end = p_begin + chunk < P ? p_begin + chunk : P;
   for (int p = threadIdx.x; p < P; p += blockDim.x) ids_lds[p] = ids[p];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wcnt[wave][4 * lane + j] = 0;
   __syncthreads();
-  if (threadIdx.x < 64)
-    group_pairs_wave(ids_lds, P, E, threadIdx.x, counts_lds, offs_lds, counts, offsets, pairs,
-                     active, active_offsets, n_active);
+  // counts of this wave's chunk
+  for (int p0 = p_begin; p0 < p_end; p0 += 64) {
+    const bool valid = p0 + lane < p_end;
+    const int e = valid ? ids_lds[p0 + lane] : 0;
+    const uint64_t same = match_id(e, valid);
+    if (valid && (same & lanes_below(lane)) == 0) wcnt[wave][e] += __popcll(same);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // per expert: chunk places relative to the expert's run start, and the total
+  if (threadIdx.x < kRouteMaxE) {
+    const int e = threadIdx.x;
+    int run = 0;
+    for (int w2 = 0; w2 < kRouteWaves; ++w2) {
+      const int c = wcnt[w2][e];
+      wcnt[w2][e] = run;
+      run += c;
+    }
+    total[e] = run;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int c[4], f[4], cex[4], fex[4], ctot, ftot;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = total[4 * lane + j];
+      f[j] = c[j] > 0 ? 1 : 0;
+    }
+    wave_scan256(c, lane, cex, ctot);
+    wave_scan256(f, lane, fex, ftot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * lane + j;
+      start[e] = cex[j];
+      if (e < E) {
+        counts[e] = c[j];
+        offsets[e] = cex[j];
+        if (f[j]) {  // active slots [0, ftot)
+          active[fex[j]] = e;
+          active_offsets[fex[j]] = cex[j];
+        }
+        if (e >= ftot) {  // unused slots [ftot, E)
+          active[e] = -1;
+          active_offsets[e] = ctot;
+        }
+      }
+    }
+    if (lane == 0) {
+      offsets[E] = ctot;
+      active_offsets[E] = ctot;
+      *n_active = ftot;
+    }
+  }
+  __syncthreads();
+  // places of this wave's chunk
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wcnt[wave][4 * lane + j] += start[4 * lane + j];
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+  for (int p0 = p_begin; p0 < p_end; p0 += 64) {
+    const bool valid = p0 + lane < p_end;
+    const int e = valid ? ids_lds[p0 + lane] : 0;
+    const uint64_t same = match_id(e, valid);
+    if (valid) {
+      const uint64_t below = same & lanes_below(lane);
+      pairs[wcnt[wave][e] + __popcll(below)] = p0 + lane;
+      if (below == 0) wcnt[wave][e] += __popcll(same);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+  }
 }
 
 }  // namespace nvfp4moe
