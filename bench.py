@@ -519,7 +519,7 @@ def bench_head(args):
 
     dev = torch.device("cuda:0")
     N = 32768 if args.workload == "head32k" else 248000
-    M = 6
+    M = args.rows or 6
     w_bytes = N * 2048 // 2 + N * 2048 // 16 + 4
     copies = args.copies or int(np.ceil(1e9 / w_bytes)) + 1
     ws, xs = [], []

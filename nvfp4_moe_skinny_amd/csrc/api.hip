@@ -394,6 +394,18 @@ int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w
                                (long long)K);
   if (!aligned(x, 16) || !aligned(w_packed, 16))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "x and w_packed must be 16-byte aligned");
+#ifndef NVFP4MOE_GEMM_DENSE_OFF
+  if (K == 2048 && M >= kGemmDenseMinRows) {
+    const int64_t blocks16 = (tiles_per_matrix(N, K) + 1) / 2;  // 16-row blocks of W
+    const int64_t want = (blocks16 + kGemmDenseWaves - 1) / kGemmDenseWaves;
+    const int64_t grid = want < kGemmDenseMaxBlocks ? want : kGemmDenseMaxBlocks;
+    const size_t lds = (size_t)(M < 16 ? M : 16) * kGemmXStride;
+    hipLaunchKernelGGL(skinny_gemm_dense_kernel, dim3((unsigned)grid),
+                       dim3(64 * kGemmDenseWaves), lds, stream, x, M, (const uint8_t*)w_packed, N,
+                       y);
+    return launched("nvfp4_skinny_gemm");
+  }
+#endif
   return dispatch_l<GemmLaunch>(K / 32, x, M, (const uint8_t*)w_packed, N, y, stream);
 }
 

@@ -4,7 +4,7 @@
 // in batches of up to 8.
 #pragma once
 
-#include "tile.hpp"
+#include "dense.hpp"
 
 namespace nvfp4moe {
 
@@ -57,6 +57,94 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const uint16_t* __rest
       gemm_rows<L, 2>(T, x, K, m0, rows, col0, lane, tile, N, g, y);
     else
       gemm_rows<L, 1>(T, x, K, m0, rows, col0, lane, tile, N, g, y);
+  }
+}
+
+
+// ---- MFMA variant for K = 2048 -----------------------------------------------------------
+//
+// Four waves per block, each taking 16 rows of W at a time (packed tiles 2b
+// and 2b + 1, 8 rows each) in a grid-stride loop; the rows of x, 16 at a time,
+// are the MFMA's columns. The weights are decoded exactly to BF16 (dense.hpp)
+// once per 16 rows of x, about 2 VALU instructions per weight, where the VALU
+// product spends 0.5 + 0.5 M. The 16 rows of x are staged once per block in
+// LDS (16-byte piece p of row r stored at piece p ^ (r % 16), so the 16 rows'
+// same piece fall in 16 different bank groups): every wave reads its B
+// operands there instead of from L2, which at M = 6 would move more bytes
+// than W itself.
+// Lane l holds W row l % 16 (chunk 4q + l / 16) and x row l % 16; D row
+// 4 (l / 16) + r is W row 16 b + 4 (l / 16) + r.
+constexpr int kGemmDenseMinRows = 4;
+constexpr int kGemmXStride = 4096;  // bytes per staged row of x
+constexpr int kGemmDenseWaves = 4;
+constexpr int64_t kGemmDenseMaxBlocks = 1024;  // grid-stride beyond
+
+// The chunks of 16-row block blk of W in MFMA order (zeros past the last tile
+// or block).
+__device__ __forceinline__ void load_gemm_block(const uint8_t* __restrict__ w, int64_t ntiles,
+                                                int64_t blk, int m, int grp, DenseRows<16>& d) {
+  const int64_t t = 2 * blk + (m >> 3);  // this lane's tile
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    if (t < ntiles) {
+      load_dense_chunk(w + t * kTileBytes, 64, m & 7, 4 * q + grp, d.c[q], d.s[q]);
+    } else {
+      d.c[q] = make_uint4(0, 0, 0, 0);
+      d.s[q] = 0u;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(64 * kGemmDenseWaves) skinny_gemm_dense_kernel(
+    const uint16_t* __restrict__ x, int64_t M, const uint8_t* __restrict__ w, int64_t N,
+    uint16_t* __restrict__ y) {
+  constexpr int64_t K = 2048;
+  extern __shared__ __align__(16) uint8_t xs[];  // [rows][256 pieces of 16 bytes]
+  const int lane = threadIdx.x & 63, m = lane & 15, grp = lane >> 4;
+  const int wave = threadIdx.x >> 6;
+  const int64_t ntiles = tiles_per_matrix(N, K);
+  const int64_t nblk = (ntiles + 1) / 2;  // 16-row blocks of W
+  const float g = reinterpret_cast<const float*>(w + gscale_offset(1, N, K))[0];
+#pragma unroll 1
+  for (int64_t c0 = 0; c0 < M; c0 += 16) {
+    const int rows = (M - c0) < 16 ? (int)(M - c0) : 16;
+    __syncthreads();  // the previous rows' reads are done
+    for (int i = threadIdx.x; i < rows * 256; i += 64 * kGemmDenseWaves) {
+      const int r = i >> 8, c = i & 255;  // 256 pieces of 16 bytes per row
+      *reinterpret_cast<uint4*>(xs + r * kGemmXStride + 16 * (c ^ (r & 15))) =
+          reinterpret_cast<const uint4*>(x + (c0 + r) * K)[c];
+    }
+    __syncthreads();
+    const bool valid = m < rows;
+    const uint8_t* xrow = xs + m * kGemmXStride;
+#pragma unroll 1
+    for (int64_t blk = (int64_t)blockIdx.x * kGemmDenseWaves + wave; blk < nblk;
+         blk += (int64_t)gridDim.x * kGemmDenseWaves) {
+      DenseRows<16> d;
+      load_gemm_block(w, ntiles, blk, m, grp, d);
+      f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        bf16x8 a[4];
+        dense_a<16>(d, q, a);
+        uint4 xv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          xv[e] = valid ? *reinterpret_cast<const uint4*>(
+                              xrow + 16 * ((4 * (4 * q + grp) + e) ^ m))
+                        : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mfma_bf16(a[e], as_bf16x8(xv[e]), acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (valid) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t n = 16 * blk + 4 * grp + r;
+          if (n < N) y[(c0 + m) * N + n] = f32_to_bf16_rne(acc[r] * g);
+        }
+      }
+    }
   }
 }
 
