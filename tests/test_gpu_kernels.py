@@ -64,7 +64,12 @@ def test_dequant_random_tensor(m, gpu):
                                      (8, 2048, 64, 2.0 ** -9),  # per-layer 2048 -> 64
                                      (3, 2048, 37, 0.37), (19, 512, 100, 1.0),
                                      (5, 256, 64, 2.0 ** -4), (2, 32, 700, 1.0),
-                                     (16, 1024, 48, 0.5), (4, 64, 5, 1.0)])
+                                     (16, 1024, 48, 0.5), (4, 64, 5, 1.0),
+                                     # MFMA path (K = 2048, M >= 4): odd tile counts,
+                                     # ragged N, one and several 16-row passes over x
+                                     (4, 2048, 8, 2.0 ** -9), (5, 2048, 24, 1.0),
+                                     (16, 2048, 100, 0.37), (17, 2048, 40, 1.0),
+                                     (33, 2048, 17, 2.0 ** -9), (6, 2048, 4104, 1.0)])
 def test_skinny_gemm(m, gpu, M, K, N, g):
     x, w = dense_skinny(seed=0, M=M, K=K, N=N, g=g)
     pw = pack(w, gpu, m)
