@@ -87,7 +87,10 @@ __device__ __forceinline__ void staged_gate_rows(const MoeParams& p, const SlotI
 
 // MFMA (H = 2048: a gate tile and an up tile hold 8 rows each, together one
 // 16-row block): h packed as hi / lo BF16 for the dense down product.
-template <int NCB>
+// AHEAD: chunk columns of x requested ahead of the one being multiplied (a
+// ring of AHEAD + 1 columns in registers; 0 in the 128-register two-wave
+// kernel, where the ring costs more than it hides).
+template <int NCB, int AHEAD>
 __device__ __forceinline__ void staged_gate_dense(const MoeParams& p, const SlotInfo& s,
                                                   const uint8_t* tg, const uint8_t* tu, int j,
                                                   float g) {
@@ -113,18 +116,44 @@ __device__ __forceinline__ void staged_gate_dense(const MoeParams& p, const Slot
     f32x4 acc[NCB];
 #pragma unroll
     for (int b = 0; b < NCB; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (AHEAD == 0) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      bf16x8 a[4];
-      dense_a<16>(d, q, a);
+      for (int q = 0; q < 16; ++q) {
+        bf16x8 a[4];
+        dense_a<16>(d, q, a);
 #pragma unroll
-      for (int b = 0; b < NCB; ++b) {
-        uint4 xv[4];
-        load_x_bf16(p.x, p.H, xrow[b], pr[b] >= 0, 32 * (4 * q + grp), xv);
+        for (int b = 0; b < NCB; ++b) {
+          uint4 xv[4];
+          load_x_bf16(p.x, p.H, xrow[b], pr[b] >= 0, 32 * (4 * q + grp), xv);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[b] = mfma_bf16(a[e], as_bf16x8(xv[e]), acc[b]);
+          for (int e = 0; e < 4; ++e) acc[b] = mfma_bf16(a[e], as_bf16x8(xv[e]), acc[b]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one chunk column's loads in flight at a time
       }
-      __builtin_amdgcn_sched_barrier(0);  // one chunk column's loads in flight at a time
+    } else {
+      uint4 xb[AHEAD + 1][NCB][4];
+#pragma unroll
+      for (int q = 0; q < AHEAD; ++q)
+#pragma unroll
+        for (int b = 0; b < NCB; ++b)
+          load_x_bf16(p.x, p.H, xrow[b], pr[b] >= 0, 32 * (4 * q + grp), xb[q][b]);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (q + AHEAD < 16) {
+#pragma unroll
+          for (int b = 0; b < NCB; ++b)
+            load_x_bf16(p.x, p.H, xrow[b], pr[b] >= 0, 32 * (4 * (q + AHEAD) + grp),
+                        xb[(q + AHEAD) % (AHEAD + 1)][b]);
+        }
+        bf16x8 a[4];
+        dense_a<16>(d, q, a);
+#pragma unroll
+        for (int b = 0; b < NCB; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[b] = mfma_bf16(a[e], as_bf16x8(xb[q % (AHEAD + 1)][b][e]), acc[b]);
+        __builtin_amdgcn_sched_barrier(0);  // AHEAD + 1 columns' loads in flight at most
+      }
     }
     // D row 4 grp + r: gate rows 0-7 in lanes 0-31, the matching up rows in lanes 32-63
 #pragma unroll
@@ -156,7 +185,7 @@ __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_gate_kernel(MoeP
   const uint8_t* tu = mat + (int64_t)(j + p.P) * kTileBytes;
   if constexpr (DENSE) {
     if (s.rows >= p.dense_min_rows) {
-      staged_gate_dense<2>(p, s, tg, tu, j, g);
+      staged_gate_dense<2, 1>(p, s, tg, tu, j, g);
       return;
     }
   }
@@ -216,7 +245,7 @@ __global__ void __launch_bounds__(128, 4) staged_gate_split_kernel(MoeParams p) 
   const uint8_t* tu = mat + (int64_t)(j + p.P) * kTileBytes;
   if constexpr (DENSE) {
     if (s.rows >= p.dense_min_rows) {
-      if (wave == 0) staged_gate_dense<2>(p, s, tg, tu, j, g);
+      if (wave == 0) staged_gate_dense<2, 0>(p, s, tg, tu, j, g);
       return;
     }
   }
