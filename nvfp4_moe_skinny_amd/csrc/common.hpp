@@ -92,6 +92,19 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Workgroups are handed to the eight XCDs (each with its own L2) in turn:
+// workgroup b runs on XCD b % 8. For a grid whose size is a multiple of 8 this
+// gives XCD x the consecutive logical blocks [x G / 8, (x + 1) G / 8), so the
+// work items that read neighbouring bytes share an L2. Other grids keep b.
+// Used where the items are uniform (the few-row MoE kernels, the FP8
+// product); measured slower where a few items carry most of the work (a
+// popular expert's tiles would all land on one XCD) and for the persistent
+// MFMA product.
+__device__ __forceinline__ int xcd_block(int b, int G) {
+  if (G & 7) return b;
+  return (b & 7) * (G >> 3) + (b >> 3);
+}
+
 // ---- cross-lane exchange ------------------------------------------------------------
 
 // DPP controls (gfx9 encoding). Those named kDppXor<m> read lane l ^ m.

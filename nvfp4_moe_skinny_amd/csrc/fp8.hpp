@@ -36,7 +36,7 @@ __global__ void __launch_bounds__(64) fp8_skinny_gemm_kernel(const uint16_t* __r
   constexpr int RPT = 8 / S;  // rows per tile
   constexpr int K = S * kFp8SlabBytes;
   const int lane = threadIdx.x;
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = xcd_block((int)blockIdx.x, (int)gridDim.x);
   const int64_t n0 = tile * RPT;
   // codes: slab i is row i / S, columns (i % S) * 1024 + 16 lane .. + 15;
   // slabs of rows past N are not read (zero)

@@ -25,7 +25,8 @@ __global__ void __launch_bounds__(128, 4) fused_route_gate_kernel(MoeParams p,
   __shared__ float up_lds[64];
   __shared__ float lp[2][kRouteMaxE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int item = blockIdx.x / p.P, j = blockIdx.x % p.P;
+  const int b = xcd_block((int)blockIdx.x, (int)gridDim.x);
+  const int item = b / p.P, j = b % p.P;
   const int npairs = p.M * p.k;
   const bool sh = item >= npairs;
   const int m = sh ? item - npairs : item / p.k;

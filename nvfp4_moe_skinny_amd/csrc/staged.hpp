@@ -480,7 +480,8 @@ template <int LIC>
 __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel(MoeParams p) {
   __shared__ float ys[kMaxTopK + 1][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int m = blockIdx.x / p.P, t = blockIdx.x % p.P;
+  const int b = xcd_block((int)blockIdx.x, (int)gridDim.x);
+  const int m = b / p.P, t = b % p.P;
   const int L = LIC ? LIC : p.LI;
   const int rpt = 16384 / p.I;  // output rows of a down tile
   {
