@@ -9,9 +9,9 @@
 //   s_b = E4M3 round-to-nearest-even of amax_b / (6 g), saturating at 448;
 //   q   = sign of x | E2M1 round-to-nearest-even of |x| / (s_b g),
 //         saturating at 6; magnitude 0 where s_b g = 0.
-// Three passes: clear the per-matrix maxima, take them (integer maximum of
-// the magnitude bits, which order like the values), quantize each block,
-// then turn the maxima into g.
+// Passes: clear the per-matrix maxima, take them (integer maximum of the
+// magnitude bits, which order like the values), quantize each block, then
+// turn the maxima into g.
 #pragma once
 
 #include "common.hpp"
@@ -19,7 +19,12 @@
 namespace nvfp4moe {
 
 constexpr int kQuantThreads = 256;
-constexpr int kQuantMaxBlocksPerMatrix = 256;
+// Workgroups of the maximum pass per matrix: a pass of tens of thousands of
+// short workgroups is bound by how fast they start (measured over
+// [256][1024][2048]: 314 us with 256 workgroups per matrix, 184 us with 16).
+// The quantising pass, one thread per 16 elements, is bound by its arithmetic
+// (16 correctly rounded divisions per block) and keeps one block per thread.
+constexpr int kQuantMaxBlocksPerMatrix = 16;
 
 // Nearest finite non-negative E4M3 code to t >= 0, ties to the even code,
 // 448 (0x7E) at and above 448: the FP32 significand rounded to 3 bits in the
@@ -85,12 +90,12 @@ __device__ __forceinline__ float quant_g(uint32_t amax_bits) {
   return amax > 0.0f ? __fdiv_rn(amax, 2688.0f) : 1.0f;
 }
 
-// One thread per 16-element block (row n, block b) of matrix g.
-__global__ void __launch_bounds__(kQuantThreads) quant_blocks_kernel(
-    const uint16_t* __restrict__ x, int64_t blocks_per_matrix, int64_t G,
-    const uint32_t* __restrict__ amax, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
-  if (i >= blocks_per_matrix * G) return;
+// One 16-element block (row n, block b) of matrix g per thread.
+__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int64_t i,
+                                            int64_t blocks_per_matrix,
+                                            const uint32_t* __restrict__ amax,
+                                            uint8_t* __restrict__ codes,
+                                            uint8_t* __restrict__ scales) {
   const float gv = quant_g(amax[i / blocks_per_matrix]);
   const uint4* xp = reinterpret_cast<const uint4*>(x) + 2 * i;
   const uint4 a = load_stream(xp), b = load_stream(xp + 1);
@@ -110,6 +115,13 @@ __global__ void __launch_bounds__(kQuantThreads) quant_blocks_kernel(
   }
   *reinterpret_cast<uint2*>(codes + 8 * i) = make_uint2(q[0], q[1]);
   scales[i] = (uint8_t)sc;
+}
+
+__global__ void __launch_bounds__(kQuantThreads) quant_blocks_kernel(
+    const uint16_t* __restrict__ x, int64_t blocks_per_matrix, int64_t G,
+    const uint32_t* __restrict__ amax, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  if (i < blocks_per_matrix * G) quant_block(x, i, blocks_per_matrix, amax, codes, scales);
 }
 
 // g[i] = amax / 2688 (1 if 0), in place over the maxima.
