@@ -242,6 +242,9 @@ int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p) {
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "I = %lld must be a multiple of 16384 / H = %lld",
                 (long long)I, (long long)rows_per_tile(H));
   if (M * k + M > (int64_t)1 << 24) return fail(NVFP4MOE_ERR_UNSUPPORTED, "M too large");
+  // every grid (items x tiles per matrix) must stay below 2^31 blocks
+  if ((M * k + M) * tiles_per_matrix(H, I) > ((int64_t)1 << 31) - 1)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "M too large for the grid");
   if (a->schedule < 0 || a->schedule > 3)
     return fail(NVFP4MOE_ERR_BAD_SHAPE, "schedule must be 0, 1, 2 or 3 (got %d)",
                 (int)a->schedule);

@@ -129,6 +129,9 @@ def test_decode_validation(m):
     assert "workspace" in m.last_error_detail()
     assert dec(_args(m, x=4096 + 8)) == m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned
     assert dec(_args(m, schedule=4)) == m.NVFP4MOE_ERR_BAD_SHAPE
+    # (M*k + M) items x 256 tiles of a 2048 x 2048 matrix would pass 2^31 blocks
+    assert dec(_args(m, M=1_000_000, I=2048)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert "grid" in m.last_error_detail()
     # two launches need FP32 h for every pair: no MFMA slot (M < dense_min_rows)
     assert dec(_args(m, schedule=3, dense_min_rows=4)) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert dec(_args(m, ids=None)) == m.NVFP4MOE_ERR_NULL_ARG
