@@ -196,7 +196,11 @@ def test_moe_route_decode_fused(m, gpu, M, E, H, I, k, shared, resid, bias):
     (17, 8, 8, True, False, 16),   # each expert holds all 17 rows: a 1-row second block
     (48, 2, 2, True, False, 16),   # 48 rows: two passes over column blocks
     (40, 3, 2, False, True, 8),    # MFMA and VALU slots side by side
-    (33, 64, 8, True, True, 4)])
+    (33, 64, 8, True, True, 4),
+    # more rows: the wide kernels (2 or 4 rows per VALU batch, MFMA passes in turn)
+    (64, 4, 2, True, True, 16),    # every slot on MFMA, ragged last passes
+    (100, 16, 4, True, False, 8),  # MFMA and VALU slots, a 7-pass shared expert
+    (72, 256, 8, False, True, 4)])  # up to 256 active slots
 def test_moe_block_dense_mfma(m, gpu, M, E, k, shared, resid, dense_min_rows):
     """Three-launch schedule at H = 2048, I = 512, where slots with at least
     dense_min_rows rows run on BF16 MFMA (exact BF16 weights, h as hi + lo)."""
