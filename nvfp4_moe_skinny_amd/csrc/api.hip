@@ -398,6 +398,14 @@ int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w
   if (!aligned(x, 16) || !aligned(w_packed, 16))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "x and w_packed must be 16-byte aligned");
 #ifndef NVFP4MOE_GEMM_DENSE_OFF
+  if (K == 2048 && M >= kGemmDenseMinRows && M <= 16 &&
+      (tiles_per_matrix(N, K) + 1) / 2 <= kGemmSplitKMaxBlocks) {
+    const int64_t blocks16 = (tiles_per_matrix(N, K) + 1) / 2;
+    hipLaunchKernelGGL(skinny_gemm_splitk_kernel, dim3((unsigned)blocks16),
+                       dim3(64 * kGemmDenseWaves), 0, stream, x, M, (const uint8_t*)w_packed, N,
+                       y);
+    return launched("nvfp4_skinny_gemm");
+  }
   if (K == 2048 && M >= kGemmDenseMinRows) {
     const int64_t blocks16 = (tiles_per_matrix(N, K) + 1) / 2;  // 16-row blocks of W
     const int64_t want = (blocks16 + kGemmDenseWaves - 1) / kGemmDenseWaves;

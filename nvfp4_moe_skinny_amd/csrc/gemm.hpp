@@ -148,4 +148,74 @@ __global__ void __launch_bounds__(64 * kGemmDenseWaves) skinny_gemm_dense_kernel
   }
 }
 
+// ---- MFMA, K split over the four waves (K = 2048, 4 <= M <= 16, few rows of W) -----------
+//
+// With few 16-row blocks of W (N = 64: four) the kernel above runs one block
+// whose waves each decode a whole 16 x 2048 block after staging x: three
+// round trips and the full decode in a row, about 10 us for 74 KB. Here a
+// block takes one 16-row block of W and its four waves split K in quarters
+// (chunk columns 4 w .. 4 w + 3): each lane requests its W chunks and its x
+// pieces together (x straight from L2: 1 KB per row and wave), decodes a
+// quarter of the block, and the four partial D tiles are added in LDS in wave
+// order.
+constexpr int64_t kGemmSplitKMaxBlocks = 256;  // 16-row blocks of W (N <= 4096)
+
+__global__ void __launch_bounds__(64 * kGemmDenseWaves) skinny_gemm_splitk_kernel(
+    const uint16_t* __restrict__ x, int64_t M, const uint8_t* __restrict__ w, int64_t N,
+    uint16_t* __restrict__ y) {
+  constexpr int64_t K = 2048;
+  __shared__ f32x4 part[kGemmDenseWaves - 1][64];
+  const int lane = threadIdx.x & 63, m = lane & 15, grp = lane >> 4;
+  const int wave = threadIdx.x >> 6;
+  const int64_t ntiles = tiles_per_matrix(N, K);
+  const int64_t blk = blockIdx.x;
+  const int64_t t = 2 * blk + (m >> 3);  // this lane's tile
+  const float g = reinterpret_cast<const float*>(w + gscale_offset(1, N, K))[0];
+  DenseRows<4> d;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int q = 4 * wave + qq;
+    if (t < ntiles) {
+      load_dense_chunk(w + t * kTileBytes, 64, m & 7, 4 * q + grp, d.c[qq], d.s[qq]);
+    } else {
+      d.c[qq] = make_uint4(0, 0, 0, 0);
+      d.s[qq] = 0u;
+    }
+  }
+  const bool valid = m < M;
+  // x row m, pieces 4 (4 q + grp) + e of 16 bytes (8 BF16), q in this wave's quarter
+  uint4 xv[4][4];
+  const uint4* xrow = reinterpret_cast<const uint4*>(x + (valid ? m : 0) * K);
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      xv[qq][e] = valid ? xrow[4 * (4 * (4 * wave + qq) + grp) + e] : make_uint4(0, 0, 0, 0);
+  f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    bf16x8 a[4];
+    dense_a<4>(d, qq, a);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma_bf16(a[e], as_bf16x8(xv[qq][e]), acc);
+  }
+  if (wave > 0) part[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int v = 0; v < kGemmDenseWaves - 1; ++v) {
+      const f32x4 o = part[v][lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] += o[r];
+    }
+    if (valid) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t n = 16 * blk + 4 * grp + r;
+        if (n < N) y[m * N + n] = f32_to_bf16_rne(acc[r] * g);
+      }
+    }
+  }
+}
+
 }  // namespace nvfp4moe

@@ -69,7 +69,9 @@ def test_dequant_random_tensor(m, gpu):
                                      # ragged N, one and several 16-row passes over x
                                      (4, 2048, 8, 2.0 ** -9), (5, 2048, 24, 1.0),
                                      (16, 2048, 100, 0.37), (17, 2048, 40, 1.0),
-                                     (33, 2048, 17, 2.0 ** -9), (6, 2048, 4104, 1.0)])
+                                     (33, 2048, 17, 2.0 ** -9), (6, 2048, 4104, 1.0),
+                                     # K split over four waves: N <= 4096, M <= 16
+                                     (12, 2048, 4096, 1.0), (7, 2048, 1, 0.5)])
 def test_skinny_gemm(m, gpu, M, K, N, g):
     x, w = dense_skinny(seed=0, M=M, K=K, N=N, g=g)
     pw = pack(w, gpu, m)
