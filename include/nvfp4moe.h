@@ -116,8 +116,11 @@ int32_t nvfp4_quantize(const uint16_t* x, int64_t G, int64_t N, int64_t K, uint8
  *
  * y[M][N] = bf16_rne( sum_k x[m][k] * W[n][k] ), one packed matrix (G = 1),
  * FP32 accumulation, BF16 activations x [M][K] and output y [M][N] (raw BF16
- * bits). M >= 1 (rows beyond 8 are taken in batches of 8 over the same
- * weight registers).
+ * bits). M >= 1, N >= 1, K = 32 * 2^j <= 2048 (else NVFP4MOE_ERR_UNSUPPORTED);
+ * x and w_packed 16-byte aligned. The FP32 summation order depends on the
+ * shape: VALU tile products (rows in batches of 8) for M < 4 or K != 2048;
+ * BF16 MFMA tiles (the weights decode exactly to BF16) for K = 2048 and
+ * M >= 4, with K split over four waves when M <= 16 and N <= 4096.
  */
 int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w_packed,
                           int64_t N, uint16_t* y, hipStream_t stream);
