@@ -128,11 +128,8 @@ int32_t launch_staged_rows(const MoeParams& p, bool specialised, int rmax, bool 
     return specialised ? launch_staged_split<64, 16, true>(p, token_major, s)
                        : launch_staged_split<0, 0, false>(p, token_major, s);
   if (!specialised) return launch_staged<0, 0, 1, 1, false>(p, s);
-  switch (rmax) {
-    case 1: return launch_staged<64, 16, 1, 1, true>(p, s);
-    case 2: return launch_staged<64, 16, 2, 2, true>(p, s);
-    default: return launch_staged<64, 16, 4, 2, true>(p, s);
-  }
+  return rmax == 2 ? launch_staged<64, 16, 2, 2, true>(p, s)
+                   : launch_staged<64, 16, 4, 2, true>(p, s);
 }
 
 template <int LH, int LI>
@@ -397,7 +394,6 @@ int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w
                                (long long)K);
   if (!aligned(x, 16) || !aligned(w_packed, 16))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "x and w_packed must be 16-byte aligned");
-#ifndef NVFP4MOE_GEMM_DENSE_OFF
   if (K == 2048 && M >= kGemmDenseMinRows && M <= 16 &&
       (tiles_per_matrix(N, K) + 1) / 2 <= kGemmSplitKMaxBlocks) {
     const int64_t blocks16 = (tiles_per_matrix(N, K) + 1) / 2;
@@ -416,7 +412,6 @@ int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w
                        y);
     return launched("nvfp4_skinny_gemm");
   }
-#endif
   return dispatch_l<GemmLaunch>(K / 32, x, M, (const uint8_t*)w_packed, N, y, stream);
 }
 
