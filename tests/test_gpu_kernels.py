@@ -85,7 +85,8 @@ def test_skinny_gemm(m, gpu, M, K, N, g):
                                         (8, 256, 8, False), (16, 256, 8, True),
                                         (64, 256, 8, True), (65, 256, 8, False),
                                         (256, 256, 8, False), (1024, 256, 8, False),
-                                        (3, 5, 2, False), (7, 64, 1, True), (20, 8, 8, False)])
+                                        (3, 5, 2, False), (7, 64, 1, True), (20, 8, 8, False),
+                                        (5, 1, 1, True)])  # one expert: every row, w = 1
 def test_route_bit_exact(m, gpu, M, E, k, bias):
     for seed in range(3):
         lg = synth.normal_f32(synth.key(seed, 100, M, E), (M, E))
@@ -143,7 +144,8 @@ def _run_block(m, gpu, lay, residual=None, **kw):
     (5, 8, 512, 512, 8, True, False), (2, 32, 1024, 256, 2, False, True),
     (6, 4, 2048, 512, 1, True, True), (11, 256, 256, 256, 8, False, False),
     (70, 64, 2048, 512, 8, True, True), (33, 40, 1024, 1024, 3, False, False),
-    (4, 256, 2048, 2048, 8, False, False), (16, 8, 2048, 256, 8, True, False)])
+    (4, 256, 2048, 2048, 8, False, False), (16, 8, 2048, 256, 8, True, False),
+    (3, 1, 256, 256, 1, True, False)])  # a single expert (k = E = 1)
 def test_moe_block_small(m, gpu, M, E, H, I, k, shared, resid, schedule):
     lay = moe_layer(seed=M + E, wl=200, M=M, E_=E, H_=H, I_=I, k=k, shared=shared)
     residual = synth.normal_bf16(synth.key(5, 201, M), (M, H)) if resid else None

@@ -83,6 +83,19 @@ def test_prefill_m256_zipf(m, gpu):
     assert tol_ratio(out[rows], ref) <= 1.0
 
 
+def test_decode_max_rows_zipf(m, gpu):
+    """The largest row count the routing launch takes (M = 1024) through the
+    default schedule: routing bit-exact on every row, outputs on sampled rows
+    (every 97th and the last)."""
+    lay = W.moe_layer(0, wl=5, layer=7, M=1024, zipf_s=1.1)
+    r, out = _block(m, gpu, lay)
+    ids, w = oracle.route_topk(lay.logits, lay.k)
+    check_routing_exact(r, ids, w, lay.E)
+    rows = np.unique(np.append(np.arange(0, lay.M, 97), lay.M - 1))
+    ref = oracle.moe_block_touched(lay, ids, w, rows=rows)
+    assert tol_ratio(out[rows], ref) <= 1.0
+
+
 @pytest.mark.parametrize("check_layers", [(0, 1, 20, 39)])
 @pytest.mark.parametrize("router", [False, True])
 def test_stack_40_layers_teacher_forced(m, gpu, check_layers, router):
