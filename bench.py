@@ -100,7 +100,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="m4", choices=["m4", "m16", "m256", "head32k", "head248k", "fp8qkv",
-                                             "fp8o", "router", "quant", "stack40"])
+                                             "fp8o", "router", "quant", "stack40",
+                                             "ceiling"])
     p.add_argument("--rows", type=int, default=0, help="rows M of a skinny-GEMM workload")
     p.add_argument("--dense-min-rows", type=int, default=0,
                    help="rows from which a slot uses MFMA (0 = library default)")
@@ -150,6 +151,8 @@ def main():
         return bench_quant(args)
     if args.workload == "stack40":
         return bench_stack(args)
+    if args.workload == "ceiling":
+        return bench_ceiling(args)
     import torch
 
     import nvfp4_moe_skinny_amd as m
@@ -245,17 +248,23 @@ def main():
 
     replays = max(1, args.steps // S)
     steps = replays * S
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the timed replays in (up to) five consecutive runs, an event between runs
+    n_runs = min(5, replays)
+    bounds = [round(r * replays / n_runs) for r in range(n_runs + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_runs + 1)]
     torch.cuda.synchronize()
     wall0 = time.time()
-    ev0.record()
-    for _ in range(replays):
-        graph.replay()
-    ev1.record()
+    evs[0].record()
+    for r in range(n_runs):
+        for _ in range(bounds[r + 1] - bounds[r]):
+            graph.replay()
+        evs[r + 1].record()
     torch.cuda.synchronize()
     wall = time.time() - wall0
-    gpu_ms = ev0.elapsed_time(ev1)
+    gpu_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = gpu_ms / steps
+    run_ms = np.array([evs[r].elapsed_time(evs[r + 1]) / ((bounds[r + 1] - bounds[r]) * S)
+                       for r in range(n_runs)])
 
     # bytes from each step's actual routing (read back after the timed region)
     n_act = np.array([len(np.unique(routes[j].ids.cpu().numpy())) for j in range(n_sets)])
@@ -320,6 +329,9 @@ def main():
                            else "moe_route_topk + moe_nvfp4_decode"},
         "rows_per_s": round(rows_per_s, 1),
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "runs": {"n": n_runs, "median_ms_per_step": round(float(np.median(run_ms)), 6),
+                 "mean_ms_per_step": round(float(run_ms.mean()), 6),
+                 "std_ms_per_step": round(float(run_ms.std(ddof=1)) if n_runs > 1 else 0.0, 6)},
         "bytes_per_step": round(mean_bytes),
         "touched_experts_mean": float(np.mean(n_act)),
         "eager_ms_per_step": round(eager_ms, 4),
@@ -622,6 +634,50 @@ def bench_stack(args):
         "outputs_finite": ok, "setup_s": round(setup_s, 1),
     }), flush=True)
     return 0 if ok else 1
+
+
+def bench_ceiling(args):
+    """The read ceiling (nvfp4moe_stream_read: one pass of 16-byte nontemporal
+    loads, the weight streams' kind): a 4 GiB buffer, and buffers of the M=4
+    step's size (54 MB) and the M=16 step's (148 MB), each cycled over >= 2 GB
+    of distinct buffers so that every pass reads HBM, in graphs timed with
+    events. value = the 4 GiB rate."""
+    import torch
+
+    import nvfp4_moe_skinny_amd as m
+
+    dev = torch.device("cuda:0")
+    res = {}
+    for name, nbytes in (("4GiB", 4 << 30), ("54MB", 54_117_108 // 16 * 16),
+                         ("148MB", 147_000_000 // 16 * 16)):
+        copies = max(1, int(np.ceil(2e9 / nbytes)))
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        sinks = [torch.empty(m.nvfp4moe_stream_blocks(nbytes), dtype=torch.int32, device=dev)
+                 for _ in range(copies)]
+
+        def step(i, bufs=bufs, sinks=sinks, copies=copies):
+            m.nvfp4moe_stream_read(bufs[i % copies], sink=sinks[i % copies])
+
+        saved = args.steps
+        args.steps = min(args.steps, 200 if nbytes > 1e9 else 4000)
+        ms, n = time_graph(step, copies, args)
+        args.steps = saved
+        res[name] = {"bytes": nbytes, "us": round(ms * 1e3, 3),
+                     "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "passes_timed": n,
+                     "buffers_cycled": copies}
+        del bufs, sinks
+        torch.cuda.empty_cache()
+    gbs = res["4GiB"]["GB/s"]
+    print(json.dumps({
+        "metric": "HBM read ceiling GB/s (16-byte nontemporal loads, one pass)",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": res["4GiB"]["passes_timed"],
+        "warmup": args.warmup, "ms_per_step": round(res["4GiB"]["us"] / 1e3, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic", "config": {"workload": "stream_read_ceiling",
+                                         "timing": "hip graph replay, events"},
+        "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "sizes": res,
+    }), flush=True)
+    return 0
 
 
 def cpu_baseline(layers_host, logit_sets, x_host, copies, n_sets, budget_s, shared, bias):

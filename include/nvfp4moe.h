@@ -261,6 +261,25 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* args, hipStream_t stream);
 int32_t moe_nvfp4_route_decode(const moe_nvfp4_args* args, const float* logits, const float* bias,
                                hipStream_t stream);
 
+/* ---- read ceiling (measurement) ---------------------------------------------------------
+ *
+ * The pages judge a decode step by the memory bandwidth it reaches against
+ * the card's ([Weakest] page, "One config is the weakest card's config": the
+ * decode roofline as bandwidth over the weight bytes read). This reads a buffer
+ * once with the 16-byte nontemporal loads the weight streams use and nothing
+ * else, so its rate is the ceiling those streams can reach on this chip, to
+ * set beside the 8 TB/s peak.
+ * nvfp4moe_stream_blocks(bytes): the number of workgroups (and sink words)
+ * used for `bytes`, at most 8192; NVFP4MOE_ERR_BAD_SHAPE for bytes < 16.
+ * nvfp4moe_stream_read: src (device, 16-byte aligned, bytes % 16 == 0,
+ * bytes >= 16) is read once; workgroup b writes to sink[b] (device) the XOR
+ * of the 32-bit words it read, so the XOR of the sink words is the XOR of the
+ * whole buffer. sink_words below nvfp4moe_stream_blocks(bytes) gives
+ * NVFP4MOE_ERR_WORKSPACE. */
+int64_t nvfp4moe_stream_blocks(int64_t bytes);
+int32_t nvfp4moe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -83,6 +83,10 @@ def _load():
     L.moe_nvfp4_decode.argtypes = [ctypes.POINTER(MoeArgs), _vp]
     L.moe_nvfp4_route_decode.restype = _i32
     L.moe_nvfp4_route_decode.argtypes = [ctypes.POINTER(MoeArgs), _vp, _vp, _vp]
+    L.nvfp4moe_stream_blocks.restype = _i64
+    L.nvfp4moe_stream_blocks.argtypes = [_i64]
+    L.nvfp4moe_stream_read.restype = _i32
+    L.nvfp4moe_stream_read.argtypes = [_vp, _i64, _vp, _i64, _vp]
     return L
 
 
@@ -92,7 +96,7 @@ EXPORTS = ["nvfp4moe_strerror", "nvfp4moe_last_error_detail", "nvfp4moe_version"
            "fp8_skinny_gemm",
            "nvfp4_packed_bytes", "nvfp4_pack", "nvfp4_quantize", "nvfp4_dequant_f32", "nvfp4_skinny_gemm",
            "moe_route_topk", "moe_route_project_topk", "moe_nvfp4_workspace_bytes", "moe_nvfp4_decode",
-           "moe_nvfp4_route_decode"]
+           "moe_nvfp4_route_decode", "nvfp4moe_stream_blocks", "nvfp4moe_stream_read"]
 
 
 def strerror(status: int) -> str:
@@ -183,6 +187,26 @@ def nvfp4_dequant_f32(w: PackedNVFP4, apply_g: bool = True, path: int = 0,
     _check(lib.nvfp4_dequant_f32(_ptr(w.data), w.G, w.N, w.K, int(apply_g), int(path),
                                  _ptr(out), _stream(stream)), "nvfp4_dequant_f32")
     return out
+
+
+def nvfp4moe_stream_blocks(nbytes: int) -> int:
+    n = lib.nvfp4moe_stream_blocks(nbytes)
+    if n < 0:
+        raise NVFP4MoEError(int(n), "nvfp4moe_stream_blocks", last_error_detail())
+    return int(n)
+
+
+def nvfp4moe_stream_read(src: torch.Tensor, stream=None,
+                         sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Reads src (any dtype, contiguous, a multiple of 16 bytes) once; returns
+    the sink, int32 [blocks], whose XOR is the XOR of src's 32-bit words."""
+    nbytes = src.numel() * src.element_size()
+    blocks = nvfp4moe_stream_blocks(nbytes)
+    if sink is None:
+        sink = torch.empty(blocks, dtype=torch.int32, device=src.device)
+    _check(lib.nvfp4moe_stream_read(_ptr(src), nbytes, _ptr(sink), sink.numel(), _stream(stream)),
+           "nvfp4moe_stream_read")
+    return sink
 
 
 def nvfp4_skinny_gemm(x: torch.Tensor, w: PackedNVFP4, stream=None,

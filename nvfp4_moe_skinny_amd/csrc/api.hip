@@ -18,6 +18,7 @@
 #include "quant.hpp"
 #include "route.hpp"
 #include "router.hpp"
+#include "stream.hpp"
 
 static_assert(nvfp4moe::kMaxTopK == nvfp4moe::kRouteMaxK, "combine unrolls to the routing bound on k");
 
@@ -357,6 +358,33 @@ int32_t nvfp4_dequant_f32(const void* packed, int64_t G, int64_t N, int64_t K, i
   hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(chunks, 256, 1 << 16)), dim3(256), 0, stream,
                      (const uint8_t*)packed, G, N, K, (int)apply_g, (int)path, out);
   return launched("nvfp4_dequant_f32");
+}
+
+int32_t nvfp4moe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words,
+                             hipStream_t stream) {
+  if (!src || !sink) return fail(NVFP4MOE_ERR_NULL_ARG, "nvfp4moe_stream_read: null");
+  if (bytes < 16 || sink_words < 1) return fail(NVFP4MOE_ERR_BAD_SHAPE, "bytes >= 16, sink_words >= 1");
+  if (bytes % 16 != 0 || !aligned(src, 16))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "bytes %% 16 == 0 and src 16-byte aligned");
+  const int64_t n = bytes / 16;
+  const int64_t blocks = nvfp4moe_stream_blocks(bytes);
+  if (sink_words < blocks)
+    return fail(NVFP4MOE_ERR_WORKSPACE, "sink needs %lld words", (long long)blocks);
+  if (stream_unroll(bytes) == 1)
+    hipLaunchKernelGGL(stream_read_kernel<1>, dim3((unsigned)blocks), dim3(kStreamThreads), 0,
+                       stream, reinterpret_cast<const uint4*>(src), n, sink);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<8>, dim3((unsigned)blocks), dim3(kStreamThreads), 0,
+                       stream, reinterpret_cast<const uint4*>(src), n, sink);
+  return launched("nvfp4moe_stream_read");
+}
+
+int64_t nvfp4moe_stream_blocks(int64_t bytes) {
+  if (bytes < 16) return fail(NVFP4MOE_ERR_BAD_SHAPE, "bytes >= 16");
+  ok();
+  const int64_t per_block = (int64_t)kStreamThreads * stream_unroll(bytes);  // vectors per pass
+  const int64_t want = (bytes / 16 + per_block - 1) / per_block;
+  return want < kStreamMaxBlocks ? want : kStreamMaxBlocks;
 }
 
 int32_t nvfp4_quantize(const uint16_t* x, int64_t G, int64_t N, int64_t K, uint8_t* codes,

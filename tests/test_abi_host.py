@@ -97,6 +97,23 @@ def test_validation_errors_before_launch(m):
         m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned x
 
 
+def test_stream_read_validation(m):
+    L = m.lib
+    fake = 4096
+    # 1 vector per thread below 512 MiB, 8 from there on; at most 8192 workgroups
+    assert m.nvfp4moe_stream_blocks(16) == 1
+    assert m.nvfp4moe_stream_blocks(256 * 16) == 1
+    assert m.nvfp4moe_stream_blocks(256 * 16 + 16) == 2
+    assert m.nvfp4moe_stream_blocks(512 << 20) == 8192
+    assert m.nvfp4moe_stream_blocks(1 << 34) == 8192  # capped: the grid strides beyond
+    assert L.nvfp4moe_stream_blocks(15) == m.NVFP4MOE_ERR_BAD_SHAPE
+    assert L.nvfp4moe_stream_read(None, 64, fake, 1, None) == m.NVFP4MOE_ERR_NULL_ARG
+    assert L.nvfp4moe_stream_read(fake, 0, fake, 1, None) == m.NVFP4MOE_ERR_BAD_SHAPE
+    assert L.nvfp4moe_stream_read(fake, 40, fake, 1, None) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert L.nvfp4moe_stream_read(fake + 4, 64, fake, 1, None) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert L.nvfp4moe_stream_read(fake, 1 << 20, fake, 1, None) == m.NVFP4MOE_ERR_WORKSPACE
+
+
 def _args(m, **kw):
     a = m.MoeArgs()
     fake = 4096
