@@ -639,9 +639,10 @@ def bench_stack(args):
 def bench_ceiling(args):
     """The read ceiling (nvfp4moe_stream_read: one pass of 16-byte nontemporal
     loads, the weight streams' kind): a 4 GiB buffer, and buffers of the M=4
-    step's size (54 MB) and the M=16 step's (148 MB), each cycled over >= 2 GB
-    of distinct buffers so that every pass reads HBM, in graphs timed with
-    events. value = the 4 GiB rate."""
+    step's size (54 MB), of its two launches' weight bytes (36 MB gate_up,
+    18 MB down: 30.6 experts) and of the M=16 step's (147 MB), each cycled
+    over >= 2 GB of distinct buffers so that every pass reads HBM, in graphs
+    timed with events. value = the 4 GiB rate."""
     import torch
 
     import nvfp4_moe_skinny_amd as m
@@ -649,7 +650,8 @@ def bench_ceiling(args):
     dev = torch.device("cuda:0")
     res = {}
     for name, nbytes in (("4GiB", 4 << 30), ("54MB", 54_117_108 // 16 * 16),
-                         ("148MB", 147_000_000 // 16 * 16)):
+                         ("36MB", 36_097_351 // 16 * 16), ("18MB", 18_048_737 // 16 * 16),
+                         ("147MB", 147_000_000 // 16 * 16)):
         copies = max(1, int(np.ceil(2e9 / nbytes)))
         bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
         sinks = [torch.empty(m.nvfp4moe_stream_blocks(nbytes), dtype=torch.int32, device=dev)
