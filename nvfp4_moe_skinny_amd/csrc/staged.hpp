@@ -230,9 +230,66 @@ __device__ __forceinline__ float tile_row_value(const TileRegs& T, const uint4 (
   return part[0][0];
 }
 
+// MFMA in a two-wave item for a slot of at most 16 rows (M <= 16: one pass):
+// wave w takes chunk columns 8 w .. 8 w + 7, half of K. Per column it requests
+// the A chunk (gate tile rows 0-7, up tile rows 0-7) and the rows' x pieces
+// RING columns ahead, so a wave waits about two round trips rather than one
+// per column, in few registers; wave 1 hands its partial D tile to wave 0
+// through LDS, and wave 0 adds it (wave 0's half first) and writes h.
+template <int RING>
+__device__ __forceinline__ void staged_gate_dense_halves(const MoeParams& p, const SlotInfo& s,
+                                                         const uint8_t* tg, const uint8_t* tu,
+                                                         int j, float g, f32x4* dred) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 15, grp = lane >> 4;
+  const bool valid = m < s.rows;
+  const int pr = valid ? lane_pair(p, s, m) : -1;
+  const int xrow = valid ? pair_xrow(p, pr) : 0;
+  const uint8_t* tile = m < 8 ? tg : tu;
+  const int q0 = 8 * wave;
+  DenseRows<RING + 1> d;
+  uint4 xv[RING + 1][4];
+#pragma unroll
+  for (int q = 0; q < RING; ++q) {
+    load_dense_chunk(tile, 64, m & 7, 4 * (q0 + q) + grp, d.c[q], d.s[q]);
+    load_x_bf16(p.x, p.H, xrow, valid, 32 * (4 * (q0 + q) + grp), xv[q]);
+  }
+  f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    if (q + RING < 8) {
+      const int r = (q + RING) % (RING + 1);
+      load_dense_chunk(tile, 64, m & 7, 4 * (q0 + q + RING) + grp, d.c[r], d.s[r]);
+      load_x_bf16(p.x, p.H, xrow, valid, 32 * (4 * (q0 + q + RING) + grp), xv[r]);
+    }
+    const int c = q % (RING + 1);
+    bf16x8 a[4];
+    dense_a<RING + 1>(d, c, a);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma_bf16(a[e], as_bf16x8(xv[c][e]), acc);
+    __builtin_amdgcn_sched_barrier(0);  // RING + 1 columns' loads in flight at most
+  }
+  if (wave == 1) dred[lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    const f32x4 o = dred[lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += o[r];
+    uint32_t* hw = reinterpret_cast<uint32_t*>(p.hp);
+    // D row 4 grp + r: gate rows 0-7 in lanes 0-31, the matching up rows in lanes 32-63
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = acc[r];
+      const float u = partner32(v, lane);
+      if (lane < 32 && valid) hw[(int64_t)pr * p.I + j * 8 + 4 * grp + r] =
+          pack_hilo(silu(v * g) * (u * g));
+    }
+  }
+}
+
 template <int LHC, bool DENSE>
 __global__ void __launch_bounds__(128, 4) staged_gate_split_kernel(MoeParams p) {
   __shared__ float up_lds[64];
+  __shared__ f32x4 dred[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = staged_slot(p, blockIdx.x / p.P), j = blockIdx.x % p.P;
   PairCache pc;
@@ -245,7 +302,7 @@ __global__ void __launch_bounds__(128, 4) staged_gate_split_kernel(MoeParams p) 
   const uint8_t* tu = mat + (int64_t)(j + p.P) * kTileBytes;
   if constexpr (DENSE) {
     if (s.rows >= p.dense_min_rows) {
-      if (wave == 0) staged_gate_dense<2, 0>(p, s, tg, tu, j, g);
+      staged_gate_dense_halves<2>(p, s, tg, tu, j, g, dred);  // s.rows <= M <= 16
       return;
     }
   }
@@ -399,7 +456,8 @@ __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_down_kernel(MoeP
   const float g = s.shared ? p.sdn_g[0] : p.dn_g[s.e];
   if constexpr (DENSE) {
     if (s.rows >= p.dense_min_rows) {
-      staged_down_dense<2>(p, s, tile, t, g);
+      // one row per VALU batch is the M <= 16 launch: a single 16-row pass
+      staged_down_dense<RMAX == 1 ? 1 : 2>(p, s, tile, t, g);
       return;
     }
   }
