@@ -96,8 +96,9 @@ int32_t launch_decode(const MoeParams& p, hipStream_t s) {
 template <int LH, int LI, int RG, int RD, bool DENSE>
 int32_t launch_staged(const MoeParams& p, hipStream_t s) {
   const int grid = p.slots * p.P;
-  hipLaunchKernelGGL((staged_gate_kernel<LH, RG, DENSE>), dim3(grid), dim3(64), 0, s, p);
-  hipLaunchKernelGGL((staged_down_kernel<LI, RD, DENSE>), dim3(grid), dim3(64), 0, s, p);
+  // many rows: the items take the slots heaviest first
+  hipLaunchKernelGGL((staged_gate_kernel<LH, RG, DENSE, true>), dim3(grid), dim3(64), 0, s, p);
+  hipLaunchKernelGGL((staged_down_kernel<LI, RD, DENSE, true>), dim3(grid), dim3(64), 0, s, p);
   const int64_t outs = (int64_t)p.M * p.H;
   hipLaunchKernelGGL(staged_combine_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s,
                      p);
@@ -114,7 +115,7 @@ int32_t launch_staged_split(const MoeParams& p, bool token_major, hipStream_t s)
                        dim3((p.k + p.has_shared) * 64), 0, s, p);
     return launched("moe_nvfp4_decode");
   }
-  hipLaunchKernelGGL((staged_down_kernel<LI, 1, DENSE>), dim3(grid), dim3(64), 0, s, p);
+  hipLaunchKernelGGL((staged_down_kernel<LI, 1, DENSE, false>), dim3(grid), dim3(64), 0, s, p);
   const int64_t outs = (int64_t)p.M * p.H;
   hipLaunchKernelGGL(staged_combine_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s,
                      p);

@@ -31,6 +31,91 @@ __device__ __forceinline__ int staged_slot(const MoeParams& p, int item_slot) {
   return item_slot == 0 ? p.routed_slots : item_slot - 1;
 }
 
+// Slot of item slot `item` when the items take the slots heaviest first. With
+// many rows a few popular experts hold most of them (Zipf(1.1) at M = 256: 219
+// rows in one slot, whose items then take 55-75 us where a one-row item takes
+// 8), and in expert order such a slot can start last and finish far behind
+// the rest. Classes by row count, 1-3, 4-15, 16-63, 64-255, 256-1023, 1024 and
+// up, are taken from the heaviest down, each in slot order; the shared expert
+// (every row) comes first. Every wave of the launch computes the same order
+// from the slots' row counts (one round trip, as slot_info's) with wave scans.
+// The whole wave must be active. Returns false for items past the last slot.
+__device__ __forceinline__ int row_class(int rows) {
+  if (rows <= 0) return -1;
+  const int c = (31 - __builtin_clz((unsigned)rows)) >> 1;
+  return c < 5 ? c : 5;
+}
+
+__device__ __forceinline__ bool ordered_slot_info(const MoeParams& p, int item, SlotInfo& s) {
+  const int lane = threadIdx.x & 63;
+  if (p.has_shared) {
+    if (item == 0) return slot_info(p, p.routed_slots, s);
+    item -= 1;
+  }
+  const int na = *p.n_active;
+  int ao[5], ex[4], cls[4];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int sl = 4 * lane + j;
+    ao[j] = sl <= na ? p.active_offsets[sl] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int sl = 4 * lane + j;
+    ex[j] = sl < na ? p.active[sl] : -1;
+    cls[j] = sl < na ? row_class(ao[j + 1] - ao[j]) : -1;
+  }
+  if (item >= na) return false;
+  const int cmax = (int)wave_max_u32_all((uint32_t)(max(max(cls[0], cls[1]), max(cls[2], cls[3])) + 1)) - 1;
+  int base = 0;
+#pragma unroll 1
+  for (int c = cmax; c >= 0; --c) {
+    int in[4], pos[4], total;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) in[j] = cls[j] == c ? 1 : 0;
+    wave_scan256(in, lane, pos, total);
+    if (item < base + total) {
+      const int rank = item - base;
+      int jj = 0;
+      uint64_t hit = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint64_t b = __ballot(in[j] && pos[j] == rank);
+        if (b) {
+          hit = b;
+          jj = j;
+        }
+      }
+      const int l = hit ? (int)__builtin_ctzll(hit) : 0;  // one lane holds the rank
+      int e = 0, b0 = 0, b1 = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ej = __builtin_amdgcn_readlane(ex[j], l);
+        const int bj = __builtin_amdgcn_readlane(ao[j], l);
+        const int nj = __builtin_amdgcn_readlane(ao[j + 1], l);
+        if (j == jj) {
+          e = ej;
+          b0 = bj;
+          b1 = nj;
+        }
+      }
+      s.e = e;
+      s.row_begin = b0;
+      s.rows = b1 - b0;
+      s.shared = false;
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
+
+template <bool ORDER>
+__device__ __forceinline__ bool item_slot_info(const MoeParams& p, int item, SlotInfo& s) {
+  if constexpr (ORDER) return ordered_slot_info(p, item, s);
+  return slot_info(p, staged_slot(p, item), s);
+}
+
 __device__ __forceinline__ const uint8_t* gate_matrix(const MoeParams& p, const SlotInfo& s) {
   return s.shared ? p.sgu : p.gu + (int64_t)s.e * p.gu_mat_bytes;
 }
@@ -171,14 +256,15 @@ __device__ __forceinline__ void staged_gate_dense(const MoeParams& p, const Slot
   }
 }
 
-template <int LHC, int RMAX, bool DENSE>
+// ORDER: the items take the slots heaviest first (the launches for many rows).
+template <int LHC, int RMAX, bool DENSE, bool ORDER>
 __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_gate_kernel(MoeParams p) {
   const int lane = threadIdx.x;
-  const int slot = staged_slot(p, blockIdx.x / p.P), j = blockIdx.x % p.P;
+  const int j = blockIdx.x % p.P;
   PairCache pc;
   load_pair_cache(p, lane, pc);
   SlotInfo s;
-  if (!slot_info(p, slot, s)) return;
+  if (!item_slot_info<ORDER>(p, blockIdx.x / p.P, s)) return;
   const uint8_t* mat = gate_matrix(p, s);
   const float g = s.shared ? p.sgu_g[0] : p.gu_g[s.e];
   const uint8_t* tg = mat + (int64_t)j * kTileBytes;
@@ -444,14 +530,14 @@ __device__ __forceinline__ void staged_down_dense(const MoeParams& p, const Slot
   }
 }
 
-template <int LIC, int RMAX, bool DENSE>
+template <int LIC, int RMAX, bool DENSE, bool ORDER>
 __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_down_kernel(MoeParams p) {
   const int lane = threadIdx.x;
-  const int slot = staged_slot(p, blockIdx.x / p.P), t = blockIdx.x % p.P;
+  const int t = blockIdx.x % p.P;
   PairCache pc;
   load_pair_cache(p, lane, pc);
   SlotInfo s;
-  if (!slot_info(p, slot, s)) return;
+  if (!item_slot_info<ORDER>(p, blockIdx.x / p.P, s)) return;
   const uint8_t* tile = down_matrix(p, s) + (int64_t)t * kTileBytes;
   const float g = s.shared ? p.sdn_g[0] : p.dn_g[s.e];
   if constexpr (DENSE) {
