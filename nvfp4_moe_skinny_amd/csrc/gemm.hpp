@@ -77,7 +77,10 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const uint16_t* __rest
 constexpr int kGemmDenseMinRows = 4;
 constexpr int kGemmXStride = 4096;  // bytes per staged row of x
 constexpr int kGemmDenseWaves = 4;
-constexpr int64_t kGemmDenseMaxBlocks = 1024;  // grid-stride beyond
+// grid-stride beyond: 512 blocks of four waves is what is resident at two waves
+// per SIMD (the kernel's registers); 1024 ran in two generations (248K head
+// 74.3 us against 73.1), 768 in one and a half (83.6 us)
+constexpr int64_t kGemmDenseMaxBlocks = 512;
 
 // The chunks of 16-row block blk of W in MFMA order (zeros past the last tile
 // or block).
