@@ -62,6 +62,27 @@ def test_decode_m4(m, gpu):
     assert tol_ratio(out, ref) <= 1.0
 
 
+def test_decode_m4_route_decode(m, gpu):
+    """The headline step as the bench times it: moe_nvfp4_route_decode (routing
+    folded into the gate_up launch) on the M=4 workload, with a reused workspace
+    and the bench's caller-owned ids / w buffers."""
+    lay = W.decode_m4()
+    d = upload_layer(lay, gpu, m)
+    ws = m.moe_workspace(lay.M, lay.E, lay.k, lay.H, lay.I, False, gpu)
+    rb = m.routing_buffers(lay.M, lay.E, lay.k, gpu)
+    out = torch.empty((lay.M, lay.H), dtype=torch.bfloat16, device=gpu)
+    for _ in range(2):
+        m.moe_nvfp4_route_decode(d["x"], d["logits"], lay.k, d["gu"], d["dn"], workspace=ws,
+                                 out=out, ids=rb.ids, w=rb.w)
+    torch.cuda.synchronize()
+    ids, w = oracle.route_topk(lay.logits, lay.k)
+    assert (rb.ids.cpu().numpy() == ids).all()
+    assert np.max(np.abs(rb.w.cpu().numpy().astype(np.float64) - w)) <= 1e-6
+    ref = oracle.moe_block_touched(lay, ids, w)
+    assert tol_ratio(dev_bf16_to_f64(out), ref) <= 1.0
+    assert m.workspace_error_flag(ws) == 0
+
+
 def test_decode_m16_bias_shared(m, gpu):
     lay = W.decode_m16_shared()
     r, out = _block(m, gpu, lay)
