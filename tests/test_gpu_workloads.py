@@ -118,14 +118,17 @@ def test_decode_max_rows_zipf(m, gpu):
 
 
 @pytest.mark.parametrize("check_layers", [(0, 1, 20, 39)])
-@pytest.mark.parametrize("router", [False, True])
-def test_stack_40_layers_teacher_forced(m, gpu, check_layers, router):
+@pytest.mark.parametrize("router,entry", [(False, "decode"), (True, "decode"),
+                                          (False, "route_decode")])
+def test_stack_40_layers_teacher_forced(m, gpu, check_layers, router, entry):
     """40 MoE blocks (routed + shared expert + residual) and a dense 2048->64
     projection per layer, run as a chain on the GPU. Checked layers are
     recomputed by the oracle from the GPU's own BF16 input of that layer.
     router=True: the logits come from each layer's own BF16 router matrix
     applied to that layer's input on the GPU (routing follows the chain);
-    they are held to the tolerance, and the oracle routes the GPU's logits."""
+    they are held to the tolerance, and the oracle routes the GPU's logits.
+    entry="route_decode": each layer is one moe_nvfp4_route_decode call
+    (routing folded in, residual), as the 40-layer bench runs it."""
     x_host = W.stack_x0()
     x = to_dev_bf16(x_host, gpu)
     worst = 0.0
@@ -136,10 +139,14 @@ def test_stack_40_layers_teacher_forced(m, gpu, check_layers, router):
         if router:
             wr = W.router_weights(seed=0, wl=4, layer=l)
             logits, r = m.moe_route_project_topk(x, to_dev_bf16(wr, gpu), lay.k)
-        else:
+        elif entry == "decode":
             r = m.moe_route_topk(d["logits"], lay.k)
         proj = m.nvfp4_skinny_gemm(x, pw)
-        x_next = m.moe_nvfp4_decode(x, r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=x)
+        if entry == "decode":
+            x_next = m.moe_nvfp4_decode(x, r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=x)
+        else:
+            x_next, ids_d, w_d = m.moe_nvfp4_route_decode(x, d["logits"], lay.k, d["gu"], d["dn"],
+                                                          None, d["sgu"], d["sdn"], residual=x)
         torch.cuda.synchronize()
         if l in check_layers:
             if router:
@@ -148,11 +155,19 @@ def test_stack_40_layers_teacher_forced(m, gpu, check_layers, router):
                 ids, w = oracle.route_topk(lg, lay.k)
             else:
                 ids, w = oracle.route_topk(lay.logits, lay.k)
-            check_routing_exact(r, ids, w, lay.E)
+            if entry == "decode":
+                check_routing_exact(r, ids, w, lay.E)
+            else:
+                assert (ids_d.cpu().numpy() == ids).all()
+                assert np.max(np.abs(w_d.cpu().numpy().astype(np.float64) - w)) <= 1e-6
             ref = oracle.moe_block_touched(lay, ids, w, residual=x_host)
             worst = max(worst, tol_ratio(dev_bf16_to_f64(x_next), ref))
             # the block's own output, without the residual that dominates x_next
-            blk = m.moe_nvfp4_decode(x, r, d["gu"], d["dn"], d["sgu"], d["sdn"])
+            if entry == "decode":
+                blk = m.moe_nvfp4_decode(x, r, d["gu"], d["dn"], d["sgu"], d["sdn"])
+            else:
+                blk = m.moe_nvfp4_route_decode(x, d["logits"], lay.k, d["gu"], d["dn"], None,
+                                               d["sgu"], d["sdn"])[0]
             torch.cuda.synchronize()
             worst = max(worst, tol_ratio(dev_bf16_to_f64(blk), oracle.moe_block_touched(lay, ids, w)))
             p = lay.extra["proj"]
