@@ -145,7 +145,8 @@ def _run_block(m, gpu, lay, residual=None, **kw):
     (6, 4, 2048, 512, 1, True, True), (11, 256, 256, 256, 8, False, False),
     (70, 64, 2048, 512, 8, True, True), (33, 40, 1024, 1024, 3, False, False),
     (4, 256, 2048, 2048, 8, False, False), (16, 8, 2048, 256, 8, True, False),
-    (3, 1, 256, 256, 1, True, False)])  # a single expert (k = E = 1)
+    (3, 1, 256, 256, 1, True, False),  # a single expert (k = E = 1)
+    (40, 1, 2048, 512, 1, True, False)])  # one routed slot of 40 rows beside the shared one
 def test_moe_block_small(m, gpu, M, E, H, I, k, shared, resid, schedule):
     lay = moe_layer(seed=M + E, wl=200, M=M, E_=E, H_=H, I_=I, k=k, shared=shared)
     residual = synth.normal_bf16(synth.key(5, 201, M), (M, H)) if resid else None
