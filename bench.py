@@ -640,9 +640,10 @@ def bench_ceiling(args):
     """The read ceiling (nvfp4moe_stream_read: one pass of 16-byte nontemporal
     loads, the weight streams' kind): a 4 GiB buffer, and buffers of the M=4
     step's size (54 MB), of its two launches' weight bytes (36 MB gate_up,
-    18 MB down: 30.6 experts) and of the M=16 step's (147 MB), each cycled
-    over >= 2 GB of distinct buffers so that every pass reads HBM, in graphs
-    timed with events. value = the 4 GiB rate."""
+    18 MB down: 30.6 experts), those two as back-to-back launches, and the
+    M=16 step's (147 MB), each cycled over >= 2 GB of distinct buffers so that
+    every pass reads HBM, in graphs timed with events. value = the 4 GiB
+    rate."""
     import torch
 
     import nvfp4_moe_skinny_amd as m
@@ -669,6 +670,27 @@ def bench_ceiling(args):
                      "buffers_cycled": copies}
         del bufs, sinks
         torch.cuda.empty_cache()
+    # two launches back to back, 36 MB then 18 MB: the M=4 step's shape (gate_up
+    # weights, then down weights) with nothing computed and nothing waited for
+    sizes = (36_097_351 // 16 * 16, 18_048_737 // 16 * 16)
+    copies = int(np.ceil(2e9 / sum(sizes)))
+    bufs = [[torch.ones(b, dtype=torch.uint8, device=dev) for b in sizes] for _ in range(copies)]
+    sinks = [[torch.empty(m.nvfp4moe_stream_blocks(b), dtype=torch.int32, device=dev)
+              for b in sizes] for _ in range(copies)]
+
+    def pair(i):
+        for h in range(2):
+            m.nvfp4moe_stream_read(bufs[i % copies][h], sink=sinks[i % copies][h])
+
+    saved = args.steps
+    args.steps = min(args.steps, 4000)
+    ms, n = time_graph(pair, copies, args)
+    args.steps = saved
+    res["36MB+18MB"] = {"bytes": sum(sizes), "us": round(ms * 1e3, 3),
+                        "GB/s": round(sum(sizes) / (ms * 1e-3) / 1e9, 1), "passes_timed": n,
+                        "buffers_cycled": copies, "launches": 2}
+    del bufs, sinks
+    torch.cuda.empty_cache()
     gbs = res["4GiB"]["GB/s"]
     print(json.dumps({
         "metric": "HBM read ceiling GB/s (16-byte nontemporal loads, one pass)",
