@@ -93,6 +93,19 @@ int32_t launch_decode(const MoeParams& p, hipStream_t s) {
   return launched("moe_nvfp4_decode");
 }
 
+// token_down_combine blocks: one wave per slot up to eight slots, else two
+// slots a wave (five waves for eight routed slots and the shared expert).
+template <int LI>
+void launch_token_down(const MoeParams& p, hipStream_t s) {
+  const int n = p.k + p.has_shared;
+  if (n <= 8)
+    hipLaunchKernelGGL((token_down_combine_kernel<LI, 1>), dim3(p.M * p.P), dim3(n * 64), 0, s,
+                       p);
+  else
+    hipLaunchKernelGGL((token_down_combine_kernel<LI, 2>), dim3(p.M * p.P),
+                       dim3((n + 1) / 2 * 64), 0, s, p);
+}
+
 template <int LH, int LI, int RG, int RD, bool DENSE>
 int32_t launch_staged(const MoeParams& p, hipStream_t s) {
   const int grid = p.slots * p.P;
@@ -111,8 +124,7 @@ int32_t launch_staged_split(const MoeParams& p, bool token_major, hipStream_t s)
   const int grid = p.slots * p.P;
   hipLaunchKernelGGL((staged_gate_split_kernel<LH, DENSE>), dim3(grid), dim3(128), 0, s, p);
   if (token_major) {
-    hipLaunchKernelGGL((token_down_combine_kernel<LI>), dim3(p.M * p.P),
-                       dim3((p.k + p.has_shared) * 64), 0, s, p);
+    launch_token_down<LI>(p, s);
     return launched("moe_nvfp4_decode");
   }
   hipLaunchKernelGGL((staged_down_kernel<LI, 1, DENSE, false>), dim3(grid), dim3(64), 0, s, p);
@@ -587,11 +599,9 @@ int32_t moe_nvfp4_route_decode(const moe_nvfp4_args* a, const float* logits, con
   const int32_t st2 = launched("moe_nvfp4_route_decode gate_up");
   if (st2 != NVFP4MOE_OK) return st2;
   if (specialised)
-    hipLaunchKernelGGL(token_down_combine_kernel<16>, dim3(p.M * p.P),
-                       dim3((p.k + p.has_shared) * 64), 0, stream, p);
+    launch_token_down<16>(p, stream);
   else
-    hipLaunchKernelGGL(token_down_combine_kernel<0>, dim3(p.M * p.P),
-                       dim3((p.k + p.has_shared) * 64), 0, stream, p);
+    launch_token_down<0>(p, stream);
   return launched("moe_nvfp4_route_decode");
 }
 

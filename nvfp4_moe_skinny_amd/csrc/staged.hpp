@@ -620,29 +620,45 @@ constexpr int kTokenMajorMaxRows = 8;
 // expert, so reading a tile per pair rather than per expert costs almost no
 // extra bytes, and y never leaves the chip (no combine launch). h must be
 // FP32 words: every slot took the VALU gate_up path.
+// Slot q of row m (q = k: the shared expert), down tile t: its outputs to ys[q].
 template <int LIC>
+__device__ __forceinline__ void token_down_slot(const MoeParams& p, int q, int m, int t, int L,
+                                                float (*ys)[64]) {
+  const int lane = threadIdx.x & 63;
+  const bool sh = q == p.k;  // the shared expert's slot (only with has_shared)
+  const int pair = sh ? p.M * p.k + m : m * p.k + q;
+  const int e = sh ? 0 : p.ids[pair];
+  const uint8_t* tile =
+      (sh ? p.sdn : p.dn + (int64_t)e * p.dn_mat_bytes) + (int64_t)t * kTileBytes;
+  const float g = sh ? p.sdn_g[0] : p.dn_g[e];
+  TileRegs T;
+  float hr[1][32];
+  load_tile(tile, lane, T);
+  load_h_f32(p.hp, p.I, pair, true, 32 * (lane % L), hr[0]);
+  float part[1][8];
+  tile_dot_f32<1>(T, hr, part);
+  reduce_slabs_rt<LIC>(part[0], lane, L);
+  if (reduced_writer_rt(lane, L)) ys[q][reduced_row(lane, L)] = part[0][0] * g;
+}
+
+template <int LIC, int SPW>
 __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel(MoeParams p) {
   __shared__ float ys[kMaxTopK + 1][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int b = xcd_block((int)blockIdx.x, (int)gridDim.x);
   const int m = b / p.P, t = b % p.P;
   const int L = LIC ? LIC : p.LI;
   const int rpt = 16384 / p.I;  // output rows of a down tile
-  {
-    const bool sh = wave == p.k;  // the shared expert's wave (only with has_shared)
-    const int pair = sh ? p.M * p.k + m : m * p.k + wave;
-    const int e = sh ? 0 : p.ids[pair];
-    const uint8_t* tile =
-        (sh ? p.sdn : p.dn + (int64_t)e * p.dn_mat_bytes) + (int64_t)t * kTileBytes;
-    const float g = sh ? p.sdn_g[0] : p.dn_g[e];
-    TileRegs T;
-    float hr[1][32];
-    load_tile(tile, lane, T);
-    load_h_f32(p.hp, p.I, pair, true, 32 * (lane % L), hr[0]);
-    float part[1][8];
-    tile_dot_f32<1>(T, hr, part);
-    reduce_slabs_rt<LIC>(part[0], lane, L);
-    if (reduced_writer_rt(lane, L)) ys[wave][reduced_row(lane, L)] = part[0][0] * g;
+  // SPW slots per wave: one up to eight slots; with the shared expert beside
+  // eight routed ones a wave takes two (q = wave, wave + waves), so that a
+  // block of five waves leaves room for three blocks per CU where nine waves
+  // left room for one (40-layer stack at M = 8: 1364 -> 1318 us)
+  if constexpr (SPW == 1) {
+    token_down_slot<LIC>(p, wave, m, t, L, ys);
+  } else {
+    const int waves = (int)(blockDim.x >> 6);
+    token_down_slot<LIC>(p, wave, m, t, L, ys);
+    if (wave + waves < p.k + p.has_shared) token_down_slot<LIC>(p, wave + waves, m, t, L, ys);
   }
   __syncthreads();
   if ((int)threadIdx.x < rpt) {
