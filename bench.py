@@ -566,9 +566,10 @@ def bench_stack(args):
     """Sustained weight streaming: the 40-block stack at M = 8 rows, all 40
     layers' weights resident (about 18 GB of packed experts, more than any
     cache, so no copies are cycled). One step runs the 40 layers back to back
-    as a chain: per layer the dense 2048->64 projection of x_l, then
-    moe_nvfp4_route_decode (routing from the layer's synthetic logits, routed
-    + shared experts, residual x_l) writing x_{l+1}. The step is captured in
+    as a chain: per layer one moe_nvfp4_route_decode call (routing from the
+    layer's synthetic logits, routed + shared experts, residual x_l) writing
+    x_{l+1}, with the dense 2048->64 projection of x_l computed by blocks of
+    its down launch. The step is captured in
     one HIP graph (at most 320 steps are timed); bytes are every layer's
     touched experts + the shared expert + the projection + activations, from
     the routing each layer actually took."""
@@ -598,15 +599,15 @@ def bench_stack(args):
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    # one stream: the projection on a second stream (joined per step) measured
-    # slower, 40.2 vs 34.1 us per layer
+    # one call per layer: the projection's blocks ride in the block's down
+    # launch (as its own launch it cost 4.3 us a layer; on a second stream,
+    # joined per step, the layer measured slower still)
     def step(_i):
         for l in range(n_layers):
             gu, dn, sgu, sdn, pw, lg = layers[l]
-            m.nvfp4_skinny_gemm(xs[l], pw, out=projs[l])
             m.moe_nvfp4_route_decode(xs[l], lg, k, gu, dn, None, sgu, sdn, residual=xs[l],
                                      workspace=ws, out=xs[l + 1], ids=routes[l].ids,
-                                     w=routes[l].w)
+                                     w=routes[l].w, proj=pw, proj_out=projs[l])
 
     args.steps = min(args.steps, 320)  # a step streams ~4 GB: keep the timed region short
     ms, n_steps = time_graph(step, 1, args)
@@ -626,7 +627,7 @@ def bench_stack(args):
                    "layers": n_layers, "M": M, "E": E, "top_k": k, "hidden": H,
                    "expert_inter": I, "proj_n": N, "resident_weight_bytes": resident,
                    "timing": "hip graph replay of the 40-layer chain, events",
-                   "path": "nvfp4_skinny_gemm + moe_nvfp4_route_decode per layer"},
+                   "path": "moe_nvfp4_route_decode (with the projection) per layer"},
         "rows_per_s": round(M / (ms * 1e-3), 1),
         "layer_us": round(ms * 1e3 / n_layers, 3),
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_b,

@@ -201,6 +201,17 @@ typedef struct moe_nvfp4_args {
                                  use BF16 MFMA (0 = library default, 16; above M = never) */
   int32_t schedule;           /* 0 = library choice, 1 = one launch, 2 = three launches,
                                  3 = two launches (per-row down + combine) */
+  /* Optional, moe_nvfp4_route_decode only (NULL = none; moe_nvfp4_decode rejects
+     it): a dense projection of the same rows, proj_out[M][proj_n] = bf16_rne(
+     x W_p^T) as nvfp4_skinny_gemm computes it, bit for bit, with W_p packed
+     G = 1, N = proj_n, K = H. Its blocks ride in the down launch, so the
+     projection costs no launch of its own (the pages' 40-layer chain runs a
+     2048 -> 64 projection of every layer's input beside the MoE block). Needs
+     H = 2048, M <= 16, proj_n <= 4096, k (+1 with a shared expert) >= 4,
+     proj_w and proj_out 16-byte aligned. */
+  const void* proj_w;
+  int64_t proj_n;
+  uint16_t* proj_out;
 } moe_nvfp4_args;
 
 /* Workspace bytes for moe_nvfp4_decode: a control block of counters, then h

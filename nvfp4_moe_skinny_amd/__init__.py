@@ -44,6 +44,7 @@ class MoeArgs(ctypes.Structure):
         ("workspace", _vp), ("workspace_bytes", _i64),
         ("M", _i64), ("E", _i64), ("k", _i64), ("H", _i64), ("I", _i64),
         ("dense_min_rows", _i64), ("schedule", _i32),
+        ("proj_w", _vp), ("proj_n", _i64), ("proj_out", _vp),
     ]
 
 # moe_nvfp4_args.schedule
@@ -372,10 +373,13 @@ def moe_nvfp4_route_decode(x: torch.Tensor, logits: torch.Tensor, k: int,
                            workspace: Optional[torch.Tensor] = None, stream=None,
                            out: Optional[torch.Tensor] = None,
                            ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
-                           dense_min_rows: int = 0):
+                           dense_min_rows: int = 0, proj: Optional[PackedNVFP4] = None,
+                           proj_out: Optional[torch.Tensor] = None):
     """Routing (top-k + weights) and the MoE block in two launches, for few
     rows: x bfloat16 [M][H], logits float32 [M][E] (+ bias float32 [E]) ->
-    (out bfloat16 [M][H], ids int32 [M][k], w float32 [M][k])."""
+    (out bfloat16 [M][H], ids int32 [M][k], w float32 [M][k]). With proj
+    (packed [N][H]), proj_out bfloat16 [M][N] = x proj^T is written too, by
+    blocks of the down launch (allocated if not given)."""
     if x.dtype != torch.bfloat16 or logits.dtype != torch.float32:
         raise ValueError("x must be bfloat16 and logits float32")
     if bias is not None and bias.dtype != torch.float32:
@@ -405,6 +409,12 @@ def moe_nvfp4_route_decode(x: torch.Tensor, logits: torch.Tensor, k: int,
     a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     a.M, a.E, a.k, a.H, a.I = M, E, k, H, I
     a.dense_min_rows, a.schedule = dense_min_rows, SCHEDULE_AUTO
+    if proj is not None:
+        if proj.G != 1 or proj.K != H:
+            raise ValueError("proj must be one packed [N][H] matrix")
+        if proj_out is None:
+            proj_out = torch.empty((M, proj.N), dtype=torch.bfloat16, device=x.device)
+        a.proj_w, a.proj_n, a.proj_out = _ptr(proj.data), proj.N, _ptr(proj_out)
     _check(lib.moe_nvfp4_route_decode(ctypes.byref(a), _ptr(logits), _ptr(bias),
                                       _stream(stream)), "moe_nvfp4_route_decode")
     return out, ids, w

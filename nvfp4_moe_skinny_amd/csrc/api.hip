@@ -98,12 +98,12 @@ int32_t launch_decode(const MoeParams& p, hipStream_t s) {
 template <int LI>
 void launch_token_down(const MoeParams& p, hipStream_t s) {
   const int n = p.k + p.has_shared;
+  const int grid = p.M * p.P + p.proj_blocks;  // the projection's blocks first
   if (n <= 8)
-    hipLaunchKernelGGL((token_down_combine_kernel<LI, 1>), dim3(p.M * p.P), dim3(n * 64), 0, s,
-                       p);
+    hipLaunchKernelGGL((token_down_combine_kernel<LI, 1>), dim3(grid), dim3(n * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((token_down_combine_kernel<LI, 2>), dim3(p.M * p.P),
-                       dim3((n + 1) / 2 * 64), 0, s, p);
+    hipLaunchKernelGGL((token_down_combine_kernel<LI, 2>), dim3(grid), dim3((n + 1) / 2 * 64), 0,
+                       s, p);
 }
 
 template <int LH, int LI, int RG, int RD, bool DENSE>
@@ -550,6 +550,8 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
   MoeParams p;
   const int32_t st = prepare_decode(a, true, p);
   if (st != NVFP4MOE_OK) return st;
+  if (a->proj_w)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "the projection rides on moe_nvfp4_route_decode only");
   const int64_t M = a->M, H = a->H, I = a->I;
   const bool specialised = H == 2048 && I == 512;
   // three launches unless one is asked for: measured at M = 4, 16 and 256,
@@ -587,6 +589,20 @@ int32_t moe_nvfp4_route_decode(const moe_nvfp4_args* a, const float* logits, con
   if (specialised && M >= p.dense_min_rows)
     return fail(NVFP4MOE_ERR_UNSUPPORTED,
                 "moe_nvfp4_route_decode needs M < dense_min_rows (FP32 h for every pair)");
+  if (a->proj_w) {
+    if (!a->proj_out) return fail(NVFP4MOE_ERR_NULL_ARG, "proj_out is null");
+    if (a->proj_n < 1) return fail(NVFP4MOE_ERR_BAD_SHAPE, "proj_n must be >= 1");
+    if (H != 2048 || M > 16 || a->proj_n > 4096 || a->k + p.has_shared < 4)
+      return fail(NVFP4MOE_ERR_UNSUPPORTED,
+                  "projection: needs H = 2048, M <= 16, proj_n <= 4096, k (+ shared) >= 4");
+    if (!aligned(a->proj_w, 16) || !aligned(a->proj_out, 16))
+      return fail(NVFP4MOE_ERR_UNSUPPORTED, "proj_w and proj_out must be 16-byte aligned");
+    p.pw = static_cast<const uint8_t*>(a->proj_w);
+    p.py = a->proj_out;
+    p.pn = a->proj_n;
+    const int64_t blocks16 = (tiles_per_matrix(a->proj_n, 2048) + 1) / 2;
+    p.proj_blocks = (int)((blocks16 + 7) / 8 * 8);  // keeps the down blocks' XCD order
+  }
   const int grid = (int)((M * a->k + (p.has_shared ? M : 0)) * p.P);
   int32_t* ids = const_cast<int32_t*>(a->ids);
   float* w = const_cast<float*>(a->w);

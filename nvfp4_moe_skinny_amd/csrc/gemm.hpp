@@ -163,46 +163,49 @@ __global__ void __launch_bounds__(64 * kGemmDenseWaves) skinny_gemm_dense_kernel
 // order.
 constexpr int64_t kGemmSplitKMaxBlocks = 256;  // 16-row blocks of W (N <= 4096)
 
-__global__ void __launch_bounds__(64 * kGemmDenseWaves) skinny_gemm_splitk_kernel(
-    const uint16_t* __restrict__ x, int64_t M, const uint8_t* __restrict__ w, int64_t N,
-    uint16_t* __restrict__ y) {
+// One 16-row block blk of W, K split over waves 0-3 of the calling block (any
+// further waves only join the barrier; every wave of the block must call it).
+__device__ __forceinline__ void splitk_block(const uint16_t* __restrict__ x, int64_t M,
+                                             const uint8_t* __restrict__ w, int64_t N,
+                                             uint16_t* __restrict__ y, int64_t blk,
+                                             f32x4 (*part)[64]) {
   constexpr int64_t K = 2048;
-  __shared__ f32x4 part[kGemmDenseWaves - 1][64];
   const int lane = threadIdx.x & 63, m = lane & 15, grp = lane >> 4;
   const int wave = threadIdx.x >> 6;
   const int64_t ntiles = tiles_per_matrix(N, K);
-  const int64_t blk = blockIdx.x;
   const int64_t t = 2 * blk + (m >> 3);  // this lane's tile
-  const float g = reinterpret_cast<const float*>(w + gscale_offset(1, N, K))[0];
-  DenseRows<4> d;
-#pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
-    const int q = 4 * wave + qq;
-    if (t < ntiles) {
-      load_dense_chunk(w + t * kTileBytes, 64, m & 7, 4 * q + grp, d.c[qq], d.s[qq]);
-    } else {
-      d.c[qq] = make_uint4(0, 0, 0, 0);
-      d.s[qq] = 0u;
-    }
-  }
   const bool valid = m < M;
-  // x row m, pieces 4 (4 q + grp) + e of 16 bytes (8 BF16), q in this wave's quarter
-  uint4 xv[4][4];
-  const uint4* xrow = reinterpret_cast<const uint4*>(x + (valid ? m : 0) * K);
-#pragma unroll
-  for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      xv[qq][e] = valid ? xrow[4 * (4 * (4 * wave + qq) + grp) + e] : make_uint4(0, 0, 0, 0);
+  const float g = reinterpret_cast<const float*>(w + gscale_offset(1, N, K))[0];
   f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (wave < kGemmDenseWaves) {
+    DenseRows<4> d;
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
-    bf16x8 a[4];
-    dense_a<4>(d, qq, a);
+    for (int qq = 0; qq < 4; ++qq) {
+      const int q = 4 * wave + qq;
+      if (t < ntiles) {
+        load_dense_chunk(w + t * kTileBytes, 64, m & 7, 4 * q + grp, d.c[qq], d.s[qq]);
+      } else {
+        d.c[qq] = make_uint4(0, 0, 0, 0);
+        d.s[qq] = 0u;
+      }
+    }
+    // x row m, pieces 4 (4 q + grp) + e of 16 bytes (8 BF16), q in this wave's quarter
+    uint4 xv[4][4];
+    const uint4* xrow = reinterpret_cast<const uint4*>(x + (valid ? m : 0) * K);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = mfma_bf16(a[e], as_bf16x8(xv[qq][e]), acc);
+    for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        xv[qq][e] = valid ? xrow[4 * (4 * (4 * wave + qq) + grp) + e] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      bf16x8 a[4];
+      dense_a<4>(d, qq, a);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = mfma_bf16(a[e], as_bf16x8(xv[qq][e]), acc);
+    }
+    if (wave > 0) part[wave - 1][lane] = acc;
   }
-  if (wave > 0) part[wave - 1][lane] = acc;
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
@@ -219,6 +222,13 @@ __global__ void __launch_bounds__(64 * kGemmDenseWaves) skinny_gemm_splitk_kerne
       }
     }
   }
+}
+
+__global__ void __launch_bounds__(64 * kGemmDenseWaves) skinny_gemm_splitk_kernel(
+    const uint16_t* __restrict__ x, int64_t M, const uint8_t* __restrict__ w, int64_t N,
+    uint16_t* __restrict__ y) {
+  __shared__ f32x4 part[kGemmDenseWaves - 1][64];
+  splitk_block(x, M, w, N, y, blockIdx.x, part);
 }
 
 }  // namespace nvfp4moe

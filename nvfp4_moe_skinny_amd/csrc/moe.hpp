@@ -79,6 +79,12 @@ struct MoeParams {
   float* hp;           // [P_tot][I] h words (FP32, or hi / lo BF16 for MFMA slots)
   float* yp;           // [P_tot][H] expert outputs (FP32)
   int dense_min_rows;  // slots with at least this many rows use MFMA
+  // optional dense projection of x, computed by the first proj_blocks blocks
+  // of the down launch (token_down_combine_kernel): py [M][pn] = x W_p^T
+  const uint8_t* pw;
+  uint16_t* py;
+  int64_t pn;
+  int proj_blocks;     // a multiple of 8 (0: none), so the XCD order of the rest holds
   uint32_t spin_limit;
 };
 

@@ -15,6 +15,7 @@
 #pragma once
 
 #include "dense.hpp"
+#include "gemm.hpp"
 #include "moe.hpp"
 
 namespace nvfp4moe {
@@ -645,7 +646,13 @@ template <int LIC, int SPW>
 __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel(MoeParams p) {
   __shared__ float ys[kMaxTopK + 1][64];
   const int wave = threadIdx.x >> 6;
-  const int b = xcd_block((int)blockIdx.x, (int)gridDim.x);
+  if ((int)blockIdx.x < p.proj_blocks) {  // the projection's 16-row blocks of W_p (>= 4 waves)
+    __shared__ f32x4 ppart[kGemmDenseWaves - 1][64];
+    if ((int64_t)blockIdx.x < (tiles_per_matrix(p.pn, 2048) + 1) / 2)
+      splitk_block(p.x, p.M, p.pw, p.pn, p.py, blockIdx.x, ppart);
+    return;
+  }
+  const int b = xcd_block((int)blockIdx.x - p.proj_blocks, (int)gridDim.x - p.proj_blocks);
   const int m = b / p.P, t = b % p.P;
   const int L = LIC ? LIC : p.LI;
   const int rpt = 16384 / p.I;  // output rows of a down tile

@@ -160,6 +160,15 @@ def test_decode_validation(m):
     assert rd(_args(m, M=4, dense_min_rows=3)) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert rd(_args(m, workspace_bytes=1)) == m.NVFP4MOE_ERR_WORKSPACE
     assert dec(_args(m, schedule=-1)) == m.NVFP4MOE_ERR_BAD_SHAPE
+    # the projection rides on moe_nvfp4_route_decode only, within its limits
+    pj = dict(proj_w=4096, proj_n=64, proj_out=4096)
+    assert dec(_args(m, **pj)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert rd(_args(m, proj_w=4096, proj_n=64)) == m.NVFP4MOE_ERR_NULL_ARG
+    assert rd(_args(m, proj_w=4096, proj_n=0, proj_out=4096)) == m.NVFP4MOE_ERR_BAD_SHAPE
+    assert rd(_args(m, proj_w=4096, proj_n=4097, proj_out=4096)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert rd(_args(m, k=2, **pj)) == m.NVFP4MOE_ERR_UNSUPPORTED  # fewer than 4 waves
+    assert rd(_args(m, H=1024, **pj)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert rd(_args(m, proj_w=4096 + 8, proj_n=64, proj_out=4096)) == m.NVFP4MOE_ERR_UNSUPPORTED
     # h [M*k][I] + y [M*k][H] as 8-byte (value, flag) words, then as 4-byte words
     assert need >= 4 * 8 * (512 + 2048) * (8 + 4)
     # plus the control block: one 128-byte counter line per slot and per output tile

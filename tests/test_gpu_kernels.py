@@ -196,6 +196,28 @@ def test_moe_route_decode_fused(m, gpu, M, E, H, I, k, shared, resid, bias):
     assert m.workspace_error_flag(ws) == 0
 
 
+@pytest.mark.parametrize("M,k,shared,N", [(4, 8, False, 64), (8, 8, True, 64), (1, 4, False, 8),
+                                         (6, 3, True, 100), (12, 8, True, 4096)])
+def test_moe_route_decode_with_projection(m, gpu, M, k, shared, N):
+    """A dense projection of x computed by blocks of the down launch: bit-identical
+    to nvfp4_skinny_gemm of the same x, and the block's own outputs unchanged."""
+    lay = moe_layer(seed=M + N, wl=207, M=M, E_=64, H_=2048, I_=512, k=k, shared=shared)
+    _, pw_h = dense_skinny(seed=M, M=M, K=2048, N=N, g=2.0 ** -9)
+    d = upload_layer(lay, gpu, m)
+    pw = pack(pw_h, gpu, m)
+    args = (d["x"], d["logits"], k, d["gu"], d["dn"], None, d["sgu"], d["sdn"])
+    out0, ids0, w0 = m.moe_nvfp4_route_decode(*args)
+    py = torch.full((M, N), 7, dtype=torch.int16, device=gpu).view(torch.bfloat16)
+    out1, ids1, w1 = m.moe_nvfp4_route_decode(*args, proj=pw, proj_out=py)
+    ref = m.nvfp4_skinny_gemm(d["x"], pw)
+    torch.cuda.synchronize()
+    assert torch.equal(py.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(ids0, ids1) and torch.equal(w0.view(torch.int32), w1.view(torch.int32))
+    pref = oracle.gemm(lay.x, pw_h.codes[0], pw_h.scales[0], float(pw_h.g[0]))
+    assert tol_ratio(dev_bf16_to_f64(py), pref) <= 1.0
+
+
 @pytest.mark.parametrize("M,E,k,shared,resid,dense_min_rows", [
     (6, 4, 1, True, True, 1),      # every slot on MFMA, most blocks with one row
     (17, 8, 8, True, False, 16),   # each expert holds all 17 rows: a 1-row second block

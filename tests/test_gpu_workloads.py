@@ -145,8 +145,13 @@ def test_stack_40_layers_teacher_forced(m, gpu, check_layers, router, entry):
         if entry == "decode":
             x_next = m.moe_nvfp4_decode(x, r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=x)
         else:
+            # the projection computed inside the call: bit-identical to its own launch
+            proj_in = torch.empty_like(proj)
             x_next, ids_d, w_d = m.moe_nvfp4_route_decode(x, d["logits"], lay.k, d["gu"], d["dn"],
-                                                          None, d["sgu"], d["sdn"], residual=x)
+                                                          None, d["sgu"], d["sdn"], residual=x,
+                                                          proj=pw, proj_out=proj_in)
+            torch.cuda.synchronize()
+            assert torch.equal(proj_in.view(torch.int16), proj.view(torch.int16))
         torch.cuda.synchronize()
         if l in check_layers:
             if router:
