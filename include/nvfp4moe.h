@@ -205,8 +205,8 @@ typedef struct moe_nvfp4_args {
      it): a dense projection of the same rows, proj_out[M][proj_n] = bf16_rne(
      x W_p^T) as nvfp4_skinny_gemm computes it, bit for bit, with W_p packed
      G = 1, N = proj_n, K = H. Its blocks ride in the down launch, so the
-     projection costs no launch of its own (the pages' 40-layer chain runs a
-     2048 -> 64 projection of every layer's input beside the MoE block). Needs
+     projection costs no launch of its own (for a layer chain that projects
+     every layer's input, e.g. 2048 -> 64, beside the MoE block). Needs
      H = 2048, M <= 16, proj_n <= 4096, k (+1 with a shared expert) >= 4,
      proj_w and proj_out 16-byte aligned. */
   const void* proj_w;
