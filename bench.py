@@ -379,13 +379,32 @@ def time_graph(step, copies, args):
     graph.replay()
     torch.cuda.synchronize()
     replays = max(1, args.steps // S)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(replays):
-        graph.replay()
-    ev1.record()
+    # (up to) five consecutive runs, an event between runs; the runs' spread
+    # is kept for the JSON line (run_stats)
+    n_runs = min(5, replays)
+    bounds = [round(r * replays / n_runs) for r in range(n_runs + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_runs + 1)]
+    evs[0].record()
+    for r in range(n_runs):
+        for _ in range(bounds[r + 1] - bounds[r]):
+            graph.replay()
+        evs[r + 1].record()
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / (replays * S), replays * S
+    per = np.array([evs[r].elapsed_time(evs[r + 1]) / ((bounds[r + 1] - bounds[r]) * S)
+                    for r in range(n_runs)])
+    _RUNS.clear()
+    _RUNS.update({"n": n_runs, "median_ms_per_step": round(float(np.median(per)), 6),
+                  "mean_ms_per_step": round(float(per.mean()), 6),
+                  "std_ms_per_step": round(float(per.std(ddof=1)) if n_runs > 1 else 0.0, 6)})
+    return evs[0].elapsed_time(evs[-1]) / (replays * S), replays * S
+
+
+_RUNS = {}
+
+
+def run_stats():
+    """The per-run spread of the last time_graph call."""
+    return dict(_RUNS)
 
 
 def bench_fp8(args):
@@ -427,6 +446,7 @@ def bench_fp8(args):
                    "weights": "fp8 e4m3 + one f32 tensor scale", "weight_copies": copies,
                    "timing": "hip graph replay, events"},
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes,
+        "runs": run_stats(),
     }), flush=True)
     return 0
 
@@ -465,6 +485,7 @@ def bench_router(args):
         "config": {"workload": f"route_project_m{M}_e{E}_h{H}_k{k}", "M": M, "E": E, "H": H,
                    "top_k": k, "router_copies": copies, "timing": "hip graph replay, events"},
         "achieved_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 2), "bytes_per_step": step_bytes,
+        "runs": run_stats(),
     }), flush=True)
     return 0
 
@@ -517,6 +538,7 @@ def bench_quant(args):
         "config": {"workload": f"nvfp4_quantize_g{G}_n{N}_k{K}", "G": G, "N": N, "K": K,
                    "timing": "eager launches, events"},
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes,
+        "runs": run_stats(),
     }), flush=True)
     return 0
 
@@ -558,6 +580,7 @@ def bench_head(args):
         "config": {"workload": f"nvfp4_skinny_gemm_m{M}_k2048_n{N}", "M": M, "K": 2048, "N": N,
                    "weight_copies": copies, "timing": "hip graph replay, events"},
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes,
+        "runs": run_stats(),
     }), flush=True)
     return 0
 
@@ -631,6 +654,7 @@ def bench_stack(args):
         "rows_per_s": round(M / (ms * 1e-3), 1),
         "layer_us": round(ms * 1e3 / n_layers, 3),
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_b,
+        "runs": run_stats(),
         "touched_experts_mean": float(np.mean(n_act)),
         "outputs_finite": ok, "setup_s": round(setup_s, 1),
     }), flush=True)
