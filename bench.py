@@ -86,8 +86,6 @@ def step_bytes(M, E, k, H, I, n_active, shared, bias, grouped=True):
 
 def decode_kernels(schedule, M):
     """The launches of one decode call under the library's schedule choice."""
-    if schedule == 1:
-        return "moe_nvfp4_decode (one call: moe_decode_kernel)"
     gate = "staged_gate_split_kernel" if M <= 16 else "staged_gate_kernel"
     if schedule == 3 or (schedule == 0 and M <= 8):
         return f"moe_nvfp4_decode (one call: {gate}, token_down_combine_kernel)"
@@ -105,8 +103,8 @@ def parse():
     p.add_argument("--rows", type=int, default=0, help="rows M of a skinny-GEMM workload")
     p.add_argument("--dense-min-rows", type=int, default=0,
                    help="rows from which a slot uses MFMA (0 = library default)")
-    p.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2, 3],
-                   help="0 = library choice, 1 = one launch, 2 = three launches")
+    p.add_argument("--schedule", type=int, default=0, choices=[0, 2, 3],
+                   help="0 = library choice, 2 = three launches, 3 = two launches")
     p.add_argument("--path", default="auto", choices=["auto", "separate", "fused"],
                    help="separate: moe_route_topk + moe_nvfp4_decode; fused: "
                         "moe_nvfp4_route_decode (few rows); auto: fused for M <= 8")
@@ -204,7 +202,7 @@ def main():
     bs = [torch.from_numpy(L.bias).to(dev) if bias else None for L in logit_sets]
     routes = [m.routing_buffers(M, E, k, dev) for _ in range(n_sets)]
     outs = [torch.empty((M, H), dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
-    ws = m.moe_workspace(M, E, k, H, I, shared, dev)  # zero-filled once
+    ws = m.moe_workspace(M, E, k, H, I, shared, dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 

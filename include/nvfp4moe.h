@@ -199,7 +199,7 @@ typedef struct moe_nvfp4_args {
   int64_t M, E, k, H, I;
   int64_t dense_min_rows;     /* three-launch schedule: slots with at least this many rows
                                  use BF16 MFMA (0 = library default, 16; above M = never) */
-  int32_t schedule;           /* 0 = library choice, 1 = one launch, 2 = three launches,
+  int32_t schedule;           /* 0 = library choice, 2 = three launches,
                                  3 = two launches (per-row down + combine) */
   /* Optional, moe_nvfp4_route_decode only (NULL = none; moe_nvfp4_decode rejects
      it): a dense projection of the same rows, proj_out[M][proj_n] = bf16_rne(
@@ -208,24 +208,21 @@ typedef struct moe_nvfp4_args {
      projection costs no launch of its own (for a layer chain that projects
      every layer's input, e.g. 2048 -> 64, beside the MoE block). Needs
      H = 2048, M <= 16, proj_n <= 4096, k (+1 with a shared expert) >= 4,
-     proj_w and proj_out 16-byte aligned. */
+     proj_w and proj_out 16-byte aligned. Its blocks read x while other
+     blocks of the same launch write out: out and proj_out must not overlap x
+     (NVFP4MOE_ERR_BAD_SHAPE; residual == out stays fine, each output element
+     is read and written by one thread). */
   const void* proj_w;
   int64_t proj_n;
   uint16_t* proj_out;
 } moe_nvfp4_args;
 
-/* Workspace bytes for moe_nvfp4_decode: a control block of counters, then h
- * rows [M*k (+M)][I] and expert outputs [M*k (+M)][H] as 64-bit (FP32 value,
- * ready flag) words for the one-launch schedule, then the same rows as plain
- * 32-bit words for the three-launch schedule.
- * The workspace must be ZERO-FILLED ONCE before its first use; every call
- * leaves the counters and the 64-bit words at zero again when it completes
- * (the plain words are simply overwritten by the next three-launch call), so
- * it can be reused (and replayed inside a HIP graph) without clearing. A
- * workspace serves one call at a time: calls that may overlap (different
- * streams) need their own. Word 2 of the workspace is a sticky error flag that
- * a call sets if one of its internal dependency waits ever exceeds its bound
- * (the call still completes; its output is then not valid). */
+/* Workspace bytes for moe_nvfp4_decode / moe_nvfp4_route_decode: h rows
+ * [M*k (+M)][I] and expert outputs [M*k (+M)][H] as 32-bit words (the
+ * two-launch schedule uses the h rows only). Every call writes what it reads
+ * before reading it, so the workspace needs no initialisation and can be
+ * reused (and replayed inside a HIP graph) as it is. A workspace serves one
+ * call at a time: calls that may overlap (different streams) need their own. */
 int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, int64_t I,
                                   int32_t has_shared);
 
@@ -234,13 +231,11 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
  * with FP32 accumulation and FP32 h. The slot sum runs in j order, then the
  * shared term, then the residual; the result is bit-reproducible from run to
  * run (no floating-point atomics).
- * Schedules: three launches (gate_up, down, combine), two launches (gate_up,
+ * Schedules: three launches (gate_up, down, combine) or two launches (gate_up,
  * then one block per (row, down tile) that runs the row's k pairs (+ the
  * shared expert) on that tile and sums them in place: no y round trip and no
  * combine launch, at the cost of reading a tile once per pair instead of once
- * per expert, which with few rows is nearly the same set), or one launch
- * (every tile item of gate_up and down in one grid, exchanging h and y
- * through the workspace with flagged words). The library's choice (0) is two
+ * per expert, which with few rows is nearly the same set). The library's choice (0) is two
  * launches for M <= 8 when M < dense_min_rows or the shape has no MFMA path,
  * else three; schedule 3 asks for two launches and returns
  * NVFP4MOE_ERR_UNSUPPORTED unless M < dense_min_rows or the shape has no
@@ -252,7 +247,7 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
  * Extra support-set conditions: H and I are each 32 * 2^j in [256, 2048], and
  * I is a multiple of 16384 / H (gate and up halves start on a tile boundary).
  * Returns NVFP4MOE_ERR_WORKSPACE if the workspace is too small and
- * NVFP4MOE_ERR_BAD_SHAPE for a schedule other than 0, 1, 2 or 3. */
+ * NVFP4MOE_ERR_BAD_SHAPE for a schedule other than 0, 2 or 3. */
 int32_t moe_nvfp4_decode(const moe_nvfp4_args* args, hipStream_t stream);
 
 /* moe_route_topk (top-k and weights only, no grouping) and moe_nvfp4_decode

@@ -48,7 +48,7 @@ class MoeArgs(ctypes.Structure):
     ]
 
 # moe_nvfp4_args.schedule
-SCHEDULE_AUTO, SCHEDULE_ONE_LAUNCH, SCHEDULE_THREE_LAUNCHES, SCHEDULE_TWO_LAUNCHES = 0, 1, 2, 3
+SCHEDULE_AUTO, SCHEDULE_THREE_LAUNCHES, SCHEDULE_TWO_LAUNCHES = 0, 2, 3
 
 
 def _load():
@@ -125,6 +125,19 @@ def _ptr(t: Optional[torch.Tensor]):
     if not t.is_contiguous():
         raise ValueError("expected a contiguous tensor")
     return t.data_ptr()
+
+
+def _want(t: Optional[torch.Tensor], name: str, shape, dtype, device):
+    """Raises ValueError unless t is None or a contiguous tensor of this
+    shape and dtype on `device` (the kernels index it by these sizes)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {list(shape)}, got {t.dtype} {list(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, x on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
 def _stream(stream=None):
@@ -220,6 +233,7 @@ def nvfp4_skinny_gemm(x: torch.Tensor, w: PackedNVFP4, stream=None,
         raise ValueError("shape mismatch")
     if out is None:
         out = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device)
+    _want(out, "out", (M, w.N), torch.bfloat16, x.device)
     _check(lib.nvfp4_skinny_gemm(_ptr(x), M, K, _ptr(w.data), w.N, _ptr(out), _stream(stream)),
            "nvfp4_skinny_gemm")
     return out
@@ -237,6 +251,7 @@ def fp8_skinny_gemm(x: torch.Tensor, w_fp8: torch.Tensor, scale: torch.Tensor, s
         raise ValueError("shape mismatch")
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _want(out, "out", (M, N), torch.bfloat16, x.device)
     _check(lib.fp8_skinny_gemm(_ptr(x), M, K, _ptr(w_fp8), _ptr(scale), N, _ptr(out),
                                _stream(stream)), "fp8_skinny_gemm")
     return out
@@ -314,14 +329,28 @@ def moe_nvfp4_workspace_bytes(M: int, E: int, k: int, H: int, I: int, has_shared
 
 def moe_workspace(M: int, E: int, k: int, H: int, I: int, has_shared: bool,
                   device) -> torch.Tensor:
-    """A zero-filled workspace (the library keeps its control block at zero)."""
-    return torch.zeros(moe_nvfp4_workspace_bytes(M, E, k, H, I, has_shared), dtype=torch.uint8,
+    """A workspace for these sizes (needs no initialisation)."""
+    return torch.empty(moe_nvfp4_workspace_bytes(M, E, k, H, I, has_shared), dtype=torch.uint8,
                        device=device)
 
 
-def workspace_error_flag(workspace: torch.Tensor) -> int:
-    """Sticky flag (word 2) set if a dependency wait inside a call hit its bound."""
-    return int(workspace[8:12].view(torch.int32).item())
+def _check_block_args(x, E, k, H, I, residual, out, ids, w, workspace, shared_gate_up,
+                      shared_down):
+    M = x.shape[0]
+    dev = x.device
+    _want(residual, "residual", (M, H), torch.bfloat16, dev)
+    _want(out, "out", (M, H), torch.bfloat16, dev)
+    _want(ids, "ids", (M, k), torch.int32, dev)
+    _want(w, "w", (M, k), torch.float32, dev)
+    if workspace is not None and (workspace.dtype != torch.uint8 or workspace.device != dev
+                                  or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor on x's device")
+    if (shared_gate_up is None) != (shared_down is None):
+        raise ValueError("shared_gate_up and shared_down go together")
+    if shared_gate_up is not None:
+        if (shared_gate_up.G, shared_gate_up.N, shared_gate_up.K) != (1, 2 * I, H) or \
+                (shared_down.G, shared_down.N, shared_down.K) != (1, H, I):
+            raise ValueError("shared expert shapes do not match the routed experts")
 
 
 def moe_nvfp4_decode(x: torch.Tensor, routing: Routing, w_gate_up: PackedNVFP4,
@@ -332,8 +361,7 @@ def moe_nvfp4_decode(x: torch.Tensor, routing: Routing, w_gate_up: PackedNVFP4,
                      out: Optional[torch.Tensor] = None, schedule: int = SCHEDULE_AUTO,
                      dense_min_rows: int = 0) -> torch.Tensor:
     """x bfloat16 [M][H] -> bfloat16 [M][H] (routed experts + shared + residual).
-    schedule: SCHEDULE_AUTO / SCHEDULE_ONE_LAUNCH / SCHEDULE_THREE_LAUNCHES /
-    SCHEDULE_TWO_LAUNCHES;
+    schedule: SCHEDULE_AUTO / SCHEDULE_THREE_LAUNCHES / SCHEDULE_TWO_LAUNCHES;
     dense_min_rows: rows from which a slot uses MFMA (0 = library default)."""
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bfloat16")
@@ -342,6 +370,14 @@ def moe_nvfp4_decode(x: torch.Tensor, routing: Routing, w_gate_up: PackedNVFP4,
     k = routing.ids.shape[1]
     if w_gate_up.N != 2 * I or w_gate_up.K != H or w_down.N != H or w_down.G != E:
         raise ValueError("expert weight shapes do not match x")
+    _check_block_args(x, E, k, H, I, residual, out, routing.ids, routing.w, workspace,
+                      shared_gate_up, shared_down)
+    dev = x.device
+    for name, t, n in (("offsets", routing.offsets, E + 1), ("pairs", routing.pairs, M * k),
+                       ("active", routing.active, E),
+                       ("active_offsets", routing.active_offsets, E + 1),
+                       ("n_active", routing.n_active, 1)):
+        _want(t, name, (n,), torch.int32, dev)
     has_shared = shared_gate_up is not None
     if workspace is None:
         workspace = moe_workspace(M, E, k, H, I, has_shared, x.device)
@@ -390,6 +426,10 @@ def moe_nvfp4_route_decode(x: torch.Tensor, logits: torch.Tensor, k: int,
         raise ValueError("expert weight shapes do not match x")
     if tuple(logits.shape) != (M, E):
         raise ValueError("logits must be [M][E]")
+    _want(logits, "logits", (M, E), torch.float32, x.device)
+    _want(bias, "bias", (E,), torch.float32, x.device)
+    _check_block_args(x, E, k, H, I, residual, out, ids, w, workspace, shared_gate_up,
+                      shared_down)
     has_shared = shared_gate_up is not None
     if workspace is None:
         workspace = moe_workspace(M, E, k, H, I, has_shared, x.device)
@@ -414,6 +454,7 @@ def moe_nvfp4_route_decode(x: torch.Tensor, logits: torch.Tensor, k: int,
             raise ValueError("proj must be one packed [N][H] matrix")
         if proj_out is None:
             proj_out = torch.empty((M, proj.N), dtype=torch.bfloat16, device=x.device)
+        _want(proj_out, "proj_out", (M, proj.N), torch.bfloat16, x.device)
         a.proj_w, a.proj_n, a.proj_out = _ptr(proj.data), proj.N, _ptr(proj_out)
     _check(lib.moe_nvfp4_route_decode(ctypes.byref(a), _ptr(logits), _ptr(bias),
                                       _stream(stream)), "moe_nvfp4_route_decode")

@@ -54,6 +54,12 @@ bool valid_k(int64_t K) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Do the byte ranges [p, p + pn) and [q, q + qn) share a byte?
+bool overlaps(const void* p, int64_t pn, const void* q, int64_t qn) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + (uintptr_t)qn && b < a + (uintptr_t)pn;
+}
+
 int grid_for(int64_t items, int64_t per_block, int64_t cap) {
   int64_t g = (items + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -85,13 +91,6 @@ struct GemmLaunch {
     return launched("nvfp4_skinny_gemm");
   }
 };
-
-template <int LH, int LI, int RMAX>
-int32_t launch_decode(const MoeParams& p, hipStream_t s) {
-  const size_t lds = (size_t)RMAX * p.I * sizeof(float);
-  hipLaunchKernelGGL((moe_decode_kernel<LH, LI, RMAX>), dim3(p.total_blocks), dim3(64), lds, s, p);
-  return launched("moe_nvfp4_decode");
-}
 
 // token_down_combine blocks: one wave per slot up to eight slots, else two
 // slots a wave (five waves for eight routed slots and the shared expert).
@@ -146,45 +145,23 @@ int32_t launch_staged_rows(const MoeParams& p, bool specialised, int rmax, bool 
                    : launch_staged<64, 16, 4, 2, true>(p, s);
 }
 
-template <int LH, int LI>
-int32_t launch_decode_rows(const MoeParams& p, int rmax, hipStream_t s) {
-  switch (rmax) {
-    case 1: return launch_decode<LH, LI, 1>(p, s);
-    case 2: return launch_decode<LH, LI, 2>(p, s);
-    case 4: return launch_decode<LH, LI, 4>(p, s);
-    default: return launch_decode<LH, LI, 8>(p, s);
-  }
-}
-
 struct WsLayout {
-  int64_t ctl_off, cnt_ds_off, cnt_dn_off, h_off, y_off, hp_off, yp_off, total;
+  int64_t hp_off, yp_off, total;
 };
 
 int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
 
-// [control words | per-slot counters | per-output-tile counters] (one
-// 128-byte line per counter), then h [P][I] and y [P][H] as 64-bit (value,
-// ready) words, P = M*k (+ M with a shared expert): all of it zero between
-// calls. Then h [P][I] and y [P][H] as plain 32-bit words for the three-launch
-// schedule (overwritten by every call that uses them).
-WsLayout ws_layout(int64_t M, int64_t E, int64_t k, int64_t H, int64_t I, bool shared) {
+// h [P][I], then y [P][H], as 32-bit words, P = M*k (+ M with a shared
+// expert); every call overwrites what it reads, so the contents never carry
+// from one call to the next. The two-launch schedule uses h only.
+WsLayout ws_layout(int64_t M, int64_t k, int64_t H, int64_t I, bool shared) {
   const int64_t P = M * k + (shared ? M : 0);
-  const int64_t slots = (E < M * k ? E : M * k) + (shared ? 1 : 0);
-  const int64_t tiles = tiles_per_matrix(H, I);
-  const int64_t line = 4 * kCounterStride;
   WsLayout w;
-  w.ctl_off = 0;
-  w.cnt_ds_off = line;
-  w.cnt_dn_off = w.cnt_ds_off + slots * line;
-  w.h_off = align256(w.cnt_dn_off + tiles * line);
-  w.y_off = w.h_off + align256(P * I * 8);
-  w.hp_off = w.y_off + align256(P * H * 8);
-  w.yp_off = w.hp_off + align256(P * I * 4);
+  w.hp_off = 0;
+  w.yp_off = align256(P * I * 4);
   w.total = w.yp_off + align256(P * H * 4);
   return w;
 }
-
-int rows_per_batch(int64_t M) { return M <= 4 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8)); }
 
 bool valid_moe_dim(int64_t v) { return valid_k(v) && v >= 256; }
 
@@ -256,11 +233,10 @@ int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p) {
   // every grid (items x tiles per matrix) must stay below 2^31 blocks
   if ((M * k + M) * tiles_per_matrix(H, I) > ((int64_t)1 << 31) - 1)
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "M too large for the grid");
-  if (a->schedule < 0 || a->schedule > 3)
-    return fail(NVFP4MOE_ERR_BAD_SHAPE, "schedule must be 0, 1, 2 or 3 (got %d)",
-                (int)a->schedule);
+  if (a->schedule != 0 && a->schedule != 2 && a->schedule != 3)
+    return fail(NVFP4MOE_ERR_BAD_SHAPE, "schedule must be 0, 2 or 3 (got %d)", (int)a->schedule);
   const bool shared = a->shared_gate_up != nullptr;
-  const WsLayout ws = ws_layout(M, E, k, H, I, shared);
+  const WsLayout ws = ws_layout(M, k, H, I, shared);
   if (a->workspace_bytes < ws.total)
     return fail(NVFP4MOE_ERR_WORKSPACE, "workspace %lld < %lld bytes",
                 (long long)a->workspace_bytes, (long long)ws.total);
@@ -286,11 +262,6 @@ int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p) {
   p.residual = a->residual;
   p.out = a->out;
   uint8_t* wsb = (uint8_t*)a->workspace;
-  p.ctl = (uint32_t*)(wsb + ws.ctl_off);
-  p.cnt_ds = (uint32_t*)(wsb + ws.cnt_ds_off);
-  p.cnt_dn = (uint32_t*)(wsb + ws.cnt_dn_off);
-  p.h = (uint64_t*)(wsb + ws.h_off);
-  p.y = (uint64_t*)(wsb + ws.y_off);
   p.M = (int)M;
   p.E = (int)E;
   p.k = (int)k;
@@ -310,7 +281,6 @@ int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p) {
     p.sdn_g = (const float*)(p.sdn + gscale_offset(1, H, I));
   }
   p.P = (int)(I / rows_per_tile(H));  // == tiles_per_matrix(H, I) == H * I / 16384
-  p.total_blocks = (p.slots + 1) * p.P;
   p.pair_regs = M * k <= 128 ? (int)((M * k + 63) / 64) : 0;
   p.hp = (float*)(wsb + ws.hp_off);
   p.yp = (float*)(wsb + ws.yp_off);
@@ -543,7 +513,7 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
   if (!valid_moe_dim(H) || !valid_moe_dim(I))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be 32 * 2^j in [256, 2048]");
   ok();
-  return ws_layout(M, E, k, H, I, has_shared != 0).total;
+  return ws_layout(M, k, H, I, has_shared != 0).total;
 }
 
 int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
@@ -554,28 +524,18 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "the projection rides on moe_nvfp4_route_decode only");
   const int64_t M = a->M, H = a->H, I = a->I;
   const bool specialised = H == 2048 && I == 512;
-  // three launches unless one is asked for: measured at M = 4, 16 and 256,
-  // the staged kernels are at least as fast as the one-launch exchange
-  const bool staged = a->schedule != 1;
-  if (staged) {
-    // per-row down + combine needs FP32 h for every pair: no slot (the shared
-    // one has M rows) may take the MFMA gate_up path
-    const bool valu_h = M < p.dense_min_rows || !specialised;
-    if (a->schedule == 3 && !valu_h)
-      return fail(NVFP4MOE_ERR_UNSUPPORTED,
-                  "schedule 3 needs M < dense_min_rows (FP32 h for every pair)");
-    const bool token_major =
-        a->schedule == 3 || (a->schedule == 0 && valu_h && M <= kTokenMajorMaxRows);
-    // one row per batch keeps these kernels at three waves per SIMD; slots
-    // with many rows go to MFMA (specialised shapes) or take more batches
-    const int rmax_s = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    return launch_staged_rows(p, specialised, rmax_s, token_major, stream);
-  }
-  p.spin_limit = 1u << 22;
-  int rmax = rows_per_batch(M);
-  while (rmax > 1 && (int64_t)rmax * I * 4 > 48 * 1024) rmax /= 2;  // LDS for staged h rows
-  if (H == 2048 && I == 512) return launch_decode_rows<64, 16>(p, rmax, stream);
-  return launch_decode_rows<0, 0>(p, rmax, stream);
+  // per-row down + combine needs FP32 h for every pair: no slot (the shared
+  // one has M rows) may take the MFMA gate_up path
+  const bool valu_h = M < p.dense_min_rows || !specialised;
+  if (a->schedule == 3 && !valu_h)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED,
+                "schedule 3 needs M < dense_min_rows (FP32 h for every pair)");
+  const bool token_major =
+      a->schedule == 3 || (a->schedule == 0 && valu_h && M <= kTokenMajorMaxRows);
+  // one row per batch keeps these kernels at three waves per SIMD; slots
+  // with many rows go to MFMA (specialised shapes) or take more batches
+  const int rmax_s = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  return launch_staged_rows(p, specialised, rmax_s, token_major, stream);
 }
 
 int32_t moe_nvfp4_route_decode(const moe_nvfp4_args* a, const float* logits, const float* bias,
@@ -597,6 +557,13 @@ int32_t moe_nvfp4_route_decode(const moe_nvfp4_args* a, const float* logits, con
                   "projection: needs H = 2048, M <= 16, proj_n <= 4096, k (+ shared) >= 4");
     if (!aligned(a->proj_w, 16) || !aligned(a->proj_out, 16))
       return fail(NVFP4MOE_ERR_UNSUPPORTED, "proj_w and proj_out must be 16-byte aligned");
+    // the projection's blocks read x while the other blocks of the same launch
+    // write out (and the projection blocks write proj_out)
+    const int64_t xb = M * H * 2;
+    if (overlaps(a->x, xb, a->out, xb) || overlaps(a->x, xb, a->proj_out, M * a->proj_n * 2))
+      return fail(NVFP4MOE_ERR_BAD_SHAPE,
+                  "with a projection, out and proj_out must not overlap x (residual == out is "
+                  "fine)");
     p.pw = static_cast<const uint8_t*>(a->proj_w);
     p.py = a->proj_out;
     p.pn = a->proj_n;

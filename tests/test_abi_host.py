@@ -146,6 +146,7 @@ def test_decode_validation(m):
     assert "workspace" in m.last_error_detail()
     assert dec(_args(m, x=4096 + 8)) == m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned
     assert dec(_args(m, schedule=4)) == m.NVFP4MOE_ERR_BAD_SHAPE
+    assert dec(_args(m, schedule=1)) == m.NVFP4MOE_ERR_BAD_SHAPE
     # (M*k + M) items x 256 tiles of a 2048 x 2048 matrix would pass 2^31 blocks
     assert dec(_args(m, M=1_000_000, I=2048)) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert "grid" in m.last_error_detail()
@@ -169,8 +170,15 @@ def test_decode_validation(m):
     assert rd(_args(m, k=2, **pj)) == m.NVFP4MOE_ERR_UNSUPPORTED  # fewer than 4 waves
     assert rd(_args(m, H=1024, **pj)) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert rd(_args(m, proj_w=4096 + 8, proj_n=64, proj_out=4096)) == m.NVFP4MOE_ERR_UNSUPPORTED
-    # h [M*k][I] + y [M*k][H] as 8-byte (value, flag) words, then as 4-byte words
-    assert need >= 4 * 8 * (512 + 2048) * (8 + 4)
-    # plus the control block: one 128-byte counter line per slot and per output tile
-    assert need <= 4 * 8 * (512 + 2048) * (8 + 4) + 128 * (1 + 32 + 64) + 1024
-    assert m.moe_nvfp4_workspace_bytes(4, 256, 8, 2048, 512, True) > need
+    # with a projection, out and proj_out must not overlap x (4 x 2048 BF16 = 16 KB)
+    big = 1 << 24
+    assert rd(_args(m, x=big, out=big, **dict(pj, proj_out=2 * big))) == \
+        m.NVFP4MOE_ERR_BAD_SHAPE
+    assert rd(_args(m, x=big, out=big + 16384 - 16, **dict(pj, proj_out=2 * big))) == \
+        m.NVFP4MOE_ERR_BAD_SHAPE
+    assert rd(_args(m, x=big, out=2 * big, **dict(pj, proj_out=big + 512))) == \
+        m.NVFP4MOE_ERR_BAD_SHAPE
+    assert "overlap" in m.last_error_detail()
+    # h [M*k][I] and y [M*k][H] as 4-byte words
+    assert need == 4 * 8 * (512 + 2048) * 4
+    assert m.moe_nvfp4_workspace_bytes(4, 256, 8, 2048, 512, True) == (4 * 8 + 4) * (512 + 2048) * 4

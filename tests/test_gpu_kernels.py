@@ -137,7 +137,7 @@ def _run_block(m, gpu, lay, residual=None, **kw):
     return r, dev_bf16_to_f64(out)
 
 
-@pytest.mark.parametrize("schedule", [1, 2, 3])
+@pytest.mark.parametrize("schedule", [2, 3])
 @pytest.mark.parametrize("M,E,H,I,k,shared,resid", [
     (1, 16, 256, 256, 4, False, False), (3, 16, 256, 256, 4, True, False),
     (8, 16, 256, 512, 4, False, True), (17, 16, 512, 256, 4, True, True),
@@ -193,7 +193,6 @@ def test_moe_route_decode_fused(m, gpu, M, E, H, I, k, shared, resid, bias):
     assert tol_ratio(dev_bf16_to_f64(out), ref) <= 1.0
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
     assert torch.equal(again.view(torch.int16), out2.view(torch.int16))
-    assert m.workspace_error_flag(ws) == 0
 
 
 @pytest.mark.parametrize("M,k,shared,N", [(4, 8, False, 64), (8, 8, True, 64), (1, 4, False, 8),
@@ -242,30 +241,20 @@ def test_moe_block_dense_mfma(m, gpu, M, E, k, shared, resid, dense_min_rows):
 
 
 def test_moe_block_deterministic_and_workspace_reuse(m, gpu):
-    """Repeated calls on one workspace give bit-identical outputs and leave its
-    control block at zero with no wait timeouts flagged."""
+    """Repeated calls on one workspace, whatever it held before (it is filled
+    with garbage first), give bit-identical outputs, in both schedules."""
     lay = moe_layer(seed=3, wl=202, M=16, E_=32, H_=512, I_=256, k=8, shared=True)
     d = upload_layer(lay, gpu, m)
     r = m.moe_route_topk(d["logits"], lay.k)
     WS_SHAPE = (16, 32, 8, 512, 256, True)
     ws = m.moe_workspace(*WS_SHAPE, gpu)
+    ws.fill_(0xA5)
     call = lambda s: m.moe_nvfp4_decode(d["x"], r, d["gu"], d["dn"], d["sgu"], d["sdn"],
-                                        workspace=ws, schedule=s)
-    a = call(1)
-    outs = [call(1) for _ in range(5)]
-    torch.cuda.synchronize()
-    for b in outs:
-        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-    assert m.workspace_error_flag(ws) == 0
-    # counters and exchange words all cleared (the three-launch region is untouched)
-    assert int(ws.count_nonzero().item()) == 0
-    # the three-launch schedule on the same workspace: deterministic too, and it
-    # leaves the one-launch region at zero
-    b3 = [call(2) for _ in range(3)]
-    c = call(1)
-    torch.cuda.synchronize()
-    for b in b3[1:]:
-        assert torch.equal(b3[0].view(torch.int16), b.view(torch.int16))
-    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
-    assert m.workspace_error_flag(ws) == 0
+                                        workspace=ws, schedule=s, dense_min_rows=17)
+    for s in (2, 3):
+        a = call(s)
+        outs = [call(s) for _ in range(4)]
+        torch.cuda.synchronize()
+        for b in outs:
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
