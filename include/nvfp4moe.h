@@ -263,9 +263,29 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* args, hipStream_t stream);
  * bit-identical to moe_route_topk + moe_nvfp4_decode with schedule 3.
  * Reading a weight tile per pair rather than per expert suits small M (up to
  * about 8); NVFP4MOE_ERR_UNSUPPORTED when H = 2048, I = 512 and M >=
- * dense_min_rows. */
+ * dense_min_rows. The workspace holds the h rows only: (M*k (+M)) * I * 4
+ * bytes rounded up to 256 suffice (moe_nvfp4_workspace_bytes is more). */
 int32_t moe_nvfp4_route_decode(const moe_nvfp4_args* args, const float* logits, const float* bias,
                                hipStream_t stream);
+
+/* moe_nvfp4_route_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture that must not call hipMalloc, tight serving loops,
+ * harnesses that forbid allocation): the same launches, with the h rows in a
+ * scratch array of the library instead of args->workspace (workspace and
+ * workspace_bytes are ignored and may be NULL / 0). The array is a static
+ * device array of 4 MiB (4194304 bytes); each GPU the library runs on holds
+ * its own copy until the process ends, and the call allocates nothing. The
+ * h rows take (M*k (+M with a shared expert)) * I * 4 bytes rounded up to
+ * 256; a call that needs more returns NVFP4MOE_ERR_UNSUPPORTED before
+ * launching. The first call on a device looks up that device's copy (the
+ * current device's: call with the stream's device current). Every call on a
+ * GPU shares that GPU's one array, which keeps the last call's contents (each
+ * call writes the rows it reads first, so nothing needs clearing): calls that
+ * may overlap on one GPU (different streams, different host threads) race and
+ * must be ordered by the caller. Everything else, outputs included, is as for
+ * moe_nvfp4_route_decode, bit for bit. */
+int32_t moe_nvfp4_route_decode_static(const moe_nvfp4_args* args, const float* logits,
+                                      const float* bias, hipStream_t stream);
 
 /* ---- read ceiling (measurement) ---------------------------------------------------------
  *

@@ -84,6 +84,8 @@ def _load():
     L.moe_nvfp4_decode.argtypes = [ctypes.POINTER(MoeArgs), _vp]
     L.moe_nvfp4_route_decode.restype = _i32
     L.moe_nvfp4_route_decode.argtypes = [ctypes.POINTER(MoeArgs), _vp, _vp, _vp]
+    L.moe_nvfp4_route_decode_static.restype = _i32
+    L.moe_nvfp4_route_decode_static.argtypes = [ctypes.POINTER(MoeArgs), _vp, _vp, _vp]
     L.nvfp4moe_stream_blocks.restype = _i64
     L.nvfp4moe_stream_blocks.argtypes = [_i64]
     L.nvfp4moe_stream_read.restype = _i32
@@ -97,7 +99,8 @@ EXPORTS = ["nvfp4moe_strerror", "nvfp4moe_last_error_detail", "nvfp4moe_version"
            "fp8_skinny_gemm",
            "nvfp4_packed_bytes", "nvfp4_pack", "nvfp4_quantize", "nvfp4_dequant_f32", "nvfp4_skinny_gemm",
            "moe_route_topk", "moe_route_project_topk", "moe_nvfp4_workspace_bytes", "moe_nvfp4_decode",
-           "moe_nvfp4_route_decode", "nvfp4moe_stream_blocks", "nvfp4moe_stream_read"]
+           "moe_nvfp4_route_decode", "moe_nvfp4_route_decode_static", "nvfp4moe_stream_blocks",
+           "nvfp4moe_stream_read"]
 
 
 def strerror(status: int) -> str:
@@ -410,12 +413,16 @@ def moe_nvfp4_route_decode(x: torch.Tensor, logits: torch.Tensor, k: int,
                            out: Optional[torch.Tensor] = None,
                            ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
                            dense_min_rows: int = 0, proj: Optional[PackedNVFP4] = None,
-                           proj_out: Optional[torch.Tensor] = None):
+                           proj_out: Optional[torch.Tensor] = None,
+                           static_scratch: bool = False):
     """Routing (top-k + weights) and the MoE block in two launches, for few
     rows: x bfloat16 [M][H], logits float32 [M][E] (+ bias float32 [E]) ->
     (out bfloat16 [M][H], ids int32 [M][k], w float32 [M][k]). With proj
     (packed [N][H]), proj_out bfloat16 [M][N] = x proj^T is written too, by
-    blocks of the down launch (allocated if not given)."""
+    blocks of the down launch (allocated if not given).
+    static_scratch: call moe_nvfp4_route_decode_static, whose h rows live in
+    the library's own device array (no workspace; pass out, ids and w to
+    allocate nothing here either)."""
     if x.dtype != torch.bfloat16 or logits.dtype != torch.float32:
         raise ValueError("x must be bfloat16 and logits float32")
     if bias is not None and bias.dtype != torch.float32:
@@ -431,7 +438,7 @@ def moe_nvfp4_route_decode(x: torch.Tensor, logits: torch.Tensor, k: int,
     _check_block_args(x, E, k, H, I, residual, out, ids, w, workspace, shared_gate_up,
                       shared_down)
     has_shared = shared_gate_up is not None
-    if workspace is None:
+    if workspace is None and not static_scratch:
         workspace = moe_workspace(M, E, k, H, I, has_shared, x.device)
     if out is None:
         out = torch.empty_like(x)
@@ -446,7 +453,8 @@ def moe_nvfp4_route_decode(x: torch.Tensor, logits: torch.Tensor, k: int,
     a.shared_down = _ptr(shared_down.data) if has_shared else None
     a.residual = _ptr(residual)
     a.out = _ptr(out)
-    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    if not static_scratch:
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     a.M, a.E, a.k, a.H, a.I = M, E, k, H, I
     a.dense_min_rows, a.schedule = dense_min_rows, SCHEDULE_AUTO
     if proj is not None:
@@ -456,6 +464,10 @@ def moe_nvfp4_route_decode(x: torch.Tensor, logits: torch.Tensor, k: int,
             proj_out = torch.empty((M, proj.N), dtype=torch.bfloat16, device=x.device)
         _want(proj_out, "proj_out", (M, proj.N), torch.bfloat16, x.device)
         a.proj_w, a.proj_n, a.proj_out = _ptr(proj.data), proj.N, _ptr(proj_out)
-    _check(lib.moe_nvfp4_route_decode(ctypes.byref(a), _ptr(logits), _ptr(bias),
-                                      _stream(stream)), "moe_nvfp4_route_decode")
+    if static_scratch:
+        _check(lib.moe_nvfp4_route_decode_static(ctypes.byref(a), _ptr(logits), _ptr(bias),
+                                                 _stream(stream)), "moe_nvfp4_route_decode_static")
+    else:
+        _check(lib.moe_nvfp4_route_decode(ctypes.byref(a), _ptr(logits), _ptr(bias),
+                                          _stream(stream)), "moe_nvfp4_route_decode")
     return out, ids, w

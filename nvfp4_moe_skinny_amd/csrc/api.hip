@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "nvfp4moe.h"
 
@@ -23,6 +24,14 @@
 static_assert(nvfp4moe::kMaxTopK == nvfp4moe::kRouteMaxK, "combine unrolls to the routing bound on k");
 
 using namespace nvfp4moe;
+
+// Scratch of moe_nvfp4_route_decode_static: the h rows of one call. Every GPU
+// the library runs on holds its own copy until the process ends; host code
+// never uses this name as an address (it is a host-side stand-in), only the
+// address hipGetSymbolAddress returns for the current device.
+constexpr int64_t kScratchBytes = 4 << 20;
+constexpr int kScratchMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -210,11 +219,15 @@ int32_t launch_route(const float* logits, const float* bias, int64_t M, int64_t 
 namespace {
 
 // Validates the arguments and fills p. routed: the routing arrays come from
-// moe_route_topk (moe_nvfp4_decode); otherwise only ids and w, which the call
-// writes (moe_nvfp4_route_decode).
-int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p) {
+// moe_route_topk (moe_nvfp4_decode: h and y in the workspace); otherwise only
+// ids and w, which the call writes (moe_nvfp4_route_decode: h only). scratch:
+// when not null, used in place of a->workspace (which is then ignored).
+int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p,
+                       void* scratch = nullptr, int64_t scratch_bytes = 0) {
   if (!a) return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_decode: args is null");
-  if (!a->x || !a->ids || !a->w || !a->w_gate_up || !a->w_down || !a->out || !a->workspace ||
+  void* const wsp = scratch ? scratch : a->workspace;
+  const int64_t ws_bytes = scratch ? scratch_bytes : a->workspace_bytes;
+  if (!a->x || !a->ids || !a->w || !a->w_gate_up || !a->w_down || !a->out || !wsp ||
       (routed && (!a->offsets || !a->pairs || !a->active || !a->active_offsets || !a->n_active)))
     return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_decode: a required pointer is null");
   if ((a->shared_gate_up == nullptr) != (a->shared_down == nullptr))
@@ -237,11 +250,12 @@ int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p) {
     return fail(NVFP4MOE_ERR_BAD_SHAPE, "schedule must be 0, 2 or 3 (got %d)", (int)a->schedule);
   const bool shared = a->shared_gate_up != nullptr;
   const WsLayout ws = ws_layout(M, k, H, I, shared);
-  if (a->workspace_bytes < ws.total)
-    return fail(NVFP4MOE_ERR_WORKSPACE, "workspace %lld < %lld bytes",
-                (long long)a->workspace_bytes, (long long)ws.total);
+  const int64_t need = routed ? ws.total : ws.yp_off;
+  if (ws_bytes < need)
+    return fail(NVFP4MOE_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes,
+                (long long)need);
   if (!aligned(a->x, 16) || !aligned(a->w_gate_up, 16) || !aligned(a->w_down, 16) ||
-      !aligned(a->workspace, 256) || (shared && (!aligned(a->shared_gate_up, 16) ||
+      !aligned(wsp, 256) || (shared && (!aligned(a->shared_gate_up, 16) ||
                                                  !aligned(a->shared_down, 16))))
     return fail(NVFP4MOE_ERR_UNSUPPORTED,
                 "x and weights need 16-byte, workspace 256-byte alignment");
@@ -261,7 +275,7 @@ int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p) {
   p.sdn = (const uint8_t*)a->shared_down;
   p.residual = a->residual;
   p.out = a->out;
-  uint8_t* wsb = (uint8_t*)a->workspace;
+  uint8_t* wsb = (uint8_t*)wsp;
   p.M = (int)M;
   p.E = (int)E;
   p.k = (int)k;
@@ -538,11 +552,17 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
   return launch_staged_rows(p, specialised, rmax_s, token_major, stream);
 }
 
-int32_t moe_nvfp4_route_decode(const moe_nvfp4_args* a, const float* logits, const float* bias,
-                               hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_nvfp4_route_decode with its h rows in `scratch` (scratch_bytes) when
+// not null, else in the caller's workspace.
+int32_t route_decode(const moe_nvfp4_args* a, const float* logits, const float* bias,
+                     hipStream_t stream, void* scratch, int64_t scratch_bytes) {
   if (!logits) return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_route_decode: logits is null");
   MoeParams p;
-  const int32_t st = prepare_decode(a, false, p);
+  const int32_t st = prepare_decode(a, false, p, scratch, scratch_bytes);
   if (st != NVFP4MOE_OK) return st;
   const int64_t M = a->M, H = a->H, I = a->I;
   const bool specialised = H == 2048 && I == 512;
@@ -586,6 +606,58 @@ int32_t moe_nvfp4_route_decode(const moe_nvfp4_args* a, const float* logits, con
   else
     launch_token_down<0>(p, stream);
   return launched("moe_nvfp4_route_decode");
+}
+
+// ---- scratch for the call that allocates nothing --------------------------------------
+
+std::mutex g_scratch_mu;
+void* g_scratch[kScratchMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (each GPU holds its own copy at its own address).
+int32_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(NVFP4MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchMaxDevices)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev,
+                kScratchMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(NVFP4MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_nvfp4_route_decode(const moe_nvfp4_args* a, const float* logits, const float* bias,
+                               hipStream_t stream) {
+  return route_decode(a, logits, bias, stream, nullptr, 0);
+}
+
+int32_t moe_nvfp4_route_decode_static(const moe_nvfp4_args* a, const float* logits,
+                                      const float* bias, hipStream_t stream) {
+  if (!a) return fail(NVFP4MOE_ERR_NULL_ARG, "moe_nvfp4_route_decode_static: args is null");
+  if (a->M >= 1 && a->k >= 1 && a->H >= 1 && a->I >= 1) {
+    const int64_t need = ws_layout(a->M, a->k, a->H, a->I, a->shared_gate_up != nullptr).yp_off;
+    if (need > kScratchBytes)
+      return fail(NVFP4MOE_ERR_UNSUPPORTED,
+                  "h rows need %lld bytes of scratch; the static scratch holds %lld",
+                  (long long)need, (long long)kScratchBytes);
+  }
+  void* ptr = nullptr;
+  const int32_t st = scratch_address(&ptr);
+  if (st != NVFP4MOE_OK) return st;
+  return route_decode(a, logits, bias, stream, ptr, kScratchBytes);
 }
 
 }  // extern "C"
