@@ -4,6 +4,11 @@ TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
 benchmark's CPU-baseline leg. The GPU library and its Python binding never
 import it. Functions take and return numpy arrays in the canonical layouts
 documented in oracle.h.
+
+The products and the MoE block split their outputs over threads (results are
+bit-identical for every thread count): by default the CPUs this process may
+run on, at most 16, or NVFP4MOE_ORACLE_THREADS if set; set_threads() changes
+it.
 """
 import ctypes
 import os
@@ -54,11 +59,38 @@ def lib():
                                         ctypes.c_float, _vp]
         L.oracle_moe_block.restype = None
         L.oracle_moe_block.argtypes = [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp] + [_vp] * 13
+        L.oracle_moe_block_f64.restype = None
+        L.oracle_moe_block_f64.argtypes = [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp] + \
+            [_vp] * 13
+        L.oracle_set_threads.restype = None
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_threads.restype = ctypes.c_int
+        L.oracle_threads.argtypes = []
+        L.oracle_set_threads(default_threads())
         L.oracle_moe_decode.restype = ctypes.c_int
         L.oracle_moe_decode.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64] + \
             [_vp] * 16
         _lib = L
     return _lib
+
+
+def default_threads() -> int:
+    env = os.environ.get("NVFP4MOE_ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
+
+
+def threads() -> int:
+    return int(lib().oracle_threads())
 
 
 def _p(a):
@@ -222,6 +254,27 @@ def moe_block(x, ids, w, gate_up, down, shared_gate_up=None, shared_down=None, r
     out = np.empty((M, H), dtype=np.float64)
     lib().oracle_moe_block(_p(x), M, H, I, E, k, _p(ids), _p(w), *[_p(a) for a in gu],
                            *[_p(a) for a in dn], *sh, _p(res), _p(out))
+    del keep
+    return out
+
+
+def moe_block_f64(x, ids, w, gate_up, down, shared_gate_up=None, shared_down=None,
+                  residual=None):
+    """moe_block with x [M][H] and residual given as float64 values (the
+    float64 chain of a layer stack)."""
+    x = _c(x, np.float64)
+    ids, w = _c(ids, np.int32), _c(w, np.float64)
+    M, H = x.shape
+    k = ids.shape[1]
+    E = gate_up.codes.shape[0]
+    I = down.codes.shape[-1] * 2
+    gu = [_c(gate_up.codes, np.uint8), _c(gate_up.scales, np.uint8), _c(gate_up.g, np.float32)]
+    dn = [_c(down.codes, np.uint8), _c(down.scales, np.uint8), _c(down.g, np.float32)]
+    sh, keep = _shared_ptrs(shared_gate_up, shared_down)
+    res = _c(residual, np.float64)
+    out = np.empty((M, H), dtype=np.float64)
+    lib().oracle_moe_block_f64(_p(x), M, H, I, E, k, _p(ids), _p(w), *[_p(a) for a in gu],
+                               *[_p(a) for a in dn], *sh, _p(res), _p(out))
     del keep
     return out
 

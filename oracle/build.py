@@ -10,7 +10,7 @@ def build(verbose: bool = False) -> str:
     # -ffp-contract=off: every product and sum rounds on its own, as written
     cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra",
            "-ffp-contract=off", "-fno-fast-math",
-           os.path.join(HERE, "oracle.cpp"), "-o", LIB + ".tmp"]
+           "-pthread", os.path.join(HERE, "oracle.cpp"), "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -9,10 +9,47 @@
 #include "oracle.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <limits>
+#include <thread>
 #include <vector>
+
+/* ---- threads ------------------------------------------------------------------
+ * The products and the MoE block split their outputs into independent jobs
+ * (rows of W, or an expert's (row, slot) pairs) over a few threads. A job
+ * writes only its own outputs and computes every one of them exactly as the
+ * single-threaded loop does, so the result is bit-identical for any count. */
+static std::atomic<int> g_threads{1};
+
+void oracle_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
+int oracle_threads(void) { return g_threads; }
+
+/* Threads that parallel_jobs uses for njobs jobs. */
+static int64_t job_workers(int64_t njobs) {
+  return std::max<int64_t>(1, std::min<int64_t>(g_threads, njobs));
+}
+
+/* fn(job, worker) for job in [0, njobs), jobs handed out one at a time to
+ * job_workers(njobs) threads; worker in [0, job_workers(njobs)) names the
+ * thread, for state a thread keeps between its jobs. */
+template <class F>
+static void parallel_jobs(int64_t njobs, F fn) {
+  const int64_t nt = job_workers(njobs);
+  if (nt <= 1) {
+    for (int64_t j = 0; j < njobs; ++j) fn(j, 0);
+    return;
+  }
+  std::atomic<int64_t> next{0};
+  auto worker = [&](int64_t t) {
+    for (int64_t j = next++; j < njobs; j = next++) fn(j, t);
+  };
+  std::vector<std::thread> pool;
+  for (int64_t t = 1; t < nt; ++t) pool.emplace_back(worker, t);
+  worker(0);
+  for (auto& th : pool) th.join();
+}
 
 /* ---- NVFP4 element and scale decoding ------------------------------------- */
 
@@ -72,15 +109,19 @@ static inline uint32_t scale_at(const uint8_t* scales, int64_t N, int64_t K, int
   return scales[(gi * N + n) * (K / 16) + k / 16];
 }
 
-/* W[n][k] = e2m1(code) * e4m3(scale of the 16-block holding k) * g. */
+/* Row n of matrix gi: W[n][k] = e2m1(code) * e4m3(scale of the 16-block
+ * holding k) * g, for k = 0 .. K-1. */
+static void dequant_row(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t N,
+                        int64_t K, int64_t gi, int64_t n, double* row) {
+  for (int64_t k = 0; k < K; ++k)
+    row[k] = oracle_e2m1(code_at(codes, N, K, gi, n, k)) *
+             oracle_e4m3(scale_at(scales, N, K, gi, n, k)) * (double)g[gi];
+}
+
 void oracle_dequant(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t G,
                     int64_t N, int64_t K, double* out) {
   for (int64_t gi = 0; gi < G; ++gi)
-    for (int64_t n = 0; n < N; ++n)
-      for (int64_t k = 0; k < K; ++k)
-        out[(gi * N + n) * K + k] = oracle_e2m1(code_at(codes, N, K, gi, n, k)) *
-                                    oracle_e4m3(scale_at(scales, N, K, gi, n, k)) *
-                                    (double)g[gi];
+    for (int64_t n = 0; n < N; ++n) dequant_row(codes, scales, g, N, K, gi, n, &out[(gi * N + n) * K]);
 }
 
 void oracle_dequant_f32(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t G,
@@ -96,30 +137,42 @@ void oracle_dequant_f32(const uint8_t* codes, const uint8_t* scales, const float
 
 /* ---- skinny product --------------------------------------------------------- */
 
-/* y[m][n] = sum over k ascending of x[m][k] * W[n][k], in double. */
+/* Rows of W per job in the threaded products. */
+static const int64_t kRowsPerJob = 64;
+
+/* y[m][n] = sum over k ascending of x[m][k] * W[n][k], in double. A job takes
+ * kRowsPerJob rows of W: each row is decoded once, then multiplied with every
+ * row of x. */
 void oracle_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* codes,
                  const uint8_t* scales, float g, int64_t N, double* y) {
-  std::vector<double> W((size_t)(N * K));
-  oracle_dequant(codes, scales, &g, 1, N, K, W.data());
-  for (int64_t m = 0; m < M; ++m)
-    for (int64_t n = 0; n < N; ++n) {
-      double acc = 0.0;
-      for (int64_t k = 0; k < K; ++k) acc += oracle_bf16(x[m * K + k]) * W[(size_t)(n * K + k)];
-      y[m * N + n] = acc;
+  std::vector<double> xd((size_t)(M * K));
+  for (int64_t i = 0; i < M * K; ++i) xd[(size_t)i] = oracle_bf16(x[i]);
+  parallel_jobs((N + kRowsPerJob - 1) / kRowsPerJob, [&](int64_t job, int64_t) {
+    std::vector<double> W((size_t)K);
+    for (int64_t n = job * kRowsPerJob; n < std::min(N, (job + 1) * kRowsPerJob); ++n) {
+      dequant_row(codes, scales, &g, N, K, 0, n, W.data());
+      for (int64_t m = 0; m < M; ++m) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) acc += xd[(size_t)(m * K + k)] * W[(size_t)k];
+        y[m * N + n] = acc;
+      }
     }
+  });
 }
 
 /* y[m][n] = (sum_k x[m][k] * e4m3(w[n][k])) * s, float64: the FP8 skinny product
  * with one scale per tensor (Elsa page, "An FP8 fast path"). */
 void oracle_gemm_fp8(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w, double s,
                      int64_t N, double* y) {
-  for (int64_t m = 0; m < M; ++m)
-    for (int64_t n = 0; n < N; ++n) {
-      double acc = 0.0;
-      for (int64_t k = 0; k < K; ++k)
-        acc += oracle_bf16(x[m * K + k]) * oracle_e4m3(w[n * K + k]);
-      y[m * N + n] = acc * s;
-    }
+  parallel_jobs((N + kRowsPerJob - 1) / kRowsPerJob, [&](int64_t job, int64_t) {
+    for (int64_t n = job * kRowsPerJob; n < std::min(N, (job + 1) * kRowsPerJob); ++n)
+      for (int64_t m = 0; m < M; ++m) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+          acc += oracle_bf16(x[m * K + k]) * oracle_e4m3(w[n * K + k]);
+        y[m * N + n] = acc * s;
+      }
+  });
 }
 
 /* logits[m][e] = sum_h x[m][h] * w_r[e][h] in float64: the router projection in
@@ -127,12 +180,13 @@ void oracle_gemm_fp8(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w, 
  * and the model"). x and w_r are BF16 bit patterns; w_r is [E][H]. */
 void oracle_router_logits(const uint16_t* x, int64_t M, int64_t H, const uint16_t* w_r, int64_t E,
                           double* logits) {
-  for (int64_t m = 0; m < M; ++m)
+  parallel_jobs(M, [&](int64_t m, int64_t) {
     for (int64_t e = 0; e < E; ++e) {
       double acc = 0.0;
       for (int64_t h = 0; h < H; ++h) acc += oracle_bf16(x[m * H + h]) * oracle_bf16(w_r[e * H + h]);
       logits[m * E + e] = acc;
     }
+  });
 }
 
 /* ---- quantization: BF16 -> canonical NVFP4 ----------------------------------------
@@ -306,41 +360,68 @@ void oracle_expert_ffn(const uint16_t* x, int64_t H, int64_t I, const uint8_t* g
 
 /* ---- MoE block ------------------------------------------------------------------- */
 
-void oracle_moe_block(const uint16_t* x, int64_t M, int64_t H, int64_t I, int64_t E, int64_t k,
-                      const int32_t* ids, const double* w, const uint8_t* gu_codes,
-                      const uint8_t* gu_scales, const float* gu_g, const uint8_t* dn_codes,
-                      const uint8_t* dn_scales, const float* dn_g, const uint8_t* sgu_codes,
-                      const uint8_t* sgu_scales, const float* sgu_g, const uint8_t* sdn_codes,
-                      const uint8_t* sdn_scales, const float* sdn_g, const uint16_t* residual,
-                      double* out) {
+/* The (row, slot) pairs of one expert, or shared-expert rows, per job. */
+static const int64_t kPairsPerJob = 8;
+
+struct FfnJob {
+  int64_t e;      /* expert (-1: the shared expert) */
+  int64_t first;  /* index into the expert's pair list (or the first row) */
+  int64_t count;
+};
+
+void oracle_moe_block_f64(const double* x, int64_t M, int64_t H, int64_t I, int64_t E, int64_t k,
+                          const int32_t* ids, const double* w, const uint8_t* gu_codes,
+                          const uint8_t* gu_scales, const float* gu_g, const uint8_t* dn_codes,
+                          const uint8_t* dn_scales, const float* dn_g, const uint8_t* sgu_codes,
+                          const uint8_t* sgu_scales, const float* sgu_g, const uint8_t* sdn_codes,
+                          const uint8_t* sdn_scales, const float* sdn_g, const double* residual,
+                          double* out) {
   const int64_t P = M * k;
-  std::vector<double> xd((size_t)(M * H));
-  for (int64_t i = 0; i < M * H; ++i) xd[(size_t)i] = oracle_bf16(x[i]);
-  /* y_p for every (row, slot) pair p = m*k + j, through expert ids[p]. Each
-   * expert is dequantized once and applied to all of its pairs. */
-  std::vector<double> Y((size_t)(P * H));
-  std::vector<double> Wgu((size_t)(2 * I * H)), Wdn((size_t)(H * I));
-  for (int64_t e = 0; e < E; ++e) {
-    bool used = false;
-    for (int64_t p = 0; p < P && !used; ++p) used = (ids[p] == e);
-    if (!used) continue;
-    oracle_dequant(gu_codes + e * (2 * I * H / 2), gu_scales + e * (2 * I * H / 16), gu_g + e, 1,
-                   2 * I, H, Wgu.data());
-    oracle_dequant(dn_codes + e * (H * I / 2), dn_scales + e * (H * I / 16), dn_g + e, 1, H, I,
-                   Wdn.data());
-    for (int64_t p = 0; p < P; ++p)
-      if (ids[p] == e)
-        ffn_dequantized(&xd[(size_t)((p / k) * H)], H, I, Wgu.data(), Wdn.data(),
-                        &Y[(size_t)(p * H)]);
-  }
-  std::vector<double> S;
-  if (sgu_codes) {
-    S.resize((size_t)(M * H));
-    oracle_dequant(sgu_codes, sgu_scales, sgu_g, 1, 2 * I, H, Wgu.data());
-    oracle_dequant(sdn_codes, sdn_scales, sdn_g, 1, H, I, Wdn.data());
-    for (int64_t m = 0; m < M; ++m)
-      ffn_dequantized(&xd[(size_t)(m * H)], H, I, Wgu.data(), Wdn.data(), &S[(size_t)(m * H)]);
-  }
+  /* y_p for every (row, slot) pair p = m*k + j, through expert ids[p], and
+   * the shared expert's output for every row. Each job dequantizes its expert
+   * (a thread keeps the last one it decoded) and applies it to its pairs. */
+  std::vector<std::vector<int64_t>> pairs_of((size_t)E);
+  for (int64_t p = 0; p < P; ++p) pairs_of[(size_t)ids[p]].push_back(p);
+  std::vector<FfnJob> jobs;
+  for (int64_t e = 0; e < E; ++e)
+    for (int64_t f = 0; f < (int64_t)pairs_of[(size_t)e].size(); f += kPairsPerJob)
+      jobs.push_back({e, f, std::min<int64_t>(kPairsPerJob, (int64_t)pairs_of[(size_t)e].size() - f)});
+  if (sgu_codes)
+    for (int64_t r = 0; r < M; r += kPairsPerJob)
+      jobs.push_back({-1, r, std::min<int64_t>(kPairsPerJob, M - r)});
+  std::vector<double> Y((size_t)(P * H)), S(sgu_codes ? (size_t)(M * H) : 0);
+  struct Held {  /* a thread's decoded expert, kept between its jobs */
+    std::vector<double> Wgu, Wdn;
+    int64_t e = -2;
+  };
+  std::vector<Held> held((size_t)job_workers((int64_t)jobs.size()));
+  parallel_jobs((int64_t)jobs.size(), [&](int64_t jn, int64_t worker) {
+    const FfnJob& J = jobs[(size_t)jn];
+    std::vector<double>& Wgu = held[(size_t)worker].Wgu;
+    std::vector<double>& Wdn = held[(size_t)worker].Wdn;
+    if (held[(size_t)worker].e != J.e) {
+      Wgu.resize((size_t)(2 * I * H));
+      Wdn.resize((size_t)(H * I));
+      if (J.e < 0) {
+        oracle_dequant(sgu_codes, sgu_scales, sgu_g, 1, 2 * I, H, Wgu.data());
+        oracle_dequant(sdn_codes, sdn_scales, sdn_g, 1, H, I, Wdn.data());
+      } else {
+        oracle_dequant(gu_codes + J.e * (2 * I * H / 2), gu_scales + J.e * (2 * I * H / 16),
+                       gu_g + J.e, 1, 2 * I, H, Wgu.data());
+        oracle_dequant(dn_codes + J.e * (H * I / 2), dn_scales + J.e * (H * I / 16), dn_g + J.e,
+                       1, H, I, Wdn.data());
+      }
+      held[(size_t)worker].e = J.e;
+    }
+    for (int64_t q = J.first; q < J.first + J.count; ++q) {
+      if (J.e < 0) {
+        ffn_dequantized(&x[q * H], H, I, Wgu.data(), Wdn.data(), &S[(size_t)(q * H)]);
+      } else {
+        const int64_t p = pairs_of[(size_t)J.e][(size_t)q];
+        ffn_dequantized(&x[(p / k) * H], H, I, Wgu.data(), Wdn.data(), &Y[(size_t)(p * H)]);
+      }
+    }
+  });
   /* combine: routing-weighted sum over the k slots in slot order, then the
    * shared expert with weight 1, then the residual */
   for (int64_t m = 0; m < M; ++m)
@@ -349,9 +430,26 @@ void oracle_moe_block(const uint16_t* x, int64_t M, int64_t H, int64_t I, int64_
       for (int64_t j = 0; j < k; ++j)
         acc += w[m * k + j] * Y[(size_t)((m * k + j) * H + n)];
       if (sgu_codes) acc += S[(size_t)(m * H + n)];
-      if (residual) acc += oracle_bf16(residual[m * H + n]);
+      if (residual) acc += residual[m * H + n];
       out[m * H + n] = acc;
     }
+}
+
+void oracle_moe_block(const uint16_t* x, int64_t M, int64_t H, int64_t I, int64_t E, int64_t k,
+                      const int32_t* ids, const double* w, const uint8_t* gu_codes,
+                      const uint8_t* gu_scales, const float* gu_g, const uint8_t* dn_codes,
+                      const uint8_t* dn_scales, const float* dn_g, const uint8_t* sgu_codes,
+                      const uint8_t* sgu_scales, const float* sgu_g, const uint8_t* sdn_codes,
+                      const uint8_t* sdn_scales, const float* sdn_g, const uint16_t* residual,
+                      double* out) {
+  /* BF16 -> double is exact, so this is the float64 block on the same values */
+  std::vector<double> xd((size_t)(M * H)), rd(residual ? (size_t)(M * H) : 0);
+  for (int64_t i = 0; i < M * H; ++i) xd[(size_t)i] = oracle_bf16(x[i]);
+  if (residual)
+    for (int64_t i = 0; i < M * H; ++i) rd[(size_t)i] = oracle_bf16(residual[i]);
+  oracle_moe_block_f64(xd.data(), M, H, I, E, k, ids, w, gu_codes, gu_scales, gu_g, dn_codes,
+                       dn_scales, dn_g, sgu_codes, sgu_scales, sgu_g, sdn_codes, sdn_scales, sdn_g,
+                       residual ? rd.data() : nullptr, out);
 }
 
 int oracle_moe_decode(const uint16_t* x, const float* logits, const float* bias, int64_t M,

@@ -41,6 +41,12 @@
 extern "C" {
 #endif
 
+/* Threads the products and the MoE block split their outputs over (default
+ * 1). The result is bit-identical for every count: each output is computed
+ * by one thread exactly as the single-threaded loop computes it. */
+void oracle_set_threads(int n);
+int oracle_threads(void);
+
 double oracle_e2m1(uint32_t code);       /* code & 15 -> value */
 double oracle_e4m3(uint32_t byte);       /* byte & 255 -> value, NaN for 0x7F / 0xFF */
 double oracle_bf16(uint16_t bits);       /* exact widening */
@@ -105,6 +111,17 @@ void oracle_moe_block(const uint16_t* x, int64_t M, int64_t H, int64_t I, int64_
                       const uint8_t* sgu_scales, const float* sgu_g, const uint8_t* sdn_codes,
                       const uint8_t* sdn_scales, const float* sdn_g, const uint16_t* residual,
                       double* out);
+
+/* oracle_moe_block with the activation rows and the residual given in double
+ * (any values, not only BF16 ones): the float64 chain of a layer stack runs
+ * on its own unrounded output. residual may be NULL. */
+void oracle_moe_block_f64(const double* x, int64_t M, int64_t H, int64_t I, int64_t E, int64_t k,
+                          const int32_t* ids, const double* w, const uint8_t* gu_codes,
+                          const uint8_t* gu_scales, const float* gu_g, const uint8_t* dn_codes,
+                          const uint8_t* dn_scales, const float* dn_g, const uint8_t* sgu_codes,
+                          const uint8_t* sgu_scales, const float* sgu_g, const uint8_t* sdn_codes,
+                          const uint8_t* sdn_scales, const float* sdn_g, const double* residual,
+                          double* out);
 
 /* The whole decode step from router logits: route, group, expert FFNs,
  * combine. ids/w/out are outputs (ids [M][k], w [M][k], out [M][H]). */

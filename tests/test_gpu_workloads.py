@@ -1,8 +1,8 @@
 """GPU parity on the five workloads at full size, against the oracle.
 
 Routing is compared bit for bit on every row. Outputs are compared under
-|gpu - ref| <= 1e-2 |ref| + 1e-3 on every element where the oracle finishes in
-seconds, otherwise on sampled rows (the oracle computes a row on its own).
+|gpu - ref| <= 1e-2 |ref| + 1e-3 on every element (the oracle splits its
+outputs over the host's threads).
 """
 import numpy as np
 import pytest
@@ -31,18 +31,16 @@ def test_dense_single_matrix(m, gpu):
     assert tol_ratio(dev_bf16_to_f64(y), ref) <= 1.0
 
 
-@pytest.mark.parametrize("M,N", [(6, 32768), (3, 32773), (1, 248000)])
-def test_draft_head_sampled(m, gpu, M, N):
-    """Large-N skinny GEMM (draft head and full head shapes): every output of
-    a sample of rows of W (spread over the matrix, plus the first and last,
-    including the ragged last tile) against the oracle on those rows."""
+@pytest.mark.parametrize("M,N", [(6, 32768), (3, 32773), (6, 248000), (1, 248000)])
+def test_draft_head(m, gpu, M, N):
+    """Large-N skinny GEMM (draft head and full head shapes, the ragged last
+    tile included): every output against the oracle."""
     x, w = W.draft_head(seed=1, M=M, N=N)
     pw = pack(w, gpu, m)
     y = dev_bf16_to_f64(m.nvfp4_skinny_gemm(to_dev_bf16(x, gpu), pw))
     torch.cuda.synchronize()
-    cols = np.unique(np.concatenate([np.arange(0, N, 97), np.arange(N - 16, N), np.arange(16)]))
-    ref = oracle.gemm(x, w.codes[0][cols], w.scales[0][cols], float(w.g[0]))
-    assert tol_ratio(y[:, cols], ref) <= 1.0
+    ref = oracle.gemm(x, w.codes[0], w.scales[0], float(w.g[0]))
+    assert tol_ratio(y, ref) <= 1.0
 
 
 def _block(m, gpu, lay):
@@ -98,39 +96,43 @@ def test_prefill_m256_zipf(m, gpu):
     g = check_routing_exact(r, ids, w, lay.E)
     counts = g["counts"]
     assert counts.max() > 100  # Zipf(1.1) over 256 experts: a few experts take most rows
-    rows = np.arange(0, lay.M, 17)
-    ref = oracle.moe_block_touched(lay, ids, w, rows=rows)
-    assert tol_ratio(out[rows], ref) <= 1.0
+    ref = oracle.moe_block_touched(lay, ids, w)
+    assert tol_ratio(out, ref) <= 1.0
 
 
 def test_decode_max_rows_zipf(m, gpu):
     """The largest row count the routing launch takes (M = 1024) through the
-    default schedule: routing bit-exact on every row, outputs on sampled rows
-    (every 97th and the last)."""
+    default schedule: routing bit-exact and outputs on every row."""
     lay = W.moe_layer(0, wl=5, layer=7, M=1024, zipf_s=1.1)
     r, out = _block(m, gpu, lay)
     ids, w = oracle.route_topk(lay.logits, lay.k)
     check_routing_exact(r, ids, w, lay.E)
-    rows = np.unique(np.append(np.arange(0, lay.M, 97), lay.M - 1))
-    ref = oracle.moe_block_touched(lay, ids, w, rows=rows)
-    assert tol_ratio(out[rows], ref) <= 1.0
+    ref = oracle.moe_block_touched(lay, ids, w)
+    assert tol_ratio(out, ref) <= 1.0
 
 
-@pytest.mark.parametrize("check_layers", [(0, 1, 20, 39)])
 @pytest.mark.parametrize("router,entry", [(False, "decode"), (True, "decode"),
                                           (False, "route_decode")])
-def test_stack_40_layers_teacher_forced(m, gpu, check_layers, router, entry):
+def test_stack_40_layers_teacher_forced(m, gpu, router, entry):
     """40 MoE blocks (routed + shared expert + residual) and a dense 2048->64
-    projection per layer, run as a chain on the GPU. Checked layers are
-    recomputed by the oracle from the GPU's own BF16 input of that layer.
+    projection per layer, run as a chain on the GPU. Every layer is recomputed
+    by the oracle from the GPU's own BF16 input of that layer (teacher
+    forcing): x_{l+1}, the block's output without the residual, and the
+    projection, every element.
     router=True: the logits come from each layer's own BF16 router matrix
     applied to that layer's input on the GPU (routing follows the chain);
     they are held to the tolerance, and the oracle routes the GPU's logits.
     entry="route_decode": each layer is one moe_nvfp4_route_decode call
-    (routing folded in, residual), as the 40-layer bench runs it."""
+    (routing folded in, residual, the projection in its down launch), as the
+    40-layer bench runs it; this variant also runs the oracle's free-running
+    float64 chain (never rounded to BF16) beside it and reports the end-to-end
+    drift of the GPU's chain from it (informative, not gated)."""
     x_host = W.stack_x0()
     x = to_dev_bf16(x_host, gpu)
     worst = 0.0
+    free = entry == "route_decode" and not router
+    xf64 = dev_bf16_to_f64(x)
+    drift = []
     for l in range(W.STACK_LAYERS):
         lay = W.stack_layer(l, x=x_host)
         d = upload_layer(lay, gpu, m)
@@ -143,43 +145,51 @@ def test_stack_40_layers_teacher_forced(m, gpu, check_layers, router, entry):
         proj = m.nvfp4_skinny_gemm(x, pw)
         if entry == "decode":
             x_next = m.moe_nvfp4_decode(x, r, d["gu"], d["dn"], d["sgu"], d["sdn"], residual=x)
+            blk = m.moe_nvfp4_decode(x, r, d["gu"], d["dn"], d["sgu"], d["sdn"])
         else:
             # the projection computed inside the call: bit-identical to its own launch
             proj_in = torch.empty_like(proj)
             x_next, ids_d, w_d = m.moe_nvfp4_route_decode(x, d["logits"], lay.k, d["gu"], d["dn"],
                                                           None, d["sgu"], d["sdn"], residual=x,
                                                           proj=pw, proj_out=proj_in)
+            blk = m.moe_nvfp4_route_decode(x, d["logits"], lay.k, d["gu"], d["dn"], None,
+                                           d["sgu"], d["sdn"])[0]
             torch.cuda.synchronize()
             assert torch.equal(proj_in.view(torch.int16), proj.view(torch.int16))
         torch.cuda.synchronize()
-        if l in check_layers:
-            if router:
-                lg = logits.cpu().numpy()
-                worst = max(worst, tol_ratio(lg.astype(np.float64), oracle.router_logits(x_host, wr)))
-                ids, w = oracle.route_topk(lg, lay.k)
-            else:
-                ids, w = oracle.route_topk(lay.logits, lay.k)
-            if entry == "decode":
-                check_routing_exact(r, ids, w, lay.E)
-            else:
-                assert (ids_d.cpu().numpy() == ids).all()
-                assert np.max(np.abs(w_d.cpu().numpy().astype(np.float64) - w)) <= 1e-6
-            ref = oracle.moe_block_touched(lay, ids, w, residual=x_host)
-            worst = max(worst, tol_ratio(dev_bf16_to_f64(x_next), ref))
-            # the block's own output, without the residual that dominates x_next
-            if entry == "decode":
-                blk = m.moe_nvfp4_decode(x, r, d["gu"], d["dn"], d["sgu"], d["sdn"])
-            else:
-                blk = m.moe_nvfp4_route_decode(x, d["logits"], lay.k, d["gu"], d["dn"], None,
-                                               d["sgu"], d["sdn"])[0]
-            torch.cuda.synchronize()
-            worst = max(worst, tol_ratio(dev_bf16_to_f64(blk), oracle.moe_block_touched(lay, ids, w)))
-            p = lay.extra["proj"]
-            pref = oracle.gemm(x_host, p.codes[0], p.scales[0], float(p.g[0]))
-            worst = max(worst, tol_ratio(dev_bf16_to_f64(proj), pref))
+        if router:
+            lg = logits.cpu().numpy()
+            worst = max(worst, tol_ratio(lg.astype(np.float64), oracle.router_logits(x_host, wr)))
+            ids, w = oracle.route_topk(lg, lay.k)
+        else:
+            ids, w = oracle.route_topk(lay.logits, lay.k)
+        if entry == "decode":
+            check_routing_exact(r, ids, w, lay.E)
+        else:
+            assert (ids_d.cpu().numpy() == ids).all()
+            assert np.max(np.abs(w_d.cpu().numpy().astype(np.float64) - w)) <= 1e-6
+        ref = oracle.moe_block_touched(lay, ids, w, residual=x_host)
+        worst = max(worst, tol_ratio(dev_bf16_to_f64(x_next), ref))
+        # the block's own output, without the residual that dominates x_next
+        worst = max(worst, tol_ratio(dev_bf16_to_f64(blk), oracle.moe_block_touched(lay, ids, w)))
+        p = lay.extra["proj"]
+        pref = oracle.gemm(x_host, p.codes[0], p.scales[0], float(p.g[0]))
+        worst = max(worst, tol_ratio(dev_bf16_to_f64(proj), pref))
+        assert worst <= 1.0, l
         x = x_next
         x_host = x.cpu().view(torch.int16).numpy().view(np.uint16)
+        if free:  # the float64 chain on its own unrounded values
+            xf64 = oracle.moe_block_f64(xf64, ids, w, lay.gate_up, lay.down, lay.shared_gate_up,
+                                        lay.shared_down, residual=xf64)
+            xg = dev_bf16_to_f64(x)
+            drift.append((l, float(np.sqrt(np.mean((xg - xf64) ** 2) / np.mean(xf64 ** 2))),
+                          float(np.max(np.abs(xg - xf64)))))
         del d, pw
     xf = dev_bf16_to_f64(x)
     assert np.isfinite(xf).all() and np.sqrt((xf ** 2).mean()) < 2.0
-    assert worst <= 1.0
+    if free:
+        print("\nfree-running float64 chain vs the GPU's BF16 chain (layer, relative rms, max abs):")
+        for l, rel, mx in drift:
+            if l in (0, 1, 4, 9, 19, 29, 39):
+                print(f"  layer {l:2d}: relative rms {rel:.3e}, max abs {mx:.3e}")
+        assert np.isfinite([d[1] for d in drift]).all()

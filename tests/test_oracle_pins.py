@@ -632,3 +632,58 @@ def test_moe_block_touched_subset_equals_full():
     assert (full == sub).all()
     rows = oracle.moe_block_touched(lay, ids, w, rows=[1, 3])
     assert (rows == full[[1, 3]]).all()
+
+
+@pytest.mark.parametrize("threads", [2, 3, 8])
+def test_threaded_oracle_is_bit_identical(threads):
+    """The thread split changes nothing: every output of the products and of
+    the MoE block (experts with more pairs than one job takes, a shared
+    expert over more rows than one job takes, a residual) equals the
+    single-threaded result bit for bit."""
+    lay = moe_layer(seed=10, wl=93, M=37, E_=12, H_=256, I_=64, k=3, shared=True)
+    ids, w = oracle.route_topk(lay.logits, lay.k)
+    res = synth.normal_bf16(synth.key(10, 94), (lay.M, lay.H))
+    rng = np.random.default_rng(3)
+    x = synth.normal_bf16(synth.key(10, 95), (5, 256))
+    wc = rng.integers(0, 256, (1, 300, 128), dtype=np.uint8)
+    ws = rng.integers(0x18, 0x58, (1, 300, 16), dtype=np.uint8)
+    w8 = rng.integers(0, 0x7F, (300, 256), dtype=np.uint8)
+    wr = synth.normal_bf16(synth.key(10, 96), (40, 256))
+
+    def run():
+        return [oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down, lay.shared_gate_up,
+                                 lay.shared_down, res),
+                oracle.gemm(x, wc[0], ws[0], 0.37), oracle.gemm_fp8(x, w8, 0.5),
+                oracle.router_logits(x, wr)]
+
+    saved = oracle.threads()
+    try:
+        oracle.set_threads(1)
+        one = run()
+        oracle.set_threads(threads)
+        assert oracle.threads() == threads
+        many = run()
+    finally:
+        oracle.set_threads(saved)
+    for a, b in zip(one, many):
+        assert a.view(np.uint64).tobytes() == b.view(np.uint64).tobytes()
+
+
+def test_moe_block_f64_on_bf16_values_equals_moe_block():
+    """The float64-input block is the same computation: on BF16-valued rows and
+    residual it gives moe_block's result bit for bit, and its rows stay
+    independent for values off the BF16 grid."""
+    lay = moe_layer(seed=11, wl=97, M=3, E_=8, H_=64, I_=32, k=2, shared=True)
+    ids, w = oracle.route_topk(lay.logits, lay.k)
+    res = synth.normal_bf16(synth.key(11, 98), (lay.M, lay.H))
+    a = oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down, lay.shared_gate_up,
+                         lay.shared_down, res)
+    b = oracle.moe_block_f64(bf16_to_f64(lay.x), ids, w, lay.gate_up, lay.down,
+                             lay.shared_gate_up, lay.shared_down, bf16_to_f64(res))
+    assert (a == b).all()
+    xf = bf16_to_f64(lay.x) * (1 + 2.0 ** -20)  # not representable in BF16
+    full = oracle.moe_block_f64(xf, ids, w, lay.gate_up, lay.down)
+    for m in range(lay.M):
+        one = oracle.moe_block_f64(xf[m:m + 1], ids[m:m + 1], w[m:m + 1], lay.gate_up,
+                                   lay.down)
+        assert (one[0] == full[m]).all()
