@@ -16,8 +16,19 @@ replayed; `value` is algorithmic bytes per step (touched expert codes + scales
 step time. The dominant call (moe_nvfp4_decode) is also timed on its own with
 HIP events on the stream it runs on, for the roofline entry.
 
+Every graph-timed workload runs at least one second of warm-up replays, then
+five runs of at least 200 steps each (more when --steps asks for more), with
+an event between runs; the line reports the median, mean and spread of the
+runs. After timing, one output set the timed replays wrote is checked against
+the float64 oracle: routing bit for bit, outputs within |gpu - ref| <=
+1e-2 |ref| + 1e-3; the worst ratio goes in the line (parity_max_ratio) and
+bench exits non-zero if it is above 1. The same byte count is read by the
+read-ceiling kernel (one pass of 16-byte loads and nothing else) in the same
+run, so the step is also reported against what a bare read of its bytes
+takes on this chip.
+
 The oracle (float64 C++ on the host) is timed on a bounded sample of the same
-steps as a reported CPU baseline.
+steps as a reported CPU baseline, single-threaded and with the host's threads.
 """
 import argparse
 import json
@@ -33,6 +44,153 @@ sys.path.insert(0, ROOT)
 METRIC = "NVFP4 MoE decode achieved HBM GB/s (% of peak) + token-rows/s at M=4"
 HBM_PEAK_GBS = 8000.0
 CPU_LAYERS = 12  # weight copies kept on the host for the CPU-baseline sample
+RTOL, ATOL = 1e-2, 1e-3  # the output tolerance against the float64 oracle
+MIN_RUNS, MIN_RUN_STEPS, MIN_WARM_S = 5, 200, 1.0
+
+
+# ---- host-side helpers (upload, compare) --------------------------------------------
+
+def to_dev_bf16(bits, dev):
+    """BF16 bit patterns (uint16 ndarray) -> torch bfloat16 on dev."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(dev)
+
+
+def pack(nv, dev, m):
+    """Canonical NVFP4 (codes, scales, g ndarrays) -> the library's packed layout on dev."""
+    import torch
+    codes = torch.from_numpy(np.ascontiguousarray(nv.codes)).to(dev)
+    scales = torch.from_numpy(np.ascontiguousarray(nv.scales)).to(dev)
+    g = torch.from_numpy(np.ascontiguousarray(nv.g, dtype=np.float32)).to(dev)
+    return m.nvfp4_pack(codes, scales, g)
+
+
+def dev_bf16_to_f64(t):
+    import torch
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def tol_ratio(got, ref):
+    """max |got - ref| / (RTOL |ref| + ATOL): <= 1 passes."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    if not np.isfinite(got).all():
+        return float("inf")
+    return float(np.max(np.abs(got - ref) / (RTOL * np.abs(ref) + ATOL)))
+
+
+def host_info():
+    """The machine the line was measured on: GPU, its compute units, the HIP
+    runtime and compiler, and the host CPU the oracle baseline ran on."""
+    import subprocess
+
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    info = {"gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+            "compute_units": props.multi_processor_count,
+            "hbm_bytes": props.total_memory, "torch": torch.__version__,
+            "hip_runtime": torch.version.hip}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            info["rocm"] = fh.read().strip()
+    except OSError:
+        pass
+    try:
+        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
+                             timeout=60).stdout.splitlines()
+        info["hipcc"] = "; ".join(l.strip() for l in out if "version" in l.lower())[:200]
+    except (OSError, subprocess.SubprocessError):
+        pass
+    info.update(cpu_info())
+    return info
+
+
+def cpu_info():
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "host_cpus_usable": usable}
+
+
+# ---- timing ----------------------------------------------------------------------------
+
+def capture(step, S):
+    """A HIP graph of step(0 .. S-1), captured on a side stream."""
+    import torch
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(S):
+                step(i)
+    torch.cuda.synchronize()
+    return graph
+
+
+def replay_timed(graph, S, want_steps, min_run_steps=MIN_RUN_STEPS):
+    """Warm-up replays for at least MIN_WARM_S seconds, then MIN_RUNS runs of
+    at least max(min_run_steps, want_steps / MIN_RUNS) steps each (whole
+    replays of the S-step graph), an event between runs. Returns (ms per
+    step over all runs, steps timed, per-run stats)."""
+    import torch
+    t0 = time.time()
+    warm = 0
+    while time.time() - t0 < MIN_WARM_S or warm < 2:
+        graph.replay()
+        warm += 1
+        if warm % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    per_run = max(min_run_steps, int(np.ceil(want_steps / MIN_RUNS)))
+    reps = max(1, int(np.ceil(per_run / S)))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(MIN_RUNS + 1)]
+    evs[0].record()
+    for r in range(MIN_RUNS):
+        for _ in range(reps):
+            graph.replay()
+        evs[r + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[r].elapsed_time(evs[r + 1]) / (reps * S) for r in range(MIN_RUNS)])
+    stats = {"n": MIN_RUNS, "steps_per_run": reps * S, "warmup_replays": warm,
+             "warmup_s": round(time.time() - t0, 2),
+             "median_ms_per_step": round(float(np.median(per)), 6),
+             "mean_ms_per_step": round(float(per.mean()), 6),
+             "std_ms_per_step": round(float(per.std(ddof=1)), 6)}
+    return evs[0].elapsed_time(evs[-1]) / (MIN_RUNS * reps * S), MIN_RUNS * reps * S, stats
+
+
+def read_ceiling(nbytes, m, want_steps=4000):
+    """Time of one bare read of nbytes (nvfp4moe_stream_read: the 16-byte
+    nontemporal loads the weight streams use, nothing computed), over
+    distinct buffers cycled through >= 2 GB so every pass reads HBM."""
+    import torch
+    nbytes = max(16, int(nbytes) // 16 * 16)
+    copies = max(2, int(np.ceil(2e9 / nbytes)))
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sinks = [torch.empty(m.nvfp4moe_stream_blocks(nbytes), dtype=torch.int32, device="cuda")
+             for _ in range(copies)]
+
+    def step(i):
+        m.nvfp4moe_stream_read(bufs[i % copies], sink=sinks[i % copies])
+
+    for i in range(copies):
+        step(i)
+    graph = capture(step, copies * int(np.ceil(16 / copies)))
+    ms, _, _ = replay_timed(graph, copies * int(np.ceil(16 / copies)),
+                            min(want_steps, 2000 if nbytes < 5e8 else 50),
+                            min_run_steps=min(MIN_RUN_STEPS, 20 if nbytes > 5e8 else 200))
+    del graph, bufs, sinks
+    torch.cuda.empty_cache()
+    return ms * 1e3
 
 
 # the device code of one moe_nvfp4_decode call (all of its launches)
@@ -50,11 +208,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
+def recorded_traffic(workload):
     """HBM bytes per decode call (its gate_up, down and combine launches) from
-    the committed FETCH_SIZE/WRITE_SIZE summary, or None once the kernels have
-    changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "moe_decode_m4_counters.md")
+    the committed FETCH_SIZE/WRITE_SIZE summary of this workload, or None if
+    there is none or the kernels have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_counters.md")
     try:
         fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
                       if line.startswith(("traffic_bytes_per_launch: ", "source_hash: ")))
@@ -97,9 +255,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20000)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--workload", default="m4", choices=["m4", "m16", "m256", "head32k", "head248k", "fp8qkv",
-                                             "fp8o", "router", "quant", "stack40",
-                                             "ceiling"])
+    p.add_argument("--workload", default="m4",
+                   choices=["m4", "m16", "m256", "dense", "head32k", "head248k", "fp8qkv",
+                            "fp8o", "router", "quant", "stack40", "ceiling"])
     p.add_argument("--rows", type=int, default=0, help="rows M of a skinny-GEMM workload")
     p.add_argument("--dense-min-rows", type=int, default=0,
                    help="rows from which a slot uses MFMA (0 = library default)")
@@ -109,7 +267,10 @@ def parse():
                    help="separate: moe_route_topk + moe_nvfp4_decode; fused: "
                         "moe_nvfp4_route_decode (few rows); auto: fused for M <= 8")
     p.add_argument("--copies", type=int, default=0, help="weight sets cycled (0: >= 1 GB)")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=8.0,
+                   help="oracle time budget per thread count (single-threaded, then all threads)")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the read-ceiling pass at the step's byte count")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager-calls", type=int, default=400, help=">= 2")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -141,6 +302,8 @@ def main():
         return calibrate_copy(args.calibrate_copy_mb)
     if args.workload.startswith("head"):
         return bench_head(args)
+    if args.workload == "dense":
+        return bench_dense(args)
     if args.workload.startswith("fp8"):
         return bench_fp8(args)
     if args.workload == "router":
@@ -155,7 +318,6 @@ def main():
 
     import nvfp4_moe_skinny_amd as m
     from synth import workloads as W
-    from tests.helpers import pack, to_dev_bf16
 
     dev = torch.device("cuda:0")
     zipf = None
@@ -232,37 +394,10 @@ def main():
     for i in range(max(args.warmup, S)):
         step(i)
     torch.cuda.synchronize()
-
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(graph, stream=cap):
-            for i in range(S):
-                step(i)
-    torch.cuda.synchronize()
-    for _ in range(2):
-        graph.replay()
-    torch.cuda.synchronize()
-
-    replays = max(1, args.steps // S)
-    steps = replays * S
-    # the timed replays in (up to) five consecutive runs, an event between runs
-    n_runs = min(5, replays)
-    bounds = [round(r * replays / n_runs) for r in range(n_runs + 1)]
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_runs + 1)]
-    torch.cuda.synchronize()
+    graph = capture(step, S)
     wall0 = time.time()
-    evs[0].record()
-    for r in range(n_runs):
-        for _ in range(bounds[r + 1] - bounds[r]):
-            graph.replay()
-        evs[r + 1].record()
-    torch.cuda.synchronize()
+    ms_per_step, steps, runs = replay_timed(graph, S, args.steps)
     wall = time.time() - wall0
-    gpu_ms = evs[0].elapsed_time(evs[-1])
-    ms_per_step = gpu_ms / steps
-    run_ms = np.array([evs[r].elapsed_time(evs[r + 1]) / ((bounds[r + 1] - bounds[r]) * S)
-                       for r in range(n_runs)])
 
     # bytes from each step's actual routing (read back after the timed region)
     n_act = np.array([len(np.unique(routes[j].ids.cpu().numpy())) for j in range(n_sets)])
@@ -271,6 +406,13 @@ def main():
     mean_bytes = float(np.mean([bytes_per_set[i % n_sets] for i in range(S)]))
     gbs = mean_bytes / (ms_per_step * 1e-3) / 1e9
     rows_per_s = M / (ms_per_step * 1e-3)
+
+    # parity of what the timed replays left in output set 0: the last step of
+    # the graph that wrote it used weight copy c
+    last = max(i for i in range(S) if i % n_sets == 0)
+    c = last % copies
+    lay_c = layers_host[c] if c < len(layers_host) else make(c)
+    parity = check_parity(lay_c, logit_sets[0], x_host[0], routes[0], outs[0], fused, M, E, k)
 
     # eager: each decode call timed with events on its own stream (roofline entry)
     stream = torch.cuda.current_stream()
@@ -309,8 +451,18 @@ def main():
         step(i)
     torch.cuda.synchronize()
     eager_ms = (time.time() - e0) * 1e3 / args.eager_calls
+    del graph
 
     outs_ok = all(torch.isfinite(o.float()).all().item() for o in outs)
+    ceiling = None
+    if not args.no_ceiling:
+        del weights
+        torch.cuda.empty_cache()
+        c_us = read_ceiling(mean_bytes, m)
+        ceiling = {"bytes": round(mean_bytes), "us": round(c_us, 3),
+                   "GB/s": round(mean_bytes / (c_us * 1e-6) / 1e9, 1),
+                   "step_frac_of_ceiling": round(c_us / (ms_per_step * 1e3), 4),
+                   "kernel": "nvfp4moe_stream_read, one launch, buffers cycled over >= 2 GB"}
 
     record = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
@@ -327,9 +479,7 @@ def main():
                            else "moe_route_topk + moe_nvfp4_decode"},
         "rows_per_s": round(rows_per_s, 1),
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-        "runs": {"n": n_runs, "median_ms_per_step": round(float(np.median(run_ms)), 6),
-                 "mean_ms_per_step": round(float(run_ms.mean()), 6),
-                 "std_ms_per_step": round(float(run_ms.std(ddof=1)) if n_runs > 1 else 0.0, 6)},
+        "runs": runs,
         "bytes_per_step": round(mean_bytes),
         "touched_experts_mean": float(np.mean(n_act)),
         "eager_ms_per_step": round(eager_ms, 4),
@@ -339,17 +489,21 @@ def main():
                                 else decode_kernels(args.schedule, M)),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic() if args.workload == "m4" else None,
+                     "traffic": recorded_traffic(f"moe_decode_{args.workload}"),
                      "avg_launch_us": round(dec_avg_ms * 1e3, 3),
                      "bytes_per_launch": round(dec_bytes),
                      "timing": ("the call's duration over the timed graph replays" if fused
                                 else "eager calls, events on the launching stream"),
                      "eager_call_us": round(eager_call_us, 3)},
+        "read_ceiling": ceiling,
+        "parity": parity, "parity_max_ratio": parity["max_ratio"],
         "outputs_finite": outs_ok, "setup_s": round(setup_s, 1), "wall_s": round(wall, 3),
+        "host": host_info(),
     }
-    if not outs_ok or gbs <= 0 or not np.isfinite(gbs):
+    failed = (not outs_ok or gbs <= 0 or not np.isfinite(gbs) or not parity["ok"])
+    if failed:
         print(json.dumps(record), flush=True)
-        print("bench: invalid result", file=sys.stderr)
+        print("bench: invalid result (parity or non-finite outputs)", file=sys.stderr)
         return 1
 
     if not args.no_cpu_baseline:
@@ -359,42 +513,44 @@ def main():
     return 0
 
 
-def time_graph(step, copies, args):
+def check_parity(lay, lset, x_host, route, out, fused, M, E, k):
+    """Routing and outputs of one timed step against the oracle: ids (and,
+    without the fused path, the grouping) bit for bit, weights within 1e-6,
+    outputs within the output tolerance."""
+    import oracle
+    ids, w = oracle.route_topk(lset.logits, k, lset.bias)
+    got_ids = route.ids.cpu().numpy()
+    ids_ok = bool((got_ids == ids).all())
+    w_err = float(np.max(np.abs(route.w.cpu().numpy().astype(np.float64) - w)))
+    group_ok = True
+    if not fused:
+        counts, offsets, pairs, active, active_offsets, na = oracle.group_by_expert(ids, E)
+        group_ok = bool((route.pairs.cpu().numpy() == pairs).all() and
+                        (route.active_offsets.cpu().numpy() == active_offsets).all() and
+                        int(route.n_active.cpu().numpy()[0]) == na)
+    lay_x = type(lay)(**{**lay.__dict__, "x": x_host, "M": M})
+    ref = oracle.moe_block_touched(lay_x, ids, w)
+    ratio = tol_ratio(dev_bf16_to_f64(out), ref)
+    ok = ids_ok and group_ok and w_err <= 1e-6 and ratio <= 1.0
+    return {"ok": ok, "max_ratio": round(ratio, 4), "ids_exact": ids_ok, "grouping_exact": group_ok,
+            "w_max_abs_err": w_err, "checked": "output set 0 as the timed replays left it",
+            "oracle_threads": oracle.threads()}
+
+
+def time_graph(step, copies, args, min_run_steps=MIN_RUN_STEPS):
     """Captures S = a multiple of copies (>= 16) calls step(0 .. S-1) in one
-    HIP graph and times its replays with events: (ms per call, calls timed)."""
+    HIP graph and times its replays (replay_timed): (ms per call, calls
+    timed); the runs' spread is kept for the JSON line (run_stats)."""
     import torch
     S = copies * int(np.ceil(16 / copies))
     for i in range(max(args.warmup, S)):
         step(i)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(graph, stream=cap):
-            for i in range(S):
-                step(i)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    replays = max(1, args.steps // S)
-    # (up to) five consecutive runs, an event between runs; the runs' spread
-    # is kept for the JSON line (run_stats)
-    n_runs = min(5, replays)
-    bounds = [round(r * replays / n_runs) for r in range(n_runs + 1)]
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_runs + 1)]
-    evs[0].record()
-    for r in range(n_runs):
-        for _ in range(bounds[r + 1] - bounds[r]):
-            graph.replay()
-        evs[r + 1].record()
-    torch.cuda.synchronize()
-    per = np.array([evs[r].elapsed_time(evs[r + 1]) / ((bounds[r + 1] - bounds[r]) * S)
-                    for r in range(n_runs)])
+    graph = capture(step, S)
+    ms, n, stats = replay_timed(graph, S, args.steps, min_run_steps)
     _RUNS.clear()
-    _RUNS.update({"n": n_runs, "median_ms_per_step": round(float(np.median(per)), 6),
-                  "mean_ms_per_step": round(float(per.mean()), 6),
-                  "std_ms_per_step": round(float(per.std(ddof=1)) if n_runs > 1 else 0.0, 6)})
-    return evs[0].elapsed_time(evs[-1]) / (replays * S), replays * S
+    _RUNS.update(stats)
+    return ms, n
 
 
 _RUNS = {}
@@ -415,7 +571,6 @@ def bench_fp8(args):
 
     import nvfp4_moe_skinny_amd as m
     from synth import workloads as W
-    from tests.helpers import to_dev_bf16
 
     dev = torch.device("cuda:0")
     K, N = (2048, 5120) if args.workload == "fp8qkv" else (4096, 2048)
@@ -433,6 +588,8 @@ def bench_fp8(args):
         m.fp8_skinny_gemm(xd, ws[i % copies], sc, out=outs[i % copies])
 
     ms, n_steps = time_graph(step, copies, args)
+    import oracle
+    ratio = tol_ratio(dev_bf16_to_f64(outs[0]), oracle.gemm_fp8(x, w, s))
     step_bytes = w.nbytes + 4 + M * K * 2 + M * N * 2
     gbs = step_bytes / (ms * 1e-3) / 1e9
     print(json.dumps({
@@ -444,9 +601,9 @@ def bench_fp8(args):
                    "weights": "fp8 e4m3 + one f32 tensor scale", "weight_copies": copies,
                    "timing": "hip graph replay, events"},
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes,
-        "runs": run_stats(),
+        "runs": run_stats(), "parity_max_ratio": round(ratio, 4),
     }), flush=True)
-    return 0
+    return 0 if ratio <= 1.0 else 1
 
 
 def bench_router(args):
@@ -457,7 +614,6 @@ def bench_router(args):
 
     import nvfp4_moe_skinny_amd as m
     from synth import workloads as W
-    from tests.helpers import to_dev_bf16
 
     dev = torch.device("cuda:0")
     M, E, H, k = args.rows or 4, 256, 2048, 8
@@ -496,7 +652,6 @@ def bench_quant(args):
 
     import nvfp4_moe_skinny_amd as m
     from synth import workloads as W
-    from tests.helpers import to_dev_bf16
 
     dev = torch.device("cuda:0")
     G, N, K = 256, 1024, 2048
@@ -541,6 +696,100 @@ def bench_quant(args):
     return 0
 
 
+def bench_dense(args):
+    """The single dense NVFP4 matrix: M = 1 BF16 row ~N(0,1) times W [512][2048]
+    (uniform codes, E4M3 scales 2^U[-4,4), g = 1.0), 594,948 bytes a call.
+    Calls cycle through >= 2048 distinct seeded matrices (1.2 GB, copy 0 is
+    the canonical seed-0 matrix) so that each reads HBM, not the last-level
+    cache. value = the amortised rate of the calls in a graph; beside it the
+    single-launch latency (each call alone between two events, eager). One
+    such call is latency-bound by construction: its bytes stream in ~74 ns at
+    8 TB/s, far below a launch's own cost."""
+    import torch
+
+    import nvfp4_moe_skinny_amd as m
+    import oracle
+    from synth import workloads as W
+
+    dev = torch.device("cuda:0")
+    M, K, N = 1, 2048, 512
+    copies = max(args.copies or 2048, 16)
+    t0 = time.time()
+    ws, xs, host = [], [], []
+    for c in range(copies):
+        x, w = W.dense_skinny(seed=0, layer=c)
+        ws.append(pack(w, dev, m))
+        xs.append(to_dev_bf16(x, dev))
+        if c < 64:
+            host.append((x, w))
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    def step(i):
+        m.nvfp4_skinny_gemm(xs[i % copies], ws[i % copies], out=outs[i % copies])
+
+    ms, n_steps = time_graph(step, copies, args)
+    runs = run_stats()
+    # what the timed replays left in output 0 (written by copy 0's calls)
+    x0, w0 = host[0]
+    ratio = tol_ratio(dev_bf16_to_f64(outs[0]), oracle.gemm(x0, w0.codes[0], w0.scales[0],
+                                                            float(w0.g[0])))
+    # single launches: each call alone between two events on its stream
+    stream = torch.cuda.current_stream()
+    n_eager = max(args.eager_calls, 64)
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(n_eager)]
+    en = [torch.cuda.Event(enable_timing=True) for _ in range(n_eager)]
+    for i in range(n_eager):
+        st[i].record(stream)
+        step(i)
+        en[i].record(stream)
+        stream.synchronize()  # nothing queued behind: the call's own latency
+    lat = np.array([a.elapsed_time(b) for a, b in zip(st, en)])[8:] * 1e3
+    w_bytes = N * K // 2 + N * K // 16 + 4
+    step_b = w_bytes + M * K * 2 + M * N * 2
+    gbs = step_b / (ms * 1e-3) / 1e9
+    ceiling_us = None if args.no_ceiling else read_ceiling(step_b, m)
+    record = {
+        "metric": "NVFP4 dense skinny GEMM achieved HBM GB/s (single 2048->512 matrix, M=1)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": n_steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "nvfp4_skinny_gemm_m1_k2048_n512", "M": M, "K": K, "N": N,
+                   "g": 1.0, "distinct_matrices": copies,
+                   "timing": "hip graph replay, events (amortised over the calls)"},
+        "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_b,
+        "runs": runs,
+        "single_launch_us": {"median": round(float(np.median(lat)), 3),
+                             "mean": round(float(lat.mean()), 3),
+                             "min": round(float(lat.min()), 3), "calls": int(lat.size),
+                             "timing": "eager, each call alone between two events"},
+        "roofline": {"bound": "hbm", "kernel": "skinny_gemm_kernel<64> (one launch a call)",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(ms * 1e3, 4), "bytes_per_launch": step_b,
+                     "timing": "launches in a graph, amortised; latency-bound (74 ns of bytes)"},
+        "read_ceiling": None if ceiling_us is None else
+        {"bytes": step_b, "us": round(ceiling_us, 3),
+         "step_frac_of_ceiling": round(ceiling_us / (ms * 1e3), 4)},
+        "parity_max_ratio": round(ratio, 4), "setup_s": round(setup_s, 1),
+        "host": host_info(),
+    }
+    if not np.isfinite(gbs) or ratio > 1.0:
+        print(json.dumps(record), flush=True)
+        print("bench: invalid result (parity)", file=sys.stderr)
+        return 1
+    if not args.no_cpu_baseline:
+        def one(i):
+            x, w = host[i % len(host)]
+            oracle.gemm(x, w.codes[0], w.scales[0], float(w.g[0]))
+            return step_b
+        record["cpu_baseline"] = baseline_record(one, args.cpu_seconds, M,
+                                                 "2048->512 products (one row each)")
+    print(json.dumps(record), flush=True)
+    return 0
+
+
 def bench_head(args):
     """Large-N skinny GEMM: M = 6 rows times a [N][2048] NVFP4 head (N = 32768,
     the draft head; N = 248000, the full head). Not the headline line: a
@@ -549,7 +798,6 @@ def bench_head(args):
 
     import nvfp4_moe_skinny_amd as m
     from synth import workloads as W
-    from tests.helpers import pack, to_dev_bf16
 
     dev = torch.device("cuda:0")
     N = 32768 if args.workload == "head32k" else 248000
@@ -561,6 +809,8 @@ def bench_head(args):
         x, w = W.draft_head(seed=0, M=M, N=N, layer=c)
         ws.append(pack(w, dev, m))
         xs.append(to_dev_bf16(x, dev))
+        if c == 0:
+            x0, w0 = x, w
         torch.cuda.synchronize()
     outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
 
@@ -568,6 +818,9 @@ def bench_head(args):
         m.nvfp4_skinny_gemm(xs[i % copies], ws[i % copies], out=outs[i % copies])
 
     ms, n_steps = time_graph(step, copies, args)
+    import oracle  # what the timed replays left in output 0 (copy 0's calls)
+    ratio = tol_ratio(dev_bf16_to_f64(outs[0]),
+                      oracle.gemm(x0, w0.codes[0], w0.scales[0], float(w0.g[0])))
     step_bytes = w_bytes + M * 2048 * 2 + M * N * 2
     gbs = step_bytes / (ms * 1e-3) / 1e9
     print(json.dumps({
@@ -578,9 +831,9 @@ def bench_head(args):
         "config": {"workload": f"nvfp4_skinny_gemm_m{M}_k2048_n{N}", "M": M, "K": 2048, "N": N,
                    "weight_copies": copies, "timing": "hip graph replay, events"},
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes,
-        "runs": run_stats(),
+        "runs": run_stats(), "parity_max_ratio": round(ratio, 4),
     }), flush=True)
-    return 0
+    return 0 if ratio <= 1.0 else 1
 
 
 def bench_stack(args):
@@ -598,7 +851,6 @@ def bench_stack(args):
 
     import nvfp4_moe_skinny_amd as m
     from synth import workloads as W
-    from tests.helpers import pack, to_dev_bf16
 
     dev = torch.device("cuda:0")
     n_layers, M = W.STACK_LAYERS, W.STACK_M
@@ -727,31 +979,64 @@ def bench_ceiling(args):
     return 0
 
 
-def cpu_baseline(layers_host, logit_sets, x_host, copies, n_sets, budget_s, shared, bias):
-    """The oracle, single-threaded, on the first steps of the same sequence
-    (weight copy i % copies, logits/x set i % n_sets) until the time budget."""
+def timed_oracle(one, budget_s, threads):
+    """Calls one(i) for i = 0, 1, ... with the oracle on `threads` threads
+    until budget_s has passed: (calls, seconds, bytes summed from the calls'
+    return values)."""
     import oracle
-    done, t0, nbytes = 0, time.time(), 0
-    while True:
-        c, j = done % copies, done % n_sets
-        if c >= len(layers_host):
-            break
+    saved = oracle.threads()
+    oracle.set_threads(threads)
+    try:
+        done, nbytes, t0 = 0, 0, time.time()
+        while True:
+            b = one(done)
+            if b is None:
+                break
+            nbytes += b
+            done += 1
+            if time.time() - t0 >= budget_s:
+                break
+        return done, time.time() - t0, nbytes
+    finally:
+        oracle.set_threads(saved)
+
+
+def baseline_record(one, budget_s, rows_per_call, what):
+    """The oracle single-threaded and on every usable host thread (at most
+    16), each for about budget_s: the multi-threaded figure is the line's
+    value, with the single-threaded one beside it."""
+    import oracle
+    T = oracle.default_threads()
+    res = {}
+    for t in (1, T):
+        n, el, nb = timed_oracle(one, budget_s, t)
+        res[t] = {"value": round(nb / el / 1e9, 5), "unit": "GB/s", "cores": t,
+                  "rows_per_s": round(rows_per_call * n / el, 3), "seconds": round(el, 2),
+                  "calls": n}
+    top = res[T]
+    return {"value": top["value"], "unit": "GB/s", "cores": T, "kind": "oracle",
+            "rows_per_s": top["rows_per_s"], "seconds": top["seconds"],
+            "sample": f"{top['calls']} {what} of the same workload on {T} threads "
+                      f"(float64 oracle; output rows split over the threads)",
+            "single_thread": res[1], **cpu_info()}
+
+
+def cpu_baseline(layers_host, logit_sets, x_host, copies, n_sets, budget_s, shared, bias):
+    """The oracle on the first steps of the same sequence (weight copy
+    i % copies, logits/x set i % n_sets), single-threaded and threaded."""
+    import oracle
+
+    def one(i):  # the copies held on the host, in turn
+        c, j = i % min(copies, len(layers_host)), i % n_sets
         lay = layers_host[c]
         L = logit_sets[j]
         ids, w, out = oracle.moe_decode(x_host[j], L.logits, lay.k, lay.gate_up, lay.down,
                                         bias=L.bias, shared_gate_up=lay.shared_gate_up,
                                         shared_down=lay.shared_down)
-        nbytes += step_bytes(lay.M, lay.E, lay.k, lay.H, lay.I, len(np.unique(ids)), shared,
-                             bias)
-        done += 1
-        if time.time() - t0 >= budget_s:
-            break
-    el = time.time() - t0
-    M = layers_host[0].M
-    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "rows_per_s": round(M * done / el, 3), "seconds": round(el, 2),
-            "sample": f"{done} decode steps (route + expert FFNs + combine, float64) of the "
-                      f"same workload, single thread"}
+        return step_bytes(lay.M, lay.E, lay.k, lay.H, lay.I, len(np.unique(ids)), shared, bias)
+
+    return baseline_record(one, budget_s, layers_host[0].M,
+                           "decode steps (route + expert FFNs + combine)")
 
 
 if __name__ == "__main__":
