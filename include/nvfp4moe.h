@@ -35,7 +35,7 @@
  *   - Arguments are validated on the host before launch. Faults inside a
  *     kernel (for example from a bad device pointer) surface at the caller's
  *     next synchronisation.
- *   - Shapes are int64_t. Support set: K is 32 * 2^j with K <= 2048; N >= 1;
+ *   - Shapes are int64_t. Support set: K % 32 == 0 with 32 <= K <= 65536; N >= 1;
  *     1 <= k <= 8; 1 <= E <= 256. Anything else returns
  *     NVFP4MOE_ERR_UNSUPPORTED; no shape ever falls back to another path.
  *   - Stateless and thread-safe.
@@ -69,10 +69,12 @@ const char* nvfp4moe_version(void);
  *
  * The library streams weights in its own packed layout: a lossless byte
  * permutation of the canonical form that puts each wavefront's codes and
- * scales in 1 KB contiguous runs. The packed layout is opaque: to take a
- * slice of a matrix, slice the canonical form and pack again (slicing a
- * repacked 4-bit head silently produced garbage on the Elsa page, "FR-Spec,
- * and a silent bug").
+ * scales in 1 KB contiguous runs (the columns in panels of the largest
+ * 32 * 2^j <= 2048 dividing K; its size is a whole number of 9216-byte tiles
+ * per 16384 / panel rows, plus the tensor scales). The packed layout is
+ * opaque: to take a slice of a matrix, slice the canonical form and pack
+ * again (slicing a repacked 4-bit head silently produced garbage on the Elsa
+ * page, "FR-Spec, and a silent bug").
  */
 
 /* Bytes of packed storage for G matrices of N x K. Returns < 0 (an error
@@ -116,9 +118,11 @@ int32_t nvfp4_quantize(const uint16_t* x, int64_t G, int64_t N, int64_t K, uint8
  *
  * y[M][N] = bf16_rne( sum_k x[m][k] * W[n][k] ), one packed matrix (G = 1),
  * FP32 accumulation, BF16 activations x [M][K] and output y [M][N] (raw BF16
- * bits). M >= 1, N >= 1, K = 32 * 2^j <= 2048 (else NVFP4MOE_ERR_UNSUPPORTED);
- * x and w_packed 16-byte aligned. The FP32 summation order depends on the
- * shape: VALU tile products (rows in batches of 8) for M < 4 or K != 2048;
+ * bits). M >= 1, N >= 1, K % 32 == 0 with 32 <= K <= 65536 (else
+ * NVFP4MOE_ERR_UNSUPPORTED); x and w_packed 16-byte aligned. The FP32
+ * summation order depends on the shape: VALU tile products (rows in batches
+ * of 8; with several panels, each panel's partial sums added in panel order
+ * before the reduction over lanes) for M < 4 or K != 2048;
  * BF16 MFMA tiles (the weights decode exactly to BF16) for K = 2048 and
  * M >= 4, with K split over four waves when M <= 16 and N <= 4096.
  */
@@ -244,8 +248,10 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
  * when H = 2048 and I = 512,
  * slots with at least dense_min_rows rows run on BF16 MFMA: weights exact in
  * BF16, x as stored, h as a hi + lo BF16 pair (relative error <= 2^-17).
- * Extra support-set conditions: H and I are each 32 * 2^j in [256, 2048], and
- * I is a multiple of 16384 / H (gate and up halves start on a tile boundary).
+ * Extra support-set conditions: H % 32 == 0 and I % 32 == 0 (each at most
+ * 65536), and I is a multiple of the rows per tile of gate_up, 16384 / Kp with
+ * Kp the largest 32 * 2^j <= 2048 dividing H (the up half then starts on a row
+ * block: for H % 256 == 0, I % 64 == 0 is enough).
  * Returns NVFP4MOE_ERR_WORKSPACE if the workspace is too small and
  * NVFP4MOE_ERR_BAD_SHAPE for a schedule other than 0, 2 or 3. */
 int32_t moe_nvfp4_decode(const moe_nvfp4_args* args, hipStream_t stream);

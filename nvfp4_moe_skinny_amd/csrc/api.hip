@@ -56,10 +56,9 @@ int32_t launched(const char* what) {
   return ok();
 }
 
-bool valid_k(int64_t K) {
-  if (K < 32 || K > 2048) return false;
-  return ((K / 32) & (K / 32 - 1)) == 0 && K % 32 == 0;
-}
+// K of a packed matrix: a multiple of 32 (whole chunks), at most kMaxK.
+constexpr int64_t kMaxK = 65536;
+bool valid_k(int64_t K) { return K >= 32 && K <= kMaxK && K % 32 == 0; }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -92,11 +91,11 @@ int32_t dispatch_l(int64_t L, Args&&... args) {
 
 template <int L>
 struct GemmLaunch {
-  static int32_t run(const uint16_t* x, int64_t M, const uint8_t* w, int64_t N, uint16_t* y,
-                     hipStream_t s) {
-    const int64_t tiles = tiles_per_matrix(N, L * 32);
-    hipLaunchKernelGGL(skinny_gemm_kernel<L>, dim3(grid_for(tiles, 4, 1 << 30)), dim3(256), 0, s,
-                       x, M, w, N, y);
+  static int32_t run(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w, int64_t N,
+                     uint16_t* y, hipStream_t s) {
+    const int64_t blocks = row_blocks(N, K);  // one wave each
+    hipLaunchKernelGGL(skinny_gemm_kernel<L>, dim3(grid_for(blocks, 4, 1 << 30)), dim3(256), 0,
+                       s, x, M, K, w, N, y);
     return launched("nvfp4_skinny_gemm");
   }
 };
@@ -106,7 +105,7 @@ struct GemmLaunch {
 template <int LI>
 void launch_token_down(const MoeParams& p, hipStream_t s) {
   const int n = p.k + p.has_shared;
-  const int grid = p.M * p.P + p.proj_blocks;  // the projection's blocks first
+  const int grid = p.M * p.PD + p.proj_blocks;  // the projection's blocks first
   if (n <= 8)
     hipLaunchKernelGGL((token_down_combine_kernel<LI, 1>), dim3(grid), dim3(n * 64), 0, s, p);
   else
@@ -116,10 +115,11 @@ void launch_token_down(const MoeParams& p, hipStream_t s) {
 
 template <int LH, int LI, int RG, int RD, bool DENSE>
 int32_t launch_staged(const MoeParams& p, hipStream_t s) {
-  const int grid = p.slots * p.P;
   // many rows: the items take the slots heaviest first
-  hipLaunchKernelGGL((staged_gate_kernel<LH, RG, DENSE, true>), dim3(grid), dim3(64), 0, s, p);
-  hipLaunchKernelGGL((staged_down_kernel<LI, RD, DENSE, true>), dim3(grid), dim3(64), 0, s, p);
+  hipLaunchKernelGGL((staged_gate_kernel<LH, RG, DENSE, true>), dim3(p.slots * p.PG), dim3(64), 0,
+                     s, p);
+  hipLaunchKernelGGL((staged_down_kernel<LI, RD, DENSE, true>), dim3(p.slots * p.PD), dim3(64), 0,
+                     s, p);
   const int64_t outs = (int64_t)p.M * p.H;
   hipLaunchKernelGGL(staged_combine_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s,
                      p);
@@ -129,13 +129,14 @@ int32_t launch_staged(const MoeParams& p, hipStream_t s) {
 // One row per batch: gate_up with two waves per item (gate tile, up tile).
 template <int LH, int LI, bool DENSE>
 int32_t launch_staged_split(const MoeParams& p, bool token_major, hipStream_t s) {
-  const int grid = p.slots * p.P;
-  hipLaunchKernelGGL((staged_gate_split_kernel<LH, DENSE>), dim3(grid), dim3(128), 0, s, p);
+  hipLaunchKernelGGL((staged_gate_split_kernel<LH, DENSE>), dim3(p.slots * p.PG), dim3(128), 0, s,
+                     p);
   if (token_major) {
     launch_token_down<LI>(p, s);
     return launched("moe_nvfp4_decode");
   }
-  hipLaunchKernelGGL((staged_down_kernel<LI, 1, DENSE, false>), dim3(grid), dim3(64), 0, s, p);
+  hipLaunchKernelGGL((staged_down_kernel<LI, 1, DENSE, false>), dim3(p.slots * p.PD), dim3(64), 0,
+                     s, p);
   const int64_t outs = (int64_t)p.M * p.H;
   hipLaunchKernelGGL(staged_combine_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s,
                      p);
@@ -172,7 +173,6 @@ WsLayout ws_layout(int64_t M, int64_t k, int64_t H, int64_t I, bool shared) {
   return w;
 }
 
-bool valid_moe_dim(int64_t v) { return valid_k(v) && v >= 256; }
 
 }  // namespace
 
@@ -237,14 +237,18 @@ int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p,
     return fail(NVFP4MOE_ERR_BAD_SHAPE, "M, E, k, H, I must be >= 1");
   if (E > kRouteMaxE || k > kRouteMaxK || k > E)
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "need E <= 256 and k <= min(8, E)");
-  if (!valid_moe_dim(H) || !valid_moe_dim(I))
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be 32 * 2^j in [256, 2048]");
+  if (!valid_k(H) || !valid_k(I))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be multiples of 32 in [32, %lld]",
+                (long long)kMaxK);
   if (I % rows_per_tile(H) != 0)
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "I = %lld must be a multiple of 16384 / H = %lld",
+    return fail(NVFP4MOE_ERR_UNSUPPORTED,
+                "I = %lld must be a multiple of the gate_up rows per tile, %lld (the up half "
+                "starts on a row block)",
                 (long long)I, (long long)rows_per_tile(H));
   if (M * k + M > (int64_t)1 << 24) return fail(NVFP4MOE_ERR_UNSUPPORTED, "M too large");
-  // every grid (items x tiles per matrix) must stay below 2^31 blocks
-  if ((M * k + M) * tiles_per_matrix(H, I) > ((int64_t)1 << 31) - 1)
+  // every grid (items x row blocks per matrix) must stay below 2^31 blocks
+  const int64_t pg = I / rows_per_tile(H), pd = row_blocks(H, I);
+  if ((M * k + M) * (pg > pd ? pg : pd) + 4096 > ((int64_t)1 << 31) - 1)
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "M too large for the grid");
   if (a->schedule != 0 && a->schedule != 2 && a->schedule != 3)
     return fail(NVFP4MOE_ERR_BAD_SHAPE, "schedule must be 0, 2 or 3 (got %d)", (int)a->schedule);
@@ -281,8 +285,14 @@ int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p,
   p.k = (int)k;
   p.H = (int)H;
   p.I = (int)I;
-  p.LH = (int)(H / 32);
-  p.LI = (int)(I / 32);
+  p.KpH = (int)panel_k(H);
+  p.KpI = (int)panel_k(I);
+  p.LH = p.KpH / 32;
+  p.LI = p.KpI / 32;
+  p.QH = (int)panels(H);
+  p.QI = (int)panels(I);
+  p.RH = (int)rows_per_tile(H);
+  p.RI = (int)rows_per_tile(I);
   p.routed_slots = (int)(E < M * k ? E : M * k);
   p.has_shared = shared ? 1 : 0;
   p.slots = p.routed_slots + p.has_shared;
@@ -294,7 +304,8 @@ int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p,
     p.sgu_g = (const float*)(p.sgu + gscale_offset(1, 2 * I, H));
     p.sdn_g = (const float*)(p.sdn + gscale_offset(1, H, I));
   }
-  p.P = (int)(I / rows_per_tile(H));  // == tiles_per_matrix(H, I) == H * I / 16384
+  p.PG = (int)pg;
+  p.PD = (int)pd;
   p.pair_regs = M * k <= 128 ? (int)((M * k + 63) / 64) : 0;
   p.hp = (float*)(wsb + ws.hp_off);
   p.yp = (float*)(wsb + ws.yp_off);
@@ -326,8 +337,9 @@ const char* nvfp4moe_version(void) { return "nvfp4moe 0.1 gfx950"; }
 
 int64_t nvfp4_packed_bytes(int64_t G, int64_t N, int64_t K) {
   if (G < 1 || N < 1) return fail(NVFP4MOE_ERR_BAD_SHAPE, "G and N must be >= 1");
-  if (!valid_k(K)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "K = %lld: need 32 * 2^j <= 2048",
-                               (long long)K);
+  if (!valid_k(K))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "K = %lld: need a multiple of 32 in [32, %lld]",
+                (long long)K, (long long)kMaxK);
   ok();
   return G * matrix_bytes(N, K) + align256(4 * G);
 }
@@ -415,8 +427,9 @@ int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w
                           int64_t N, uint16_t* y, hipStream_t stream) {
   if (!x || !w_packed || !y) return fail(NVFP4MOE_ERR_NULL_ARG, "nvfp4_skinny_gemm: null");
   if (M < 1 || N < 1) return fail(NVFP4MOE_ERR_BAD_SHAPE, "M and N must be >= 1");
-  if (!valid_k(K)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "K = %lld: need 32 * 2^j <= 2048",
-                               (long long)K);
+  if (!valid_k(K))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "K = %lld: need a multiple of 32 in [32, %lld]",
+                (long long)K, (long long)kMaxK);
   if (!aligned(x, 16) || !aligned(w_packed, 16))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "x and w_packed must be 16-byte aligned");
   if (K == 2048 && M >= kGemmDenseMinRows && M <= 16 &&
@@ -437,7 +450,9 @@ int32_t nvfp4_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const void* w
                        y);
     return launched("nvfp4_skinny_gemm");
   }
-  return dispatch_l<GemmLaunch>(K / 32, x, M, (const uint8_t*)w_packed, N, y, stream);
+  if (row_blocks(N, K) > ((int64_t)1 << 32))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "N too large for the grid");
+  return dispatch_l<GemmLaunch>(panel_k(K) / 32, x, M, K, (const uint8_t*)w_packed, N, y, stream);
 }
 
 int32_t fp8_skinny_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w_fp8,
@@ -524,8 +539,9 @@ int64_t moe_nvfp4_workspace_bytes(int64_t M, int64_t E, int64_t k, int64_t H, in
                                   int32_t has_shared) {
   if (M < 1 || E < 1 || k < 1 || H < 1 || I < 1)
     return fail(NVFP4MOE_ERR_BAD_SHAPE, "sizes must be >= 1");
-  if (!valid_moe_dim(H) || !valid_moe_dim(I))
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be 32 * 2^j in [256, 2048]");
+  if (!valid_k(H) || !valid_k(I))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "H and I must be multiples of 32 in [32, %lld]",
+                (long long)kMaxK);
   ok();
   return ws_layout(M, k, H, I, has_shared != 0).total;
 }
@@ -590,7 +606,7 @@ int32_t route_decode(const moe_nvfp4_args* a, const float* logits, const float* 
     const int64_t blocks16 = (tiles_per_matrix(a->proj_n, 2048) + 1) / 2;
     p.proj_blocks = (int)((blocks16 + 7) / 8 * 8);  // keeps the down blocks' XCD order
   }
-  const int grid = (int)((M * a->k + (p.has_shared ? M : 0)) * p.P);
+  const int grid = (int)((M * a->k + (p.has_shared ? M : 0)) * p.PG);
   int32_t* ids = const_cast<int32_t*>(a->ids);
   float* w = const_cast<float*>(a->w);
   if (specialised)

@@ -1,19 +1,26 @@
 // common.hpp - packed NVFP4 geometry and wavefront building blocks for gfx950.
 //
-// Packed layout of one [N][K] matrix (K = 32 * 2^j <= 2048):
+// Packed layout of one [N][K] matrix (K % 32 == 0):
+//   panel     Kp = the largest 32 * 2^j <= 2048 that divides K; the matrix's
+//             columns fall into Q = K / Kp panels of Kp columns
 //   chunk     16 bytes of codes = 32 consecutive elements of one row
-//   L         chunks per row = K / 32 (lanes that share a row in a slab)
-//   slab      64 consecutive chunks in canonical row-major order = 1 KB, one
-//             128-bit load per lane of a wave64
-//   tile      8 slabs = 16384 / K rows: 8 KB of codes followed by 1 KB of
-//             scales, scales arranged [lane][slab][2] so that one 128-bit
-//             load gives a lane the two E4M3 scales of each of its 8 chunks
-//   matrix    ceil(N / rows_per_tile) tiles (rows past N are zero)
+//   L         chunks per row of a panel = Kp / 32 (lanes that share a row in
+//             a slab)
+//   slab      64 consecutive chunks of one panel, rows in canonical
+//             row-major order = 1 KB, one 128-bit load per lane of a wave64
+//   tile      8 slabs = R = 16384 / Kp rows of one panel: 8 KB of codes
+//             followed by 1 KB of scales, scales arranged [lane][slab][2] so
+//             that one 128-bit load gives a lane the two E4M3 scales of each
+//             of its 8 chunks
+//   row block R rows across the whole K: the Q tiles of its panels, back to
+//             back (tile b Q + q is row block b, panel q)
+//   matrix    ceil(N / R) row blocks (rows past N are zero)
 //   tensor    G matrices back to back, then the G FP32 tensor scales
-// Lane l of slab i of tile t holds chunk 64 i + l of the tile: row
-// t * rows_per_tile + i * (64 / L) + l / L, elements 32 (l % L) ... + 31.
-// A lane therefore sees the same 32 columns in every slab, so activation
-// values stay in its registers for a whole tile.
+// Lane l of slab i of tile (b, q) holds chunk 64 i + l of the tile: row
+// b R + i (64 / L) + l / L, elements q Kp + 32 (l % L) ... + 31. A lane
+// therefore sees the same 32 columns in every slab of a tile, so activation
+// values stay in its registers for a whole tile. When K is a power of two
+// (up to 2048) there is one panel and a row block is one tile.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,9 +36,20 @@ constexpr int kTileBytes = 9216;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-__host__ __device__ constexpr int64_t rows_per_tile(int64_t K) { return 16384 / K; }
-__host__ __device__ constexpr int64_t tiles_per_matrix(int64_t N, int64_t K) {
+// Panel width of a K-column matrix (K % 32 == 0): the largest 32 * 2^j <= 2048
+// dividing K.
+__host__ __device__ constexpr int64_t panel_k(int64_t K) {
+  int64_t kp = 32;
+  while (kp < 2048 && K % (2 * kp) == 0) kp *= 2;
+  return kp;
+}
+__host__ __device__ constexpr int64_t panels(int64_t K) { return K / panel_k(K); }
+__host__ __device__ constexpr int64_t rows_per_tile(int64_t K) { return 16384 / panel_k(K); }
+__host__ __device__ constexpr int64_t row_blocks(int64_t N, int64_t K) {
   return (N + rows_per_tile(K) - 1) / rows_per_tile(K);
+}
+__host__ __device__ constexpr int64_t tiles_per_matrix(int64_t N, int64_t K) {
+  return row_blocks(N, K) * panels(K);
 }
 __host__ __device__ constexpr int64_t matrix_bytes(int64_t N, int64_t K) {
   return tiles_per_matrix(N, K) * kTileBytes;

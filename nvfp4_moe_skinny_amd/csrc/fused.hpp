@@ -22,11 +22,12 @@ __global__ void __launch_bounds__(128, 4) fused_route_gate_kernel(MoeParams p,
                                                                   const float* __restrict__ bias,
                                                                   int32_t* __restrict__ ids,
                                                                   float* __restrict__ w) {
-  __shared__ float up_lds[64];
+  constexpr int NV = LHC ? 1 : 8;  // reduced values a lane may hold
+  __shared__ float up_lds[NV][64];
   __shared__ float lp[2][kRouteMaxE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = xcd_block((int)blockIdx.x, (int)gridDim.x);
-  const int item = b / p.P, j = b % p.P;
+  const int item = b / p.PG, j = b % p.PG;
   const int npairs = p.M * p.k;
   const bool sh = item >= npairs;
   const int m = sh ? item - npairs : item / p.k;
@@ -50,14 +51,32 @@ __global__ void __launch_bounds__(128, 4) fused_route_gate_kernel(MoeParams p,
   }
   const uint8_t* mat = sh ? p.sgu : p.gu + (int64_t)e * p.gu_mat_bytes;
   const float g = sh ? p.sgu_g[0] : p.gu_g[e];
-  TileRegs T;
-  load_tile(mat + (int64_t)(wave == 0 ? j : j + p.P) * kTileBytes, lane, T);
-  const float v = tile_row_value<LHC>(T, xr, L);
-  if (wave == 1) up_lds[lane] = v;
+  const int rb = wave == 0 ? j : j + p.PG;  // gate row block j, or the matching up one
+  float v[8];
+  if (LHC != 0 || p.QH == 1) {
+    TileRegs T;
+    load_tile(mat + (int64_t)rb * kTileBytes, lane, T);
+    float part[1][8];
+    tile_dot_bf16<1>(T, xr, part);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = part[0][i];
+    reduce_slabs_rt<LHC>(v, lane, L);
+  } else {
+    panels_dot_bf16<LHC>(mat, rb, p.QH, p.KpH, p.x, p.H, m, lane, L, v);
+  }
+  const int nv = LHC ? 1 : reduced_values(L);
+#pragma unroll
+  for (int q = 0; q < NV; ++q)
+    if (wave == 1 && q < nv) up_lds[q][lane] = v[q];
   __syncthreads();
   if (wave == 0 && reduced_writer_rt(lane, L)) {
-    const int i = j * (16384 / p.H) + reduced_row(lane, L);
-    p.hp[(int64_t)item * p.I + i] = silu(v * g) * (up_lds[lane] * g);
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      if (q < nv) {
+        const int i = j * p.RH + reduced_row_v(lane, L, q);
+        p.hp[(int64_t)item * p.I + i] = silu(v[q] * g) * (up_lds[q][lane] * g);
+      }
+    }
   }
 }
 

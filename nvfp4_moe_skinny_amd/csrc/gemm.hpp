@@ -1,13 +1,37 @@
 // gemm.hpp - dense skinny NVFP4 product y = x W^T (BF16 rows, BF16 out).
 //
-// One wave per packed tile; the tile stays in registers while the rows pass
-// in batches of up to 8.
+// One wave per row block of W. With one panel (K a power of two <= 2048) the
+// tile stays in registers while the rows pass in batches of up to 8; with Q
+// panels the wave streams the row block's Q tiles per batch of rows, adding
+// each panel's per-slab partial sums before one reduction.
 #pragma once
 
 #include "dense.hpp"
 
 namespace nvfp4moe {
 
+// Reduces R rows' per-slab partial sums and writes rows m0 .. m0 + rows - 1
+// of y for row block blk.
+template <int L, int R>
+__device__ __forceinline__ void gemm_write(float (&part)[R][8], int64_t m0, int rows, int lane,
+                                           int64_t blk, int64_t N, float g,
+                                           uint16_t* __restrict__ y) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) reduce_slabs<L>(part[r], lane);
+  if (!reduced_writer<L>(lane)) return;
+  const int64_t rpt = 16384 / (L * 32);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= rows) break;
+#pragma unroll
+    for (int j = 0; j < reduced_count<L>(); ++j) {
+      const int64_t n = blk * rpt + tile_row<L>(reduced_slab<L>(lane) + j, lane);
+      if (n < N) y[(m0 + r) * N + n] = f32_to_bf16_rne(part[r][j] * g);
+    }
+  }
+}
+
+// One panel (the tile held in T): rows m0 .. m0 + rows - 1.
 template <int L, int R>
 __device__ __forceinline__ void gemm_rows(const TileRegs& T, const uint16_t* __restrict__ x,
                                           int64_t K, int64_t m0, int rows, int col0, int lane,
@@ -18,30 +42,62 @@ __device__ __forceinline__ void gemm_rows(const TileRegs& T, const uint16_t* __r
   for (int r = 0; r < R; ++r) load_x_bf16(x, K, m0 + r, r < rows, col0, xr[r]);
   float part[R][8];
   tile_dot_bf16<R>(T, xr, part);
-#pragma unroll
-  for (int r = 0; r < R; ++r) reduce_slabs<L>(part[r], lane);
-  if (!reduced_writer<L>(lane)) return;
-  const int64_t rpt = rows_per_tile(L * 32);
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (r >= rows) break;
-#pragma unroll
-    for (int j = 0; j < reduced_count<L>(); ++j) {
-      const int64_t n = tile * rpt + tile_row<L>(reduced_slab<L>(lane) + j, lane);
-      if (n < N) y[(m0 + r) * N + n] = f32_to_bf16_rne(part[r][j] * g);
-    }
-  }
+  gemm_write<L, R>(part, m0, rows, lane, tile, N, g, y);
 }
 
+// Q panels: the row block's tiles streamed in turn for rows m0 .. m0 + rows - 1.
+template <int L, int R>
+__device__ __forceinline__ void gemm_rows_panels(const uint8_t* __restrict__ blk_tiles, int64_t Q,
+                                                 const uint16_t* __restrict__ x, int64_t K,
+                                                 int64_t m0, int rows, int col0, int lane,
+                                                 int64_t blk, int64_t N, float g,
+                                                 uint16_t* __restrict__ y) {
+  float acc[R][8];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[r][i] = 0.0f;
+#pragma unroll 1
+  for (int64_t q = 0; q < Q; ++q) {
+    uint4 xr[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_x_bf16(x, K, m0 + r, r < rows, q * (L * 32) + col0, xr[r]);
+    TileRegs T;
+    load_tile(blk_tiles + q * kTileBytes, lane, T);
+    tile_dot_bf16<R, true>(T, xr, acc);
+  }
+  gemm_write<L, R>(acc, m0, rows, lane, blk, N, g, y);
+}
+
+// L = Kp / 32 of the matrix's panel width; K = Q Kp.
 template <int L>
 __global__ void __launch_bounds__(256) skinny_gemm_kernel(const uint16_t* __restrict__ x,
-                                                          int64_t M, const uint8_t* __restrict__ w,
+                                                          int64_t M, int64_t K,
+                                                          const uint8_t* __restrict__ w,
                                                           int64_t N, uint16_t* __restrict__ y) {
-  constexpr int64_t K = L * 32;
   const int lane = threadIdx.x & 63;
-  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tile >= tiles_per_matrix(N, K)) return;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // row block of W
+  if (blk >= row_blocks(N, K)) return;
   const float g = reinterpret_cast<const float*>(w + gscale_offset(1, N, K))[0];
+  const int64_t Q = K / (L * 32);
+  if (Q > 1) {
+    const uint8_t* tiles = w + blk * Q * kTileBytes;
+    const int col0 = 32 * (lane % L);
+#pragma unroll 1
+    for (int64_t m0 = 0; m0 < M; m0 += 8) {
+      const int rows = (int)((M - m0) < 8 ? (M - m0) : 8);
+      if (rows > 4)
+        gemm_rows_panels<L, 8>(tiles, Q, x, K, m0, rows, col0, lane, blk, N, g, y);
+      else if (rows > 2)
+        gemm_rows_panels<L, 4>(tiles, Q, x, K, m0, rows, col0, lane, blk, N, g, y);
+      else if (rows > 1)
+        gemm_rows_panels<L, 2>(tiles, Q, x, K, m0, rows, col0, lane, blk, N, g, y);
+      else
+        gemm_rows_panels<L, 1>(tiles, Q, x, K, m0, rows, col0, lane, blk, N, g, y);
+    }
+    return;
+  }
+  const int64_t tile = blk;
   TileRegs T;
   load_tile(w + tile * kTileBytes, lane, T);
   const int col0 = 32 * (lane % L);

@@ -2,9 +2,12 @@
 // slots (one per active expert, plus the shared expert) and their rows, and
 // the reduction of a tile's per-slab partial sums for a runtime row width.
 //
-// Tiles: with rows_per_tile(K) = 16384 / K, the gate half of one expert's
-// fused [2I][H] gate_up matrix and its [H][I] down matrix both hold
-// P = H * I / 16384 tiles. Slot s < n_active is expert active[s] with the
+// Row blocks: the gate half of one expert's fused [2I][H] gate_up matrix
+// holds PG = I / RH row blocks of RH = 16384 / panel_k(H) rows (the up half
+// the next PG), each of QH = H / panel_k(H) tiles; its [H][I] down matrix
+// holds PD = ceil(H / RI) row blocks of RI = 16384 / panel_k(I) rows, each of
+// QI tiles. With H = 2048 and I = 512 (one panel each) PG = PD = 64 and a
+// row block is one tile. Slot s < n_active is expert active[s] with the
 // (row, slot) pairs pairs[offsets[e] .. offsets[e+1]); slot `routed_slots` is
 // the shared expert over every row.
 #pragma once
@@ -34,9 +37,13 @@ struct MoeParams {
   const float* sdn_g;
   int64_t gu_mat_bytes, dn_mat_bytes;
   int M, E, k, H, I;
-  int LH, LI;          // lanes per row: H / 32, I / 32
+  int LH, LI;          // lanes per row of a panel: panel_k(H) / 32, panel_k(I) / 32
+  int QH, QI;          // panels: H / panel_k(H), I / panel_k(I)
+  int KpH, KpI;        // panel widths
+  int RH, RI;          // rows per tile: 16384 / panel_k(H), 16384 / panel_k(I)
+  int PG;              // row blocks per gate (or up) half: I / RH
+  int PD;              // row blocks of a down matrix: ceil(H / RI)
   int routed_slots, has_shared, slots;
-  int P;               // tiles per gate half = tiles per down matrix = H * I / 16384
   int pair_regs;       // ceil(M * k / 64) <= 2: pairs[] is held in registers; else 0
   float* hp;           // [P_tot][I] h words (FP32, or hi / lo BF16 for MFMA slots)
   float* yp;           // [P_tot][H] expert outputs (FP32)
@@ -109,39 +116,95 @@ __device__ __forceinline__ int pair_xrow(const MoeParams& p, int pair) {
   return pair >= p.M * p.k ? pair - p.M * p.k : pair / p.k;
 }
 
-// ---- segmented reduction with a runtime row width (L >= 8) ----------------------------
+// ---- segmented reduction with a runtime row width -------------------------------------
 
-// After: v[0] of lane l holds the full sum for slab ((l & (L-1)) >> (log2 L - 3)),
-// identical in the L/8 lanes of its group.
+__device__ __forceinline__ int log2i(int v) { return 31 - __builtin_clz(v); }
+
+// Reduces a lane's 8 per-slab partial sums over the L lanes that share a row
+// (L = LC when LC != 0, else the runtime Lrt; L a power of two <= 64). After:
+// L >= 8: v[0] holds the full sum of slab ((l & (L-1)) >> (log2 L - 3)),
+// identical in the L/8 lanes of its group; L < 8: v[0 .. 8/L) hold the sums
+// of slabs ((l & (L-1)) << (3 - log2 L)) + j. reduced_values / reduced_row_v
+// / reduced_writer_rt name them.
 template <int LC>
 __device__ __forceinline__ void reduce_slabs_rt(float (&v)[8], int lane, int Lrt) {
   if constexpr (LC != 0) {
     reduce_slabs<LC>(v, lane);
   } else {
+    const int halvings = Lrt >= 8 ? 3 : log2i(Lrt);
     int count = 8;
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
-      const int d = Lrt >> (t + 1);
-      const int half = count >> 1;
+      if (t < halvings) {
+        const int d = Lrt >> (t + 1);
+        const int half = count >> 1;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j < half) v[j] = halve(v[j], v[j + half], d, lane);
+        for (int j = 0; j < 4; ++j) {
+          if (j < half) v[j] = halve(v[j], v[j + half], d, lane);
+        }
+        count = half;
       }
-      count = half;
     }
     for (int d = Lrt / 16; d >= 1; d >>= 1) v[0] = fold(v[0], d, lane);
   }
 }
 
-__device__ __forceinline__ int log2i(int v) { return 31 - __builtin_clz(v); }
+// Reduced values per lane: 1 for L >= 8, else 8 / L.
+__device__ __forceinline__ int reduced_values(int L) { return L >= 8 ? 1 : 8 / L; }
 
-// (tile row, writer?) of the reduced value held by `lane` for row width L >= 8.
-__device__ __forceinline__ int reduced_row(int lane, int L) {
-  const int slab = ((lane & (L - 1)) >> (log2i(L) - 3)) & 7;
+// Tile row of reduced value j of `lane`.
+__device__ __forceinline__ int reduced_row_v(int lane, int L, int j) {
+  const int slab = L >= 8 ? ((lane & (L - 1)) >> (log2i(L) - 3)) & 7
+                          : ((lane & (L - 1)) << (3 - log2i(L))) + j;
   return slab * (64 / L) + lane / L;
 }
+__device__ __forceinline__ int reduced_row(int lane, int L) { return reduced_row_v(lane, L, 0); }
+
+// Lanes that write their reduced values (one per distinct result).
 __device__ __forceinline__ bool reduced_writer_rt(int lane, int L) {
-  return (lane & (L / 8 - 1)) == 0;
+  return L <= 8 || (lane & (L / 8 - 1)) == 0;
+}
+
+// ---- a row block over its panels, one activation row ------------------------------------
+
+// v = the per-slab sums of row block rb of a matrix (its Q tiles back to back
+// from `mat`) with one activation row, reduced over the row's lanes
+// (reduce_slabs_rt): BF16 row x[xrow] of length ldx, or FP32 row h[hrow].
+// Each panel's tile and the row's matching columns are loaded in turn.
+template <int LC>
+__device__ __forceinline__ void panels_dot_bf16(const uint8_t* mat, int rb, int Q, int Kp,
+                                                const uint16_t* x, int64_t ldx, int64_t xrow,
+                                                int lane, int L, float (&v)[8]) {
+  float acc[1][8] = {{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll 1
+  for (int q = 0; q < Q; ++q) {
+    uint4 xr[1][4];
+    load_x_bf16(x, ldx, xrow, true, q * Kp + 32 * (lane % L), xr[0]);
+    TileRegs T;
+    load_tile(mat + ((int64_t)rb * Q + q) * kTileBytes, lane, T);
+    tile_dot_bf16<1, true>(T, xr, acc);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = acc[0][i];
+  reduce_slabs_rt<LC>(v, lane, L);
+}
+
+template <int LC>
+__device__ __forceinline__ void panels_dot_f32(const uint8_t* mat, int rb, int Q, int Kp,
+                                               const float* h, int64_t ldh, int64_t hrow,
+                                               int lane, int L, float (&v)[8]) {
+  float acc[1][8] = {{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll 1
+  for (int q = 0; q < Q; ++q) {
+    float hr[1][32];
+    load_h_f32(h, ldh, hrow, true, q * Kp + 32 * (lane % L), hr[0]);
+    TileRegs T;
+    load_tile(mat + ((int64_t)rb * Q + q) * kTileBytes, lane, T);
+    tile_dot_f32<1, true>(T, hr, acc);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = acc[0][i];
+  reduce_slabs_rt<LC>(v, lane, L);
 }
 
 // Pair ids and activation rows r0 .. r0 + R - 1 of a slot (rows past `rows` are zero).

@@ -11,7 +11,8 @@ __global__ void __launch_bounds__(256) pack_kernel(const uint8_t* __restrict__ c
                                                    const uint8_t* __restrict__ scales,
                                                    const float* __restrict__ g, int64_t G,
                                                    int64_t N, int64_t K, uint8_t* __restrict__ out) {
-  const int64_t L = K / 32;
+  const int64_t L = panel_k(K) / 32;
+  const int64_t Q = panels(K);
   const int64_t rpt = rows_per_tile(K);
   const int64_t tiles = tiles_per_matrix(N, K);
   const int64_t total = G * tiles * 512;
@@ -20,11 +21,11 @@ __global__ void __launch_bounds__(256) pack_kernel(const uint8_t* __restrict__ c
        c += (int64_t)gridDim.x * blockDim.x) {
     const int64_t gi = c / (tiles * 512);
     const int64_t rem = c - gi * tiles * 512;
-    const int64_t t = rem / 512;
+    const int64_t t = rem / 512;   // row block t / Q, panel t % Q
     const int64_t ct = rem % 512;  // chunk within tile = 64 * slab + lane
     const int64_t slab = ct / 64, lane = ct % 64;
-    const int64_t n = t * rpt + ct / L;
-    const int64_t q = ct % L;
+    const int64_t n = (t / Q) * rpt + ct / L;
+    const int64_t q = (t % Q) * L + ct % L;  // chunk of the row
     uint8_t* dst = out + gi * mbytes + t * kTileBytes;
     uint8_t* sdst = dst + kTileCodeBytes + lane * 16 + slab * 2;
     if (n < N) {
@@ -52,7 +53,8 @@ __global__ void __launch_bounds__(256) pack_kernel(const uint8_t* __restrict__ c
 __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ packed, int64_t G,
                                                       int64_t N, int64_t K, int apply_g, int path,
                                                       float* __restrict__ out) {
-  const int64_t L = K / 32;
+  const int64_t L = panel_k(K) / 32;
+  const int64_t Q = panels(K);
   const int64_t rpt = rows_per_tile(K);
   const int64_t tiles = tiles_per_matrix(N, K);
   const int64_t total = G * tiles * 512;
@@ -65,9 +67,9 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict_
     const int64_t t = rem / 512;
     const int ct = (int)(rem % 512);
     const int slab = ct / 64, lane = ct % 64;
-    const int64_t n = t * rpt + ct / L;
+    const int64_t n = (t / Q) * rpt + ct / L;
     if (n >= N) continue;
-    const int64_t q = ct % L;
+    const int64_t q = (t % Q) * L + ct % L;  // chunk of the row
     const uint8_t* tile = packed + gi * mbytes + t * kTileBytes;
     const uint4 cv = *reinterpret_cast<const uint4*>(tile + ct * 16);
     const uint4 sv = *reinterpret_cast<const uint4*>(tile + kTileCodeBytes + lane * 16);

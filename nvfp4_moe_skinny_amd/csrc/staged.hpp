@@ -153,11 +153,27 @@ __device__ __forceinline__ void staged_gate_math(const MoeParams& p, const TileR
     }
   }
   if (reduced_writer_rt(lane, L)) {
-    const int i = j * (16384 / p.H) + reduced_row(lane, L);
+    const int i = j * p.RH + reduced_row(lane, L);
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (r < rows) p.hp[(int64_t)pr[r] * p.I + i] = silu(ug[r] * g) * (uu[r] * g);
   }
+}
+
+// Generic row widths (any L, any number of panels), one row: h of the row's
+// pair for gate row block j (gate rows in wave `gwave`'s values vg, up rows
+// in vu) is written by the lanes that hold the reduced values.
+__device__ __forceinline__ void write_h_generic(const MoeParams& p, int pair, int j, float g,
+                                                const float (&vg)[8], const float (&vu)[8],
+                                                int L) {
+  const int lane = threadIdx.x & 63;
+  if (!reduced_writer_rt(lane, L)) return;
+  const int nv = reduced_values(L);
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    if (q < nv)
+      p.hp[(int64_t)pair * p.I + j * p.RH + reduced_row_v(lane, L, q)] =
+          silu(vg[q] * g) * (vu[q] * g);
 }
 
 template <int LC, int R>
@@ -261,15 +277,15 @@ __device__ __forceinline__ void staged_gate_dense(const MoeParams& p, const Slot
 template <int LHC, int RMAX, bool DENSE, bool ORDER>
 __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_gate_kernel(MoeParams p) {
   const int lane = threadIdx.x;
-  const int j = blockIdx.x % p.P;
+  const int j = blockIdx.x % p.PG;
   PairCache pc;
   load_pair_cache(p, lane, pc);
   SlotInfo s;
-  if (!item_slot_info<ORDER>(p, blockIdx.x / p.P, s)) return;
+  if (!item_slot_info<ORDER>(p, blockIdx.x / p.PG, s)) return;
   const uint8_t* mat = gate_matrix(p, s);
   const float g = s.shared ? p.sgu_g[0] : p.gu_g[s.e];
   const uint8_t* tg = mat + (int64_t)j * kTileBytes;
-  const uint8_t* tu = mat + (int64_t)(j + p.P) * kTileBytes;
+  const uint8_t* tu = mat + (int64_t)(j + p.PG) * kTileBytes;
   if constexpr (DENSE) {
     if (s.rows >= p.dense_min_rows) {
       staged_gate_dense<2, 1>(p, s, tg, tu, j, g);
@@ -277,6 +293,20 @@ __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_gate_kernel(MoeP
     }
   }
   const int L = LHC ? LHC : p.LH;
+  if constexpr (LHC == 0) {
+    if (p.QH > 1 || L < 8) {  // any row width, any number of panels: one row at a time
+#pragma unroll 1
+      for (int r = 0; r < s.rows; ++r) {
+        const int pair = slot_pair(p, s, r, pc);
+        float vg[8], vu[8];
+        panels_dot_bf16<0>(mat, j, p.QH, p.KpH, p.x, p.H, pair_xrow(p, pair), lane, L, vg);
+        panels_dot_bf16<0>(mat, j + p.PG, p.QH, p.KpH, p.x, p.H, pair_xrow(p, pair), lane, L,
+                           vu);
+        write_h_generic(p, pair, j, g, vg, vu, L);
+      }
+      return;
+    }
+  }
   TileRegs TG, TU;
   // the first batch's activation rows are requested before the tiles, and
   // its slabs are multiplied as they arrive (no wait for the whole tiles)
@@ -378,7 +408,7 @@ __global__ void __launch_bounds__(128, 4) staged_gate_split_kernel(MoeParams p) 
   __shared__ float up_lds[64];
   __shared__ f32x4 dred[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = staged_slot(p, blockIdx.x / p.P), j = blockIdx.x % p.P;
+  const int slot = staged_slot(p, blockIdx.x / p.PG), j = blockIdx.x % p.PG;
   PairCache pc;
   load_pair_cache(p, lane, pc);
   SlotInfo s;
@@ -386,7 +416,7 @@ __global__ void __launch_bounds__(128, 4) staged_gate_split_kernel(MoeParams p) 
   const uint8_t* mat = gate_matrix(p, s);
   const float g = s.shared ? p.sgu_g[0] : p.gu_g[s.e];
   const uint8_t* tg = mat + (int64_t)j * kTileBytes;
-  const uint8_t* tu = mat + (int64_t)(j + p.P) * kTileBytes;
+  const uint8_t* tu = mat + (int64_t)(j + p.PG) * kTileBytes;
   if constexpr (DENSE) {
     if (s.rows >= p.dense_min_rows) {
       staged_gate_dense_halves<2>(p, s, tg, tu, j, g, dred);  // s.rows <= M <= 16
@@ -394,8 +424,32 @@ __global__ void __launch_bounds__(128, 4) staged_gate_split_kernel(MoeParams p) 
     }
   }
   const int L = LHC ? LHC : p.LH;
+  if constexpr (LHC == 0) {
+    if (p.QH > 1 || L < 8) {  // any row width, any number of panels: wave 1 takes the up half
+      __shared__ float up_rows[8][64];
+      const int nv = reduced_values(L);
+#pragma unroll 1
+      for (int r = 0; r < s.rows; ++r) {
+        const int pair = slot_pair(p, s, r, pc);
+        float v[8];
+        panels_dot_bf16<0>(mat, wave == 0 ? j : j + p.PG, p.QH, p.KpH, p.x, p.H,
+                           pair_xrow(p, pair), lane, L, v);
+        for (int q = 0; q < nv; ++q)
+          if (wave == 1) up_rows[q][lane] = v[q];
+        __syncthreads();
+        if (wave == 0) {
+          float vu[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) vu[q] = q < nv ? up_rows[q][lane] : 0.0f;
+          write_h_generic(p, pair, j, g, v, vu, L);
+        }
+        __syncthreads();
+      }
+      return;
+    }
+  }
   const bool writer = reduced_writer_rt(lane, L);
-  const int i = j * (16384 / p.H) + reduced_row(lane, L);
+  const int i = j * p.RH + reduced_row(lane, L);
   TileRegs T;
 #pragma unroll 1
   for (int r = 0; r < s.rows; ++r) {
@@ -443,7 +497,7 @@ __device__ __forceinline__ void staged_down_math(const MoeParams& p, const TileR
   tile_dot_f32<R>(T, hr, part);
 #pragma unroll
   for (int r = 0; r < R; ++r) reduce_slabs_rt<LC>(part[r], lane, L);
-  const int n = t * (16384 / p.I) + reduced_row(lane, L);
+  const int n = t * p.RI + reduced_row(lane, L);
   if (reduced_writer_rt(lane, L) && n < p.H) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -534,11 +588,11 @@ __device__ __forceinline__ void staged_down_dense(const MoeParams& p, const Slot
 template <int LIC, int RMAX, bool DENSE, bool ORDER>
 __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_down_kernel(MoeParams p) {
   const int lane = threadIdx.x;
-  const int t = blockIdx.x % p.P;
+  const int t = blockIdx.x % p.PD;
   PairCache pc;
   load_pair_cache(p, lane, pc);
   SlotInfo s;
-  if (!item_slot_info<ORDER>(p, blockIdx.x / p.P, s)) return;
+  if (!item_slot_info<ORDER>(p, blockIdx.x / p.PD, s)) return;
   const uint8_t* tile = down_matrix(p, s) + (int64_t)t * kTileBytes;
   const float g = s.shared ? p.sdn_g[0] : p.dn_g[s.e];
   if constexpr (DENSE) {
@@ -549,6 +603,24 @@ __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_down_kernel(MoeP
     }
   }
   const int L = LIC ? LIC : p.LI;
+  if constexpr (LIC == 0) {
+    if (p.QI > 1 || L < 8) {  // any row width, any number of panels: one row at a time
+      const int nv = reduced_values(L);
+#pragma unroll 1
+      for (int r = 0; r < s.rows; ++r) {
+        const int pair = slot_pair(p, s, r, pc);
+        float v[8];
+        panels_dot_f32<0>(down_matrix(p, s), t, p.QI, p.KpI, p.hp, p.I, pair, lane, L, v);
+        if (reduced_writer_rt(lane, L)) {
+          for (int q = 0; q < nv; ++q) {
+            const int n = t * p.RI + reduced_row_v(lane, L, q);
+            if (n < p.H) p.yp[(int64_t)pair * p.H + n] = v[q] * g;
+          }
+        }
+      }
+      return;
+    }
+  }
   TileRegs T;
   // h is complete (the gate_up launch has ended): the first batch's rows go
   // out with the tile and its slabs are multiplied as they arrive
@@ -624,7 +696,7 @@ constexpr int kTokenMajorMaxRows = 8;
 // Slot q of row m (q = k: the shared expert), down tile t: its outputs to ys[q].
 template <int LIC>
 __device__ __forceinline__ void token_down_slot(const MoeParams& p, int q, int m, int t, int L,
-                                                float (*ys)[64]) {
+                                                float (*ys)[LIC ? 512 / LIC : 512]) {
   const int lane = threadIdx.x & 63;
   const bool sh = q == p.k;  // the shared expert's slot (only with has_shared)
   const int pair = sh ? p.M * p.k + m : m * p.k + q;
@@ -632,6 +704,16 @@ __device__ __forceinline__ void token_down_slot(const MoeParams& p, int q, int m
   const uint8_t* tile =
       (sh ? p.sdn : p.dn + (int64_t)e * p.dn_mat_bytes) + (int64_t)t * kTileBytes;
   const float g = sh ? p.sdn_g[0] : p.dn_g[e];
+  if constexpr (LIC == 0) {
+    if (p.QI > 1 || L < 8) {  // any row width, any number of panels
+      float v[8];
+      panels_dot_f32<0>(sh ? p.sdn : p.dn + (int64_t)e * p.dn_mat_bytes, t, p.QI, p.KpI, p.hp,
+                        p.I, pair, lane, L, v);
+      if (reduced_writer_rt(lane, L))
+        for (int j = 0; j < reduced_values(L); ++j) ys[q][reduced_row_v(lane, L, j)] = v[j] * g;
+      return;
+    }
+  }
   TileRegs T;
   float hr[1][32];
   load_tile(tile, lane, T);
@@ -644,7 +726,7 @@ __device__ __forceinline__ void token_down_slot(const MoeParams& p, int q, int m
 
 template <int LIC, int SPW>
 __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel(MoeParams p) {
-  __shared__ float ys[kMaxTopK + 1][64];
+  __shared__ float ys[kMaxTopK + 1][LIC ? 512 / LIC : 512];  // a down tile's rows per slot
   const int wave = threadIdx.x >> 6;
   if ((int)blockIdx.x < p.proj_blocks) {  // the projection's 16-row blocks of W_p (>= 4 waves)
     __shared__ f32x4 ppart[kGemmDenseWaves - 1][64];
@@ -653,9 +735,9 @@ __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel
     return;
   }
   const int b = xcd_block((int)blockIdx.x - p.proj_blocks, (int)gridDim.x - p.proj_blocks);
-  const int m = b / p.P, t = b % p.P;
+  const int m = b / p.PD, t = b % p.PD;
   const int L = LIC ? LIC : p.LI;
-  const int rpt = 16384 / p.I;  // output rows of a down tile
+  const int rpt = p.RI;  // output rows of a down tile
   // SPW slots per wave: one up to eight slots; with the shared expert beside
   // eight routed ones a wave takes two (q = wave, wave + waves), so that a
   // block of five waves leaves room for three blocks per CU where nine waves
@@ -668,8 +750,9 @@ __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel
     if (wave + waves < p.k + p.has_shared) token_down_slot<LIC>(p, wave + waves, m, t, L, ys);
   }
   __syncthreads();
-  if ((int)threadIdx.x < rpt) {
-    const int r = threadIdx.x;
+  // the tile's output rows (past H in a ragged last row block: none)
+  const int nrows = min(rpt, p.H - t * rpt);
+  for (int r = (int)threadIdx.x; r < nrows; r += (int)blockDim.x) {
     const int64_t o = (int64_t)m * p.H + t * rpt + r;
     float acc = 0.0f;
 #pragma unroll

@@ -38,9 +38,10 @@ __device__ __forceinline__ void opaque_tile(TileRegs& t) {
   asm volatile("" : "+v"(t.scales.x), "+v"(t.scales.y), "+v"(t.scales.z), "+v"(t.scales.w));
 }
 
-// part[r][i] = sum over the lane's 32 columns of slab i of W * x_r (no g).
+// part[r][i] = sum over the lane's 32 columns of slab i of W * x_r (no g);
+// ACC: added to part[r][i] instead (the panels of one row block).
 // x[r] holds the row's 32 BF16 values of the lane's columns as 4 x uint4.
-template <int R>
+template <int R, bool ACC = false>
 __device__ __forceinline__ void tile_dot_bf16(const TileRegs& t, const uint4 (&x)[R][4],
                                               float (&part)[R][8]) {
 #pragma unroll
@@ -61,7 +62,7 @@ __device__ __forceinline__ void tile_dot_bf16(const TileRegs& t, const uint4 (&x
       for (int p = 8; p < 16; ++p)
         a1 = __builtin_amdgcn_fdot2_f32_bf16(w[p], as_bf16x2(u4_get(x[r][p >> 2], p & 3)), a1,
                                              false);
-      part[r][i] = a0 * s0 + a1 * s1;
+      part[r][i] = ACC ? part[r][i] + (a0 * s0 + a1 * s1) : a0 * s0 + a1 * s1;
     }
     // keep each slab's decode next to its use (no hoisting of all decodes)
     __builtin_amdgcn_sched_barrier(0);
@@ -69,7 +70,7 @@ __device__ __forceinline__ void tile_dot_bf16(const TileRegs& t, const uint4 (&x
 }
 
 // Same with FP32 activation rows: h[r] = 32 FP32 values of the lane's columns.
-template <int R>
+template <int R, bool ACC = false>
 __device__ __forceinline__ void tile_dot_f32(const TileRegs& t, const float (&h)[R][32],
                                              float (&part)[R][8]) {
 #pragma unroll
@@ -92,7 +93,7 @@ __device__ __forceinline__ void tile_dot_f32(const TileRegs& t, const float (&h)
         a1 = __builtin_fmaf(w[p][0], h[r][2 * p], a1);
         a1 = __builtin_fmaf(w[p][1], h[r][2 * p + 1], a1);
       }
-      part[r][i] = a0 * s0 + a1 * s1;
+      part[r][i] = ACC ? part[r][i] + (a0 * s0 + a1 * s1) : a0 * s0 + a1 * s1;
     }
     __builtin_amdgcn_sched_barrier(0);
   }

@@ -46,7 +46,14 @@ def test_packed_bytes(m):
     assert m.nvfp4_packed_bytes(256, 1024, 2048) == 256 * 128 * 9216 + 1024
     assert m.nvfp4_packed_bytes(256, 2048, 512) == 256 * 64 * 9216 + 1024
     assert m.nvfp4_packed_bytes(1, 33, 512) == 2 * 9216 + 256     # ragged rows pad
-    for K in (16, 48, 96, 4096, 0):
+    # K % 32 == 0 in general: Q = K / Kp panels of Kp = the largest 32 * 2^j <= 2048
+    # dividing K; a row block is Q tiles of 16384 / Kp rows
+    assert m.nvfp4_packed_bytes(1, 600, 96) == 2 * 3 * 9216 + 256      # Kp 32: 512 rows
+    assert m.nvfp4_packed_bytes(1, 512, 1536) == 16 * 3 * 9216 + 256   # Kp 512: 32 rows
+    assert m.nvfp4_packed_bytes(1, 17, 3072) == 2 * 3 * 9216 + 256     # Kp 1024: 16 rows
+    assert m.nvfp4_packed_bytes(2, 2048, 4096) == 2 * 256 * 2 * 9216 + 256  # Kp 2048
+    assert m.nvfp4_packed_bytes(1, 8, 65536) == 32 * 9216 + 256
+    for K in (16, 48, 100, 65568, 0):
         assert m.lib.nvfp4_packed_bytes(1, 8, K) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert m.lib.nvfp4_packed_bytes(0, 8, 64) == m.NVFP4MOE_ERR_BAD_SHAPE
 
@@ -55,10 +62,12 @@ def test_validation_errors_before_launch(m):
     L = m.lib
     fake = 4096  # never dereferenced: every call below fails validation first
     assert L.nvfp4_pack(None, fake, fake, 1, 8, 64, fake, None) == m.NVFP4MOE_ERR_NULL_ARG
-    assert L.nvfp4_pack(fake, fake, fake, 1, 8, 96, fake, None) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert L.nvfp4_pack(fake, fake, fake, 1, 8, 80 + 8, fake, None) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert L.nvfp4_dequant_f32(fake, 1, 8, 64, 1, 2, fake, None) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert L.nvfp4_skinny_gemm(fake, 0, 64, fake, 8, fake, None) == m.NVFP4MOE_ERR_BAD_SHAPE
-    assert L.nvfp4_skinny_gemm(fake, 1, 4096, fake, 8, fake, None) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert L.nvfp4_skinny_gemm(fake, 1, 4100, fake, 8, fake, None) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert L.nvfp4_skinny_gemm(fake, 1, 1 << 17, fake, 8, fake, None) == \
+        m.NVFP4MOE_ERR_UNSUPPORTED
     assert L.nvfp4_skinny_gemm(fake + 2, 1, 64, fake, 8, fake, None) == \
         m.NVFP4MOE_ERR_UNSUPPORTED  # misaligned x
     assert L.fp8_skinny_gemm(None, 1, 2048, fake, fake, 8, fake, None) == m.NVFP4MOE_ERR_NULL_ARG
@@ -136,11 +145,14 @@ def test_decode_validation(m):
     assert dec(_args(m, M=0)) == m.NVFP4MOE_ERR_BAD_SHAPE
     assert dec(_args(m, E=300)) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert dec(_args(m, k=9)) == m.NVFP4MOE_ERR_UNSUPPORTED
-    assert dec(_args(m, H=3000)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    assert dec(_args(m, H=3000)) == m.NVFP4MOE_ERR_UNSUPPORTED  # not a multiple of 32
     assert dec(_args(m, I=100)) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert dec(_args(m, H=2048, I=4)) == m.NVFP4MOE_ERR_UNSUPPORTED
-    assert dec(_args(m, H=128, I=256)) == m.NVFP4MOE_ERR_UNSUPPORTED  # below 256
-    assert dec(_args(m, H=256, I=128)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    # the up half of gate_up must start on a row block: I % (16384 / panel_k(H)) == 0
+    assert dec(_args(m, H=96, I=256)) == m.NVFP4MOE_ERR_UNSUPPORTED  # 512-row blocks
+    assert "row block" in m.last_error_detail()
+    assert dec(_args(m, H=1536, I=48)) == m.NVFP4MOE_ERR_UNSUPPORTED  # 32-row blocks
+    assert dec(_args(m, H=1 << 17)) == m.NVFP4MOE_ERR_UNSUPPORTED
     need = m.moe_nvfp4_workspace_bytes(4, 256, 8, 2048, 512, False)
     assert dec(_args(m, workspace_bytes=need - 1)) == m.NVFP4MOE_ERR_WORKSPACE
     assert "workspace" in m.last_error_detail()

@@ -36,7 +36,9 @@ def _all_codes_all_scales(G, N, K, gvals, seed=0):
 
 
 @pytest.mark.parametrize("K,N", [(2048, 8), (2048, 11), (512, 33), (64, 300), (32, 513),
-                                 (1024, 16), (128, 128)])
+                                 (1024, 16), (128, 128),
+                                 # several panels: K = 3 x 32, 5 x 32, 3 x 512, 3 x 1024, 2 x 2048
+                                 (96, 700), (160, 513), (1536, 40), (3072, 17), (4096, 9)])
 @pytest.mark.parametrize("path", [0, 1])
 def test_dequant_bit_exact_every_code_and_scale(m, gpu, K, N, path):
     nv = _all_codes_all_scales(3, N, K, [1.0, 2.0 ** -9, 0.37], seed=K + N)
@@ -71,7 +73,12 @@ def test_dequant_random_tensor(m, gpu):
                                      (16, 2048, 100, 0.37), (17, 2048, 40, 1.0),
                                      (33, 2048, 17, 2.0 ** -9), (6, 2048, 4104, 1.0),
                                      # K split over four waves: N <= 4096, M <= 16
-                                     (12, 2048, 4096, 1.0), (7, 2048, 1, 0.5)])
+                                     (12, 2048, 4096, 1.0), (7, 2048, 1, 0.5),
+                                     # K % 32 == 0 beyond powers of two (several panels)
+                                     (1, 96, 600, 1.0), (3, 96, 1025, 0.5), (9, 160, 70, 1.0),
+                                     (1, 1536, 512, 2.0 ** -8), (5, 3072, 300, 2.0 ** -9),
+                                     (6, 4096, 2048, 2.0 ** -9), (17, 4096, 33, 1.0),
+                                     (2, 2016, 40, 1.0), (8, 6144, 100, 2.0 ** -9)])
 def test_skinny_gemm(m, gpu, M, K, N, g):
     x, w = dense_skinny(seed=0, M=M, K=K, N=N, g=g)
     pw = pack(w, gpu, m)
@@ -215,6 +222,42 @@ def test_moe_route_decode_with_projection(m, gpu, M, k, shared, N):
     assert torch.equal(ids0, ids1) and torch.equal(w0.view(torch.int32), w1.view(torch.int32))
     pref = oracle.gemm(lay.x, pw_h.codes[0], pw_h.scales[0], float(pw_h.g[0]))
     assert tol_ratio(dev_bf16_to_f64(py), pref) <= 1.0
+
+
+@pytest.mark.parametrize("M,E,H,I,k,shared,resid", [
+    (4, 16, 1536, 768, 8, True, True),     # gate 3 panels of 512, down 3 panels of 256
+    (3, 8, 96, 512, 2, True, False),       # gate one chunk per row and panel (L = 1), 3 panels
+    (5, 8, 160, 512, 4, False, True),      # 5 panels of 32; down rows past H in the last block
+    (6, 16, 2560, 1408, 8, True, False),   # down 11 panels of 128 (L = 4: two rows a lane)
+    (2, 4, 4096, 1024, 2, False, True),    # gate 2 panels of 2048
+    (20, 8, 1536, 768, 4, True, True),     # more rows: the expert-major launches
+    (40, 4, 96, 512, 2, True, False),
+    (3, 8, 128, 256, 2, False, True)])     # one panel of 128: four lanes a row (L = 4)
+@pytest.mark.parametrize("entry", ["decode", "decode3", "route_decode"])
+def test_moe_block_panel_shapes(m, gpu, M, E, H, I, k, shared, resid, entry):
+    """H and I that are multiples of 32 but not powers of two up to 2048 (the
+    matrices split into several panels, some with fewer than eight lanes per
+    row): every schedule against the oracle, every element."""
+    lay = moe_layer(seed=M + H + I, wl=208, M=M, E_=E, H_=H, I_=I, k=k, shared=shared,
+                    bias=shared)
+    residual = synth.normal_bf16(synth.key(5, 209, M), (M, H)) if resid else None
+    d = upload_layer(lay, gpu, m)
+    res = None if residual is None else to_dev_bf16(residual, gpu)
+    if entry == "route_decode":
+        out, ids_d, w_d = m.moe_nvfp4_route_decode(d["x"], d["logits"], k, d["gu"], d["dn"],
+                                                   d["bias"], d["sgu"], d["sdn"], residual=res)
+        torch.cuda.synchronize()
+        ids, w = oracle.route_topk(lay.logits, k, lay.bias)
+        assert (ids_d.cpu().numpy() == ids).all()
+    else:
+        r, got = _run_block(m, gpu, lay, residual, schedule=3 if entry == "decode3" else 0)
+        ids, w = oracle.route_topk(lay.logits, k, lay.bias)
+        check_routing_exact(r, ids, w, E)
+    if entry == "route_decode":
+        got = dev_bf16_to_f64(out)
+    ref = oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down, lay.shared_gate_up,
+                           lay.shared_down, residual)
+    assert tol_ratio(got, ref) <= 1.0
 
 
 @pytest.mark.parametrize("M,E,k,shared,resid,dense_min_rows", [
