@@ -59,6 +59,9 @@ int32_t launched(const char* what) {
 // K of a packed matrix: a multiple of 32 (whole chunks), at most kMaxK.
 constexpr int64_t kMaxK = 65536;
 bool valid_k(int64_t K) { return K >= 32 && K <= kMaxK && K % 32 == 0; }
+// Bounds that keep every size product of a packed tensor inside int64_t.
+constexpr int64_t kMaxG = (int64_t)1 << 20;
+constexpr int64_t kMaxN = (int64_t)1 << 32;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -337,6 +340,9 @@ const char* nvfp4moe_version(void) { return "nvfp4moe 0.1 gfx950"; }
 
 int64_t nvfp4_packed_bytes(int64_t G, int64_t N, int64_t K) {
   if (G < 1 || N < 1) return fail(NVFP4MOE_ERR_BAD_SHAPE, "G and N must be >= 1");
+  if (G > kMaxG || N > kMaxN)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "G <= %lld and N <= %lld", (long long)kMaxG,
+                (long long)kMaxN);
   if (!valid_k(K))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "K = %lld: need a multiple of 32 in [32, %lld]",
                 (long long)K, (long long)kMaxK);
