@@ -33,7 +33,7 @@ __global__ void __launch_bounds__(128, 4) fused_route_gate_kernel(MoeParams p,
   const int m = sh ? item - npairs : item / p.k;
   const int L = LHC ? LHC : p.LH;
   uint4 xr[1][4];
-  load_x_bf16(p.x, p.H, m, true, 32 * (lane % L), xr[0]);
+  load_x_bf16(p.x, p.H, m, 32 * (lane % L), xr[0]);
   int e = 0;
   if (!sh) {
     int my_id;

@@ -39,7 +39,10 @@ __device__ __forceinline__ void gemm_rows(const TileRegs& T, const uint16_t* __r
                                           uint16_t* __restrict__ y) {
   uint4 xr[R][4];
 #pragma unroll
-  for (int r = 0; r < R; ++r) load_x_bf16(x, K, m0 + r, r < rows, col0, xr[r]);
+  for (int r = 0; r < R; ++r) {
+    if (r < rows) load_x_bf16(x, K, m0 + r, col0, xr[r]);
+    else for (int j = 0; j < 4; ++j) xr[r][j] = make_uint4(0, 0, 0, 0);
+  }
   float part[R][8];
   tile_dot_bf16<R>(T, xr, part);
   gemm_write<L, R>(part, m0, rows, lane, tile, N, g, y);
@@ -61,7 +64,10 @@ __device__ __forceinline__ void gemm_rows_panels(const uint8_t* __restrict__ blk
   for (int64_t q = 0; q < Q; ++q) {
     uint4 xr[R][4];
 #pragma unroll
-    for (int r = 0; r < R; ++r) load_x_bf16(x, K, m0 + r, r < rows, q * (L * 32) + col0, xr[r]);
+    for (int r = 0; r < R; ++r) {
+      if (r < rows) load_x_bf16(x, K, m0 + r, q * (L * 32) + col0, xr[r]);
+      else for (int j = 0; j < 4; ++j) xr[r][j] = make_uint4(0, 0, 0, 0);
+    }
     TileRegs T;
     load_tile(blk_tiles + q * kTileBytes, lane, T);
     tile_dot_bf16<R, true>(T, xr, acc);
@@ -143,14 +149,15 @@ constexpr int64_t kGemmDenseMaxBlocks = 512;
 __device__ __forceinline__ void load_gemm_block(const uint8_t* __restrict__ w, int64_t ntiles,
                                                 int64_t blk, int m, int grp, DenseRows<16>& d) {
   const int64_t t = 2 * blk + (m >> 3);  // this lane's tile
+  const bool valid = t < ntiles;
+  const uint8_t* tile = w + (valid ? t : ntiles - 1) * kTileBytes;  // always issued
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
-    if (t < ntiles) {
-      load_dense_chunk(w + t * kTileBytes, 64, m & 7, 4 * q + grp, d.c[q], d.s[q]);
-    } else {
-      d.c[q] = make_uint4(0, 0, 0, 0);
-      d.s[q] = 0u;
-    }
+    uint4 c;
+    uint32_t sc;
+    load_dense_chunk(tile, 64, m & 7, 4 * q + grp, c, sc);
+    d.c[q] = valid ? c : make_uint4(0, 0, 0, 0);
+    d.s[q] = valid ? sc : 0u;
   }
 }
 
@@ -235,15 +242,18 @@ __device__ __forceinline__ void splitk_block(const uint16_t* __restrict__ x, int
   f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   if (wave < kGemmDenseWaves) {
     DenseRows<4> d;
+    // every load is issued (past the last tile or row: the last one, zeroed
+    // after the load), so the compiler counts the loads in flight exactly
+    const bool tvalid = t < ntiles;
+    const uint8_t* tile = w + (tvalid ? t : ntiles - 1) * kTileBytes;
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int q = 4 * wave + qq;
-      if (t < ntiles) {
-        load_dense_chunk(w + t * kTileBytes, 64, m & 7, 4 * q + grp, d.c[qq], d.s[qq]);
-      } else {
-        d.c[qq] = make_uint4(0, 0, 0, 0);
-        d.s[qq] = 0u;
-      }
+      uint4 c;
+      uint32_t sc;
+      load_dense_chunk(tile, 64, m & 7, 4 * q + grp, c, sc);
+      d.c[qq] = tvalid ? c : make_uint4(0, 0, 0, 0);
+      d.s[qq] = tvalid ? sc : 0u;
     }
     // x row m, pieces 4 (4 q + grp) + e of 16 bytes (8 BF16), q in this wave's quarter
     uint4 xv[4][4];
@@ -251,8 +261,10 @@ __device__ __forceinline__ void splitk_block(const uint16_t* __restrict__ x, int
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        xv[qq][e] = valid ? xrow[4 * (4 * (4 * wave + qq) + grp) + e] : make_uint4(0, 0, 0, 0);
+      for (int e = 0; e < 4; ++e) {
+        const uint4 v = xrow[4 * (4 * (4 * wave + qq) + grp) + e];
+        xv[qq][e] = valid ? v : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       bf16x8 a[4];

@@ -94,8 +94,10 @@ struct PairCache {
 __device__ __forceinline__ void load_pair_cache(const MoeParams& p, int lane, PairCache& c) {
   const int n = p.M * p.k;
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    c.v[q] = (q < p.pair_regs && q * 64 + lane < n) ? p.pairs[q * 64 + lane] : 0;
+  for (int q = 0; q < 2; ++q) {
+    const int idx = q * 64 + lane;
+    c.v[q] = p.pairs[idx < n ? idx : n - 1];  // read only below n, and only if pair_regs
+  }
 }
 
 // Reads another lane's register: call with every lane of the wave active (in
@@ -179,7 +181,7 @@ __device__ __forceinline__ void panels_dot_bf16(const uint8_t* mat, int rb, int 
 #pragma unroll 1
   for (int q = 0; q < Q; ++q) {
     uint4 xr[1][4];
-    load_x_bf16(x, ldx, xrow, true, q * Kp + 32 * (lane % L), xr[0]);
+    load_x_bf16(x, ldx, xrow, q * Kp + 32 * (lane % L), xr[0]);
     TileRegs T;
     load_tile(mat + ((int64_t)rb * Q + q) * kTileBytes, lane, T);
     tile_dot_bf16<1, true>(T, xr, acc);
@@ -197,7 +199,7 @@ __device__ __forceinline__ void panels_dot_f32(const uint8_t* mat, int rb, int Q
 #pragma unroll 1
   for (int q = 0; q < Q; ++q) {
     float hr[1][32];
-    load_h_f32(h, ldh, hrow, true, q * Kp + 32 * (lane % L), hr[0]);
+    load_h_f32(h, ldh, hrow, q * Kp + 32 * (lane % L), hr[0]);
     TileRegs T;
     load_tile(mat + ((int64_t)rb * Q + q) * kTileBytes, lane, T);
     tile_dot_f32<1, true>(T, hr, acc);
@@ -207,7 +209,9 @@ __device__ __forceinline__ void panels_dot_f32(const uint8_t* mat, int rb, int Q
   reduce_slabs_rt<LC>(v, lane, L);
 }
 
-// Pair ids and activation rows r0 .. r0 + R - 1 of a slot (rows past `rows` are zero).
+// Pair ids and activation rows r0 .. r0 + R - 1 of a slot (rows past `rows`:
+// zeros, not loaded; `rows` is the same in every lane, so the branch is the
+// wave's, and the batch's products wait for every load of it anyway).
 template <int R>
 __device__ __forceinline__ void load_rows(const MoeParams& p, const SlotInfo& s,
                                           const PairCache& c, int r0, int rows, int col0,
@@ -215,7 +219,12 @@ __device__ __forceinline__ void load_rows(const MoeParams& p, const SlotInfo& s,
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     pr[r] = r < rows ? slot_pair(p, s, r0 + r, c) : 0;
-    load_x_bf16(p.x, p.H, pair_xrow(p, pr[r]), r < rows, col0, xr[r]);
+    if (r < rows) {
+      load_x_bf16(p.x, p.H, pair_xrow(p, pr[r]), col0, xr[r]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xr[r][j] = make_uint4(0, 0, 0, 0);
+    }
   }
 }
 

@@ -20,9 +20,12 @@
 
 namespace nvfp4moe {
 
-// Pair index (row of h / y) of row r of a slot, per lane.
+// Pair index (row of h / y) of row r of a slot, per lane; rows past the
+// slot's last (padding, never written; s.rows >= 1) repeat it, so that every
+// lane issues its load (see load_x_bf16).
 __device__ __forceinline__ int lane_pair(const MoeParams& p, const SlotInfo& s, int r) {
-  return s.shared ? p.M * p.k + r : p.pairs[s.row_begin + r];
+  const int rc = r < s.rows ? r : s.rows - 1;
+  return s.shared ? p.M * p.k + rc : p.pairs[s.row_begin + rc];
 }
 
 // Slot of a tile item: the shared expert (if any) comes first, so that its
@@ -53,20 +56,23 @@ __device__ __forceinline__ bool ordered_slot_info(const MoeParams& p, int item, 
     if (item == 0) return slot_info(p, p.routed_slots, s);
     item -= 1;
   }
-  const int na = *p.n_active;
+  // active[E] and active_offsets[E + 1] are written in full (unused slots:
+  // expert -1), so every entry is read at once, without waiting for n_active
+  const int E = p.E;
   int ao[5], ex[4], cls[4];
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
     const int sl = 4 * lane + j;
-    ao[j] = sl <= na ? p.active_offsets[sl] : 0;
+    const int v = p.active_offsets[sl <= E ? sl : E];
+    ao[j] = sl <= E ? v : 0;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int sl = 4 * lane + j;
-    ex[j] = sl < na ? p.active[sl] : -1;
-    cls[j] = sl < na ? row_class(ao[j + 1] - ao[j]) : -1;
+    const int v = p.active[sl < E ? sl : E - 1];
+    ex[j] = sl < E ? v : -1;
+    cls[j] = ex[j] >= 0 ? row_class(ao[j + 1] - ao[j]) : -1;
   }
-  if (item >= na) return false;
   const int cmax = (int)wave_max_u32_all((uint32_t)(max(max(cls[0], cls[1]), max(cls[2], cls[3])) + 1)) - 1;
   int base = 0;
 #pragma unroll 1
@@ -212,8 +218,9 @@ __device__ __forceinline__ void staged_gate_dense(const MoeParams& p, const Slot
 #pragma unroll
     for (int b = 0; b < NCB; ++b) {
       const int r = cb0 + 16 * b + m;
-      pr[b] = r < s.rows ? lane_pair(p, s, r) : -1;
-      xrow[b] = pr[b] < 0 ? 0 : pair_xrow(p, pr[b]);
+      const int lp = lane_pair(p, s, r);
+      pr[b] = r < s.rows ? lp : -1;
+      xrow[b] = pair_xrow(p, lp);
     }
     f32x4 acc[NCB];
 #pragma unroll
@@ -226,7 +233,7 @@ __device__ __forceinline__ void staged_gate_dense(const MoeParams& p, const Slot
 #pragma unroll
         for (int b = 0; b < NCB; ++b) {
           uint4 xv[4];
-          load_x_bf16(p.x, p.H, xrow[b], pr[b] >= 0, 32 * (4 * q + grp), xv);
+          load_x_bf16(p.x, p.H, xrow[b], 32 * (4 * q + grp), xv);
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[b] = mfma_bf16(a[e], as_bf16x8(xv[e]), acc[b]);
         }
@@ -238,13 +245,13 @@ __device__ __forceinline__ void staged_gate_dense(const MoeParams& p, const Slot
       for (int q = 0; q < AHEAD; ++q)
 #pragma unroll
         for (int b = 0; b < NCB; ++b)
-          load_x_bf16(p.x, p.H, xrow[b], pr[b] >= 0, 32 * (4 * q + grp), xb[q][b]);
+          load_x_bf16(p.x, p.H, xrow[b], 32 * (4 * q + grp), xb[q][b]);
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         if (q + AHEAD < 16) {
 #pragma unroll
           for (int b = 0; b < NCB; ++b)
-            load_x_bf16(p.x, p.H, xrow[b], pr[b] >= 0, 32 * (4 * (q + AHEAD) + grp),
+            load_x_bf16(p.x, p.H, xrow[b], 32 * (4 * (q + AHEAD) + grp),
                         xb[(q + AHEAD) % (AHEAD + 1)][b]);
         }
         bf16x8 a[4];
@@ -359,8 +366,8 @@ __device__ __forceinline__ void staged_gate_dense_halves(const MoeParams& p, con
                                                          int j, float g, f32x4* dred) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 15, grp = lane >> 4;
   const bool valid = m < s.rows;
-  const int pr = valid ? lane_pair(p, s, m) : -1;
-  const int xrow = valid ? pair_xrow(p, pr) : 0;
+  const int pr = lane_pair(p, s, m);
+  const int xrow = pair_xrow(p, pr);
   const uint8_t* tile = m < 8 ? tg : tu;
   const int q0 = 8 * wave;
   DenseRows<RING + 1> d;
@@ -368,7 +375,7 @@ __device__ __forceinline__ void staged_gate_dense_halves(const MoeParams& p, con
 #pragma unroll
   for (int q = 0; q < RING; ++q) {
     load_dense_chunk(tile, 64, m & 7, 4 * (q0 + q) + grp, d.c[q], d.s[q]);
-    load_x_bf16(p.x, p.H, xrow, valid, 32 * (4 * (q0 + q) + grp), xv[q]);
+    load_x_bf16(p.x, p.H, xrow, 32 * (4 * (q0 + q) + grp), xv[q]);
   }
   f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -376,7 +383,7 @@ __device__ __forceinline__ void staged_gate_dense_halves(const MoeParams& p, con
     if (q + RING < 8) {
       const int r = (q + RING) % (RING + 1);
       load_dense_chunk(tile, 64, m & 7, 4 * (q0 + q + RING) + grp, d.c[r], d.s[r]);
-      load_x_bf16(p.x, p.H, xrow, valid, 32 * (4 * (q0 + q + RING) + grp), xv[r]);
+      load_x_bf16(p.x, p.H, xrow, 32 * (4 * (q0 + q + RING) + grp), xv[r]);
     }
     const int c = q % (RING + 1);
     bf16x8 a[4];
@@ -483,7 +490,12 @@ __device__ __forceinline__ void staged_load_h(const MoeParams& p, const SlotInfo
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     pr[r] = r < rows ? slot_pair(p, s, r0 + r, c) : 0;
-    load_h_f32(p.hp, p.I, pr[r], r < rows, col0, hr[r]);
+    if (r < rows) {
+      load_h_f32(p.hp, p.I, pr[r], col0, hr[r]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) hr[r][j] = 0.0f;
+    }
   }
 }
 
@@ -532,11 +544,12 @@ __device__ __forceinline__ void staged_down_dense(const MoeParams& p, const Slot
   for (int cb0 = 0; cb0 < s.rows; cb0 += 16 * NCB) {
     opaque_dense<4>(d[0]);
     opaque_dense<4>(d[1]);
-    int pr[NCB];
+    int pr[NCB], hrow[NCB];
 #pragma unroll
     for (int b = 0; b < NCB; ++b) {
       const int r = cb0 + 16 * b + m;
-      pr[b] = r < s.rows ? lane_pair(p, s, r) : -1;
+      hrow[b] = lane_pair(p, s, r);  // padding lanes: their D columns are not written
+      pr[b] = r < s.rows ? hrow[b] : -1;
     }
     f32x4 acc[2][NCB];
 #pragma unroll
@@ -550,17 +563,14 @@ __device__ __forceinline__ void staged_down_dense(const MoeParams& p, const Slot
       dense_a<4>(d[1], q, a[1]);
 #pragma unroll
       for (int b = 0; b < NCB; ++b) {
-        // the lane's 32 h values of chunk column q: 8 words per operand pair
+        // the lane's 32 h values of chunk column q (8 words per operand
+        // pair), all requested before the first product that needs them
         uint4 hv[8];
-        if (pr[b] >= 0) {
-          const uint4* src =
-              reinterpret_cast<const uint4*>(hw + (int64_t)pr[b] * p.I + 32 * (4 * q + grp));
+        const uint4* src =
+            reinterpret_cast<const uint4*>(hw + (int64_t)hrow[b] * p.I + 32 * (4 * q + grp));
 #pragma unroll
-          for (int v = 0; v < 8; ++v) hv[v] = src[v];
-        } else {
-#pragma unroll
-          for (int v = 0; v < 8; ++v) hv[v] = make_uint4(0, 0, 0, 0);
-        }
+        for (int v = 0; v < 8; ++v) hv[v] = src[v];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           bf16x8 hi, lo;
@@ -571,6 +581,7 @@ __device__ __forceinline__ void staged_down_dense(const MoeParams& p, const Slot
             acc[rb][b] = mfma_bf16(a[rb][e], lo, acc[rb][b]);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
@@ -717,7 +728,7 @@ __device__ __forceinline__ void token_down_slot(const MoeParams& p, int q, int m
   TileRegs T;
   float hr[1][32];
   load_tile(tile, lane, T);
-  load_h_f32(p.hp, p.I, pair, true, 32 * (lane % L), hr[0]);
+  load_h_f32(p.hp, p.I, pair, 32 * (lane % L), hr[0]);
   float part[1][8];
   tile_dot_f32<1>(T, hr, part);
   reduce_slabs_rt<LIC>(part[0], lane, L);

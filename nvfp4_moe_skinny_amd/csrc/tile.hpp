@@ -99,34 +99,30 @@ __device__ __forceinline__ void tile_dot_f32(const TileRegs& t, const float (&h)
   }
 }
 
-// Loads the lane's 32 BF16 columns of activation row `row` (or zeros).
-__device__ __forceinline__ void load_x_bf16(const uint16_t* x, int64_t ld, int64_t row, bool valid,
-                                            int col0, uint4 (&xr)[4]) {
-  if (valid) {
-    const uint4* p = reinterpret_cast<const uint4*>(x + row * ld + col0);
+// Loads the lane's 32 BF16 columns of activation row `row`. Callers pad a
+// batch with a row that exists (results of padding rows are never written,
+// and in these products no output reads another row's activations) rather
+// than skip the load: a load under a branch leaves the compiler unable to
+// count the loads in flight where the paths join, and its waits then also
+// cover every load issued after it, prefetches included.
+__device__ __forceinline__ void load_x_bf16(const uint16_t* x, int64_t ld, int64_t row, int col0,
+                                            uint4 (&xr)[4]) {
+  const uint4* p = reinterpret_cast<const uint4*>(x + row * ld + col0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xr[j] = p[j];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xr[j] = make_uint4(0, 0, 0, 0);
-  }
+  for (int j = 0; j < 4; ++j) xr[j] = p[j];
 }
 
-__device__ __forceinline__ void load_h_f32(const float* h, int64_t ld, int64_t row, bool valid,
-                                           int col0, float (&hr)[32]) {
-  if (valid) {
-    const float4* p = reinterpret_cast<const float4*>(h + row * ld + col0);
+// The lane's 32 FP32 columns of h row `row` (padding as for load_x_bf16).
+__device__ __forceinline__ void load_h_f32(const float* h, int64_t ld, int64_t row, int col0,
+                                           float (&hr)[32]) {
+  const float4* p = reinterpret_cast<const float4*>(h + row * ld + col0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float4 v = p[j];
-      hr[4 * j] = v.x;
-      hr[4 * j + 1] = v.y;
-      hr[4 * j + 2] = v.z;
-      hr[4 * j + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) hr[j] = 0.0f;
+  for (int j = 0; j < 8; ++j) {
+    const float4 v = p[j];
+    hr[4 * j] = v.x;
+    hr[4 * j + 1] = v.y;
+    hr[4 * j + 2] = v.z;
+    hr[4 * j + 3] = v.w;
   }
 }
 
