@@ -193,6 +193,23 @@ __device__ __forceinline__ void staged_gate_rows(const MoeParams& p, const SlotI
   staged_gate_math<LC, R>(p, TG, TU, xr, pr, rows, j, g, L);
 }
 
+// The first batch of R rows: its activation rows are requested before the
+// tiles, and its slabs are multiplied as they arrive (no wait for the whole
+// tiles). TG / TU keep the tiles for the later batches.
+template <int LC, int R>
+__device__ __forceinline__ void staged_gate_first(const MoeParams& p, const SlotInfo& s,
+                                                  const PairCache& c, const uint8_t* tg,
+                                                  const uint8_t* tu, int rows, int j, float g,
+                                                  int L, TileRegs& TG, TileRegs& TU) {
+  int pr[R];
+  uint4 xr[R][4];
+  load_rows<R>(p, s, c, 0, rows, 32 * ((int)threadIdx.x % L), pr, xr);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile_pair(tg, tu, (int)threadIdx.x, TG, TU);
+  __builtin_amdgcn_sched_barrier(0);
+  staged_gate_math<LC, R>(p, TG, TU, xr, pr, rows, j, g, L);
+}
+
 // MFMA (H = 2048: a gate tile and an up tile hold 8 rows each, together one
 // 16-row block): h packed as hi / lo BF16 for the dense down product.
 // AHEAD: chunk columns of x requested ahead of the one being multiplied (a
@@ -315,17 +332,17 @@ __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_gate_kernel(MoeP
     }
   }
   TileRegs TG, TU;
-  // the first batch's activation rows are requested before the tiles, and
-  // its slabs are multiplied as they arrive (no wait for the whole tiles)
+  // the first batch is sized to the slot's rows (1, 2 or RMAX): the products
+  // of padding rows are as dear as real ones, and most slots of a many-row
+  // step hold a row or two (M = 256: three of four VALU slots)
   {
     const int rows0 = s.rows < RMAX ? s.rows : RMAX;
-    int pr[RMAX];
-    uint4 xr[RMAX][4];
-    load_rows<RMAX>(p, s, pc, 0, rows0, 32 * (lane % L), pr, xr);
-    __builtin_amdgcn_sched_barrier(0);
-    load_tile_pair(tg, tu, lane, TG, TU);
-    __builtin_amdgcn_sched_barrier(0);
-    staged_gate_math<LHC, RMAX>(p, TG, TU, xr, pr, rows0, j, g, L);
+    if (RMAX >= 4 && rows0 > 2)
+      staged_gate_first<LHC, RMAX>(p, s, pc, tg, tu, rows0, j, g, L, TG, TU);
+    else if (RMAX >= 2 && rows0 == 2)
+      staged_gate_first<LHC, (RMAX >= 2 ? 2 : 1)>(p, s, pc, tg, tu, rows0, j, g, L, TG, TU);
+    else
+      staged_gate_first<LHC, 1>(p, s, pc, tg, tu, rows0, j, g, L, TG, TU);
   }
 #pragma unroll 1
   for (int r0 = RMAX; r0 < s.rows; r0 += RMAX) {
@@ -527,6 +544,19 @@ __device__ __forceinline__ void staged_down_rows(const MoeParams& p, const SlotI
   staged_down_math<LC, R>(p, T, pr, hr, rows, t, g, L);
 }
 
+// The first batch of R rows: h is complete (the gate_up launch has ended), so
+// its rows go out with the tile and its slabs are multiplied as they arrive.
+template <int LC, int R>
+__device__ __forceinline__ void staged_down_first(const MoeParams& p, const SlotInfo& s,
+                                                  const PairCache& c, const uint8_t* tile,
+                                                  int rows, int t, float g, int L, TileRegs& T) {
+  int pr[R];
+  float hr[R][32];
+  load_tile(tile, (int)threadIdx.x, T);
+  staged_load_h<R>(p, s, c, 0, rows, L, pr, hr);
+  staged_down_math<LC, R>(p, T, pr, hr, rows, t, g, L);
+}
+
 // MFMA (I = 512: a down tile holds 32 rows, two 16-row blocks; K = 512 is 4
 // chunk columns per lane group).
 template <int NCB>
@@ -633,15 +663,15 @@ __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_down_kernel(MoeP
     }
   }
   TileRegs T;
-  // h is complete (the gate_up launch has ended): the first batch's rows go
-  // out with the tile and its slabs are multiplied as they arrive
+  // the first batch is sized to the slot's rows (1, 2 or RMAX), as in gate_up
   {
     const int rows0 = s.rows < RMAX ? s.rows : RMAX;
-    int pr[RMAX];
-    float hr[RMAX][32];
-    load_tile(tile, lane, T);
-    staged_load_h<RMAX>(p, s, pc, 0, rows0, L, pr, hr);
-    staged_down_math<LIC, RMAX>(p, T, pr, hr, rows0, t, g, L);
+    if (RMAX >= 4 && rows0 > 2)
+      staged_down_first<LIC, RMAX>(p, s, pc, tile, rows0, t, g, L, T);
+    else if (RMAX >= 2 && rows0 == 2)
+      staged_down_first<LIC, (RMAX >= 2 ? 2 : 1)>(p, s, pc, tile, rows0, t, g, L, T);
+    else
+      staged_down_first<LIC, 1>(p, s, pc, tile, rows0, t, g, L, T);
   }
 #pragma unroll 1
   for (int r0 = RMAX; r0 < s.rows; r0 += RMAX) {
