@@ -202,7 +202,9 @@ typedef struct moe_nvfp4_args {
   int64_t workspace_bytes;
   int64_t M, E, k, H, I;
   int64_t dense_min_rows;     /* three-launch schedule: slots with at least this many rows
-                                 use BF16 MFMA (0 = library default, 16; above M = never) */
+                                 use BF16 MFMA (above M = never; 0 = library default, by
+                                 M: 16 for M <= 8, 3 for M <= 16, 6 for M <= 32, 8 above;
+                                 16 in moe_nvfp4_route_decode) */
   int32_t schedule;           /* 0 = library choice, 2 = three launches,
                                  3 = two launches (per-row down + combine) */
   /* Optional, moe_nvfp4_route_decode only (NULL = none; moe_nvfp4_decode rejects

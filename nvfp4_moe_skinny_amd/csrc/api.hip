@@ -314,7 +314,7 @@ int32_t prepare_decode(const moe_nvfp4_args* a, bool routed, MoeParams& p,
   p.yp = (float*)(wsb + ws.yp_off);
   p.dense_min_rows = a->dense_min_rows > 0
                          ? (int)(a->dense_min_rows < (int64_t)1 << 30 ? a->dense_min_rows : 1 << 30)
-                         : kDenseRowsDefault;
+                         : dense_rows_default(M, routed);
   return ok();
 }
 

@@ -29,8 +29,20 @@ namespace nvfp4moe {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Slots with at least this many rows take the MFMA path by default.
-constexpr int kDenseRowsDefault = 16;
+// Slots with at least this many rows take the MFMA path by default, by the
+// number of rows M of the step (crossovers measured on the MoE decode step,
+// H = 2048, I = 512, E = 256, top-8, uniform and Zipf(1.1) routing): with one
+// row per VALU batch (9 <= M <= 16) a slot of 3 rows is already cheaper on
+// MFMA, whose cost hardly depends on the row count up to 16, and such slots
+// were the launch's last items (M = 16: 51.9 -> 46.8 us, M = 12: 52.6 ->
+// 36.6 us against a threshold of 16); with RMAX-row batches the VALU path
+// holds out longer (M <= 32: 6, above: 8). M <= 8 keeps every slot on VALU,
+// as the two-launch schedule needs. moe_nvfp4_route_decode keeps 16.
+inline int dense_rows_default(int64_t M, bool routed) {
+  if (!routed || M <= 8) return 16;
+  if (M <= 16) return 3;
+  return M <= 32 ? 6 : 8;
+}
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -164,6 +164,8 @@ def test_decode_validation(m):
     assert "grid" in m.last_error_detail()
     # two launches need FP32 h for every pair: no MFMA slot (M < dense_min_rows)
     assert dec(_args(m, schedule=3, dense_min_rows=4)) == m.NVFP4MOE_ERR_UNSUPPORTED
+    # the library's default threshold for 9 <= M <= 16 is 3 rows (MFMA slots)
+    assert dec(_args(m, M=12, schedule=3)) == m.NVFP4MOE_ERR_UNSUPPORTED
     assert dec(_args(m, ids=None)) == m.NVFP4MOE_ERR_NULL_ARG
     # routing folded in: grouping arrays not needed; logits required; M < dense_min_rows
     rd = lambda a, lg=4096: L.moe_nvfp4_route_decode(ctypes.byref(a), lg, None, None)
