@@ -2,10 +2,12 @@
 """Benchmark of the NVFP4 MoE decode step on one MI355X.
 
 A step is one pass of the routed MoE hot path over one batch of rows: router
-top-k + grouping (moe_route_topk), then gate_up -> SiLU*up -> down -> combine
-(moe_nvfp4_decode). The headline workload is one MoE block at M = 4 rows (one
-token plus three draft tokens verified together): 256 experts, top-8,
-hidden 2048, expert width 512, NVFP4 weights, BF16 activations.
+top-k, then gate_up -> SiLU*up -> down -> combine. For M <= 8 that is one
+moe_nvfp4_route_decode call (routing folded into the gate_up launch); above,
+moe_route_topk (top-k + grouping) then moe_nvfp4_decode. The headline workload
+is one MoE block at M = 4 rows (one token plus three draft tokens verified
+together): 256 experts, top-8, hidden 2048, expert width 512, NVFP4 weights,
+BF16 activations.
 
 To keep the 256 MB Infinity Cache from serving weights, each step uses the
 next of `copies` independently seeded weight sets (>= 1 GB streams between two
@@ -13,8 +15,9 @@ uses of the same bytes) and the next of 64 router-logit sets. Inputs are
 resident in HBM before timing starts. Steps are captured into a HIP graph and
 replayed; `value` is algorithmic bytes per step (touched expert codes + scales
 + tensor scales, activations in and out, logits and routing arrays) over the
-step time. The dominant call (moe_nvfp4_decode) is also timed on its own with
-HIP events on the stream it runs on, for the roofline entry.
+step time. For the roofline entry the decode call is timed on the stream it
+runs on: over the graph replays when the call is the whole step (M <= 8),
+else on its own with HIP events.
 
 Every graph-timed workload runs at least one second of warm-up replays, then
 five runs of at least 200 steps each (more when --steps asks for more), with
