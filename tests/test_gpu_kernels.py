@@ -283,6 +283,23 @@ def test_moe_block_dense_mfma(m, gpu, M, E, k, shared, resid, dense_min_rows):
     assert tol_ratio(out, ref) <= 1.0
 
 
+@pytest.mark.parametrize("M", [9, 12, 24, 33, 48])
+def test_moe_block_default_threshold_zipf(m, gpu, M):
+    """The library's default MFMA threshold, which depends on M (3 rows for
+    9 <= M <= 16, 6 up to 32, 8 above), on Zipf(1.1)-skewed routing: slots of
+    every size from one row to dozens take the VALU or the MFMA path side by
+    side, every element against the oracle."""
+    lay = moe_layer(0, wl=5, layer=300 + M, M=M, zipf_s=1.1)
+    r, out = _run_block(m, gpu, lay)
+    ids, w = oracle.route_topk(lay.logits, lay.k, lay.bias)
+    check_routing_exact(r, ids, w, lay.E)
+    counts = np.bincount(ids.ravel(), minlength=lay.E)
+    assert counts.max() >= 3  # at least one MFMA slot at the default threshold
+    ref = oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down, lay.shared_gate_up,
+                           lay.shared_down, None)
+    assert tol_ratio(out, ref) <= 1.0
+
+
 def test_moe_block_deterministic_and_workspace_reuse(m, gpu):
     """Repeated calls on one workspace, whatever it held before (it is filled
     with garbage first), give bit-identical outputs, in both schedules."""
