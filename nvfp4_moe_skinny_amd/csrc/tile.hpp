@@ -99,12 +99,14 @@ __device__ __forceinline__ void tile_dot_f32(const TileRegs& t, const float (&h)
   }
 }
 
-// Loads the lane's 32 BF16 columns of activation row `row`. Callers pad a
-// batch with a row that exists (results of padding rows are never written,
-// and in these products no output reads another row's activations) rather
-// than skip the load: a load under a branch leaves the compiler unable to
-// count the loads in flight where the paths join, and its waits then also
-// cover every load issued after it, prefetches included.
+// Loads the lane's 32 BF16 columns of activation row `row`. Where loads run
+// ahead of their use (the MFMA column rings), callers pad a batch with a row
+// that exists (results of padding rows are never written, and in these
+// products no output reads another row's activations) rather than skip the
+// load: a load under a branch leaves the compiler unable to count the loads
+// in flight where the paths join, and its waits then also cover every load
+// issued after it, prefetches included. The VALU row batches, whose products
+// wait for the whole batch anyway, skip a padding row's load instead.
 __device__ __forceinline__ void load_x_bf16(const uint16_t* x, int64_t ld, int64_t row, int col0,
                                             uint4 (&xr)[4]) {
   const uint4* p = reinterpret_cast<const uint4*>(x + row * ld + col0);
