@@ -202,12 +202,18 @@ DECODE_SOURCES = ("common.hpp", "tile.hpp", "dense.hpp", "moe.hpp", "staged.hpp"
 
 
 def kernel_source_hash():
-    """Hash of the decode call's kernel sources, to tie recorded counters to the code."""
+    """Hash of the decode call's kernel sources, to tie recorded counters to the
+    code: comments and whitespace are left out, so that a comment edit does
+    not void them."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in DECODE_SOURCES:
-        with open(os.path.join(ROOT, "nvfp4_moe_skinny_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "nvfp4_moe_skinny_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
