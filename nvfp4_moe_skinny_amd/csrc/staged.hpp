@@ -638,8 +638,9 @@ __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_down_kernel(MoeP
   const float g = s.shared ? p.sdn_g[0] : p.dn_g[s.e];
   if constexpr (DENSE) {
     if (s.rows >= p.dense_min_rows) {
-      // one row per VALU batch is the M <= 16 launch: a single 16-row pass
-      staged_down_dense<RMAX == 1 ? 1 : 2>(p, s, tile, t, g);
+      // the M <= 16 launches (plain slot order): at most 16 rows a slot, one
+      // 16-row pass
+      staged_down_dense<(RMAX == 1 || !ORDER) ? 1 : 2>(p, s, tile, t, g);
       return;
     }
   }
