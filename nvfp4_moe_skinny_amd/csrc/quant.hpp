@@ -23,7 +23,7 @@ constexpr int kQuantThreads = 256;
 // short workgroups is bound by how fast they start (measured over
 // [256][1024][2048]: 314 us with 256 workgroups per matrix, 184 us with 16).
 // The quantising pass, one thread per 16 elements, is bound by its arithmetic
-// (16 correctly rounded divisions per block) and keeps one block per thread.
+// (16 correctly rounded quotients per block) and keeps one block per thread.
 constexpr int kQuantMaxBlocksPerMatrix = 16;
 
 // Nearest finite non-negative E4M3 code to t >= 0, ties to the even code,
@@ -90,6 +90,23 @@ __device__ __forceinline__ float quant_g(uint32_t amax_bits) {
   return amax > 0.0f ? __fdiv_rn(amax, 2688.0f) : 1.0f;
 }
 
+// The two BF16 elements of word w (low half first) divided by sg, each
+// quotient correctly rounded (q0 = RN(x y), then one FMA correction with the
+// exact remainder; y = RN(1 / sg)), converted to E2M1 codes into byte SEL of
+// `codes`. The correction turns -0 into +0 (+0 + -0 rounds to +0), so the
+// quotient takes x's sign back (a no-op for every other value).
+template <int SEL>
+__device__ __forceinline__ uint32_t quotients_to_e2m1(uint32_t codes, uint32_t w, float y,
+                                                     float sg) {
+  const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xFFFF0000u);
+  const float q0 = __fmul_rn(x0, y), q1 = __fmul_rn(x1, y);
+  const float r0 =
+      __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, sg, x0), y, q0), x0);
+  const float r1 =
+      __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q1, sg, x1), y, q1), x1);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, r0, r1, 1.0f, SEL);
+}
+
 // One 16-element block (row n, block b) of matrix g per thread.
 __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int64_t i,
                                             int64_t blocks_per_matrix,
@@ -106,12 +123,39 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int6
   const float t = __fdiv_rn(__uint_as_float(mb << 16), __fmul_rn(6.0f, gv));
   const uint32_t sc = e4m3_rne_code(t);
   const float sg = __fmul_rn(e4m3_f32(sc, 0), gv);
+  // The 16 quotients |x| / sg, each correctly rounded, with one division:
+  // Markstein's method. With y the correctly rounded reciprocal of sg and
+  // q0 = RN(|x| y) (within one ulp of the quotient), the remainder
+  // |x| - q0 sg is exact in one FMA and RN(q0 + remainder * y) is the
+  // correctly rounded quotient, provided nothing leaves the normal range. So
+  // the fast form is taken for 2^-100 <= sg <= 2^100 (y and the quotients near
+  // E2M1's decision points, all >= 0.25, normal; smaller quotients round to
+  // code 0 either way, and the block scale keeps the quotients below 12), and
+  // the division itself otherwise (sg zero, subnormal, huge, inf or NaN).
+  // In the fast form the signed quotients go to the E2M1 conversion
+  // instruction, two per instruction: it rounds to nearest even on the E2M1
+  // grid and saturates at 6 exactly as e2m1_rne_code does for every finite
+  // value (checked on the chip over every decision point and its neighbours);
+  // it differs only for NaN, which the fast form never sees (a NaN or inf
+  // element makes the matrix maximum, hence sg, NaN or inf).
+  const bool fast = sg >= 0x1p-100f && sg <= 0x1p100f;
   uint32_t q[2] = {0u, 0u};
+  if (fast) {
+    const float y = __fdiv_rn(1.0f, sg);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint32_t bits = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    const uint32_t mag = sg > 0.0f ? e2m1_rne_code(__fdiv_rn(bf16_abs_f32(bits), sg)) : 0u;
-    q[j >> 3] |= (((bits >> 15) << 3) | mag) << (4 * (j & 7));
+    for (int h = 0; h < 2; ++h) {
+      q[h] = quotients_to_e2m1<0>(q[h], w[4 * h], y, sg);
+      q[h] = quotients_to_e2m1<1>(q[h], w[4 * h + 1], y, sg);
+      q[h] = quotients_to_e2m1<2>(q[h], w[4 * h + 2], y, sg);
+      q[h] = quotients_to_e2m1<3>(q[h], w[4 * h + 3], y, sg);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t bits = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      const uint32_t mag = sg > 0.0f ? e2m1_rne_code(__fdiv_rn(bf16_abs_f32(bits), sg)) : 0u;
+      q[j >> 3] |= (((bits >> 15) << 3) | mag) << (4 * (j & 7));
+    }
   }
   *reinterpret_cast<uint2*>(codes + 8 * i) = make_uint2(q[0], q[1]);
   scales[i] = (uint8_t)sc;

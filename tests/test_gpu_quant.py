@@ -73,6 +73,48 @@ def test_quantize_zero_matrix_and_ties(m, gpu):
     assert g[0] == 1.0 and (s[0] == 0).all() and (c[0] == 0).all()
 
 
+def _bf16_next(bits, up):
+    """The BF16 neighbour of non-negative BF16 bit patterns, away from or toward zero."""
+    return (bits.astype(np.int32) + (1 if up else -1)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("k", [-110, -30, 0, 25])
+def test_quantize_quotients_on_midpoints(m, gpu, k):
+    """Tensor scale g = 2^k (matrix amax 2688 * 2^k), every non-zero E4M3 block
+    scale code s_b (block amax 6 s_b g), and elements exactly on each E2M1
+    midpoint times s_b g (quotients that are exact ties) and one BF16 step to
+    either side: the per-element quotients |x| / (s_b g) must be the correctly
+    rounded ones for every code to match. k = -110 puts s_b g below 2^-100."""
+    K = 256
+    codes = np.arange(1, 0x7F)  # 126 block scales
+    nblk = K // 16
+    N = (len(codes) + 1 + nblk - 1) // nblk
+    g = np.float32(2.0 ** k)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    x = np.zeros((1, N, K), np.float32)
+    x[0, 0, 0] = 2688.0 * g  # sets amax: g = 2^k exactly; block 0 scale 448
+    for i, c in enumerate(codes):
+        b = i + 1
+        n, col = b // nblk, 16 * (b % nblk)
+        s_b = float(torch.tensor([int(c)], dtype=torch.uint8).view(torch.float8_e4m3fn)
+                    .to(torch.float32)[0])
+        sg = np.float32(s_b) * g
+        x[0, n, col] = 6.0 * sg                       # block amax: t = s_b exactly
+        x[0, n, col + 1:col + 8] = mids * sg           # exact ties
+        x[0, n, col + 8:col + 15] = -mids * sg
+    bits = _bf16(x.ravel().tolist()).reshape(x.shape)
+    # one BF16 step away from the ties on every other block, toward zero on the rest
+    for b in range(1, len(codes) + 1):
+        n, col = b // nblk, 16 * (b % nblk)
+        seg = bits[0, n, col + 1:col + 15]
+        mag = seg & 0x7FFF
+        step = _bf16_next(mag, up=(b % 2 == 0))
+        seg[:] = (seg & 0x8000) | np.where(b % 3 == 0, mag, step)
+        if b % 2:
+            bits[0, n, col + 15] = 0x8000  # -0 inside a block with a scale: code 8
+    _check(m, gpu, bits)
+
+
 def test_quantize_inverts_exact_dequant(m, gpu):
     """x = dequant(c, s, g) exactly in BF16 with every block reaching 6 s_b g:
     quantizing it gives c, s, g back."""
