@@ -26,6 +26,24 @@ __device__ __forceinline__ bf16x2 fp8_pair_bf16(uint32_t w, bool hi_word) {
                  : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
 }
 
+// The lane's 16 columns of each of the S slab positions of x rows m0 ..
+// m0 + R - 1 (rows past M read row M - 1).
+template <int R, int S>
+__device__ __forceinline__ void load_fp8_rows(const uint16_t* __restrict__ x, int64_t m0,
+                                              int64_t M, int lane, uint4 (&xr)[R][S][2]) {
+  constexpr int K = S * kFp8SlabBytes;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = m0 + r < M ? m0 + r : M - 1;
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+      const uint4* p = reinterpret_cast<const uint4*>(x + row * K + q * 1024 + 16 * lane);
+      xr[r][q][0] = p[0];
+      xr[r][q][1] = p[1];
+    }
+  }
+}
+
 // One wave per tile of 8 / S rows; rows of x in batches of up to R.
 template <int S, int RMAX>
 __global__ void __launch_bounds__(64) fp8_skinny_gemm_kernel(const uint16_t* __restrict__ x,
@@ -38,31 +56,26 @@ __global__ void __launch_bounds__(64) fp8_skinny_gemm_kernel(const uint16_t* __r
   const int lane = threadIdx.x;
   const int64_t tile = xcd_block((int)blockIdx.x, (int)gridDim.x);
   const int64_t n0 = tile * RPT;
-  // codes: slab i is row i / S, columns (i % S) * 1024 + 16 lane .. + 15;
-  // slabs of rows past N are not read (zero)
+  const float s = scale[0];
+  const int rlane = lane >> (6 - (RPT == 8 ? 3 : RPT == 4 ? 2 : RPT == 2 ? 1 : 0));
+  // The first batch's activation rows are requested before the tile, so each
+  // slab is multiplied as it lands. Every load is issued (a row past M or N
+  // reads the last one: its results are not written), since a load skipped
+  // under a branch makes the compiler's waits cover later loads too.
+  uint4 xr[RMAX][S][2];
+  load_fp8_rows<RMAX, S>(x, 0, M, lane, xr);
+  __builtin_amdgcn_sched_barrier(0);
+  // codes: slab i is row i / S, columns (i % S) * 1024 + 16 lane .. + 15
   uint4 c[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int64_t n = n0 + i / S;
-    c[i] = n < N ? load_stream(reinterpret_cast<const uint4*>(w + n * K + (i % S) * 1024) + lane)
-                 : make_uint4(0, 0, 0, 0);
+    const int64_t n = n0 + i / S < N ? n0 + i / S : N - 1;
+    c[i] = load_stream(reinterpret_cast<const uint4*>(w + n * K + (i % S) * 1024) + lane);
   }
-  const float s = scale[0];
-  const int rlane = lane >> (6 - (RPT == 8 ? 3 : RPT == 4 ? 2 : RPT == 2 ? 1 : 0));
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 1
   for (int64_t m0 = 0; m0 < M; m0 += RMAX) {
-    // the lane's 16 columns of each of the S slab positions, for RMAX rows
-    uint4 xr[RMAX][S][2];
-#pragma unroll
-    for (int r = 0; r < RMAX; ++r) {
-      const bool valid = m0 + r < M;
-#pragma unroll
-      for (int q = 0; q < S; ++q) {
-        const uint4* p = reinterpret_cast<const uint4*>(x + (m0 + r) * K + q * 1024 + 16 * lane);
-        xr[r][q][0] = valid ? p[0] : make_uint4(0, 0, 0, 0);
-        xr[r][q][1] = valid ? p[1] : make_uint4(0, 0, 0, 0);
-      }
-    }
+    if (m0 > 0) load_fp8_rows<RMAX, S>(x, m0, M, lane, xr);
     float part[RMAX][8];
 #pragma unroll
     for (int r = 0; r < RMAX; ++r)
