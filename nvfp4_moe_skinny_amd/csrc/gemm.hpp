@@ -48,6 +48,29 @@ __device__ __forceinline__ void gemm_rows(const TileRegs& T, const uint16_t* __r
   gemm_write<L, R>(part, m0, rows, lane, tile, N, g, y);
 }
 
+// The first batch (rows 0 .. rows - 1) with the tile: the rows' loads go out
+// first (a padding row's are skipped under a branch of the whole wave; they
+// all precede the tile's, so the waits for the tile stay exact), then the
+// tile's, and each slab is multiplied as it lands. T keeps the tile.
+template <int L, int R>
+__device__ __forceinline__ void gemm_first(const uint8_t* __restrict__ tile_ptr,
+                                           const uint16_t* __restrict__ x, int64_t K, int rows,
+                                           int col0, int lane, int64_t tile, int64_t N, float g,
+                                           uint16_t* __restrict__ y, TileRegs& T) {
+  uint4 xr[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < rows) load_x_bf16(x, K, r, col0, xr[r]);
+    else for (int j = 0; j < 4; ++j) xr[r][j] = make_uint4(0, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(tile_ptr, lane, T);
+  __builtin_amdgcn_sched_barrier(0);
+  float part[R][8];
+  tile_dot_bf16<R>(T, xr, part);
+  gemm_write<L, R>(part, 0, rows, lane, tile, N, g, y);
+}
+
 // Q panels: the row block's tiles streamed in turn for rows m0 .. m0 + rows - 1.
 template <int L, int R>
 __device__ __forceinline__ void gemm_rows_panels(const uint8_t* __restrict__ blk_tiles, int64_t Q,
@@ -105,10 +128,22 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const uint16_t* __rest
   }
   const int64_t tile = blk;
   TileRegs T;
-  load_tile(w + tile * kTileBytes, lane, T);
   const int col0 = 32 * (lane % L);
+  // the first batch's rows are requested before the tile, so each slab is
+  // multiplied as it lands (the later batches reuse the tile in registers)
+  {
+    const int rows = (int)(M < 8 ? M : 8);
+    if (rows > 4)
+      gemm_first<L, 8>(w + tile * kTileBytes, x, K, rows, col0, lane, tile, N, g, y, T);
+    else if (rows > 2)
+      gemm_first<L, 4>(w + tile * kTileBytes, x, K, rows, col0, lane, tile, N, g, y, T);
+    else if (rows > 1)
+      gemm_first<L, 2>(w + tile * kTileBytes, x, K, rows, col0, lane, tile, N, g, y, T);
+    else
+      gemm_first<L, 1>(w + tile * kTileBytes, x, K, rows, col0, lane, tile, N, g, y, T);
+  }
 #pragma unroll 1
-  for (int64_t m0 = 0; m0 < M; m0 += 8) {
+  for (int64_t m0 = 8; m0 < M; m0 += 8) {
     opaque_tile(T);
     const int rows = (int)((M - m0) < 8 ? (M - m0) : 8);
     if (rows > 4)
