@@ -545,15 +545,18 @@ __device__ __forceinline__ void staged_down_rows(const MoeParams& p, const SlotI
 }
 
 // The first batch of R rows: h is complete (the gate_up launch has ended), so
-// its rows go out with the tile and its slabs are multiplied as they arrive.
+// its rows go out first, then the tile, whose slabs are multiplied as they
+// arrive (M = 16: 46.61 -> 46.17 us, M = 256: 208.1 -> 207.0 us).
 template <int LC, int R>
 __device__ __forceinline__ void staged_down_first(const MoeParams& p, const SlotInfo& s,
                                                   const PairCache& c, const uint8_t* tile,
                                                   int rows, int t, float g, int L, TileRegs& T) {
   int pr[R];
   float hr[R][32];
-  load_tile(tile, (int)threadIdx.x, T);
   staged_load_h<R>(p, s, c, 0, rows, L, pr, hr);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(tile, (int)threadIdx.x, T);
+  __builtin_amdgcn_sched_barrier(0);
   staged_down_math<LC, R>(p, T, pr, hr, rows, t, g, L);
 }
 
@@ -756,6 +759,9 @@ __device__ __forceinline__ void token_down_slot(const MoeParams& p, int q, int m
       return;
     }
   }
+  // the tile's loads first: with h requested ahead of them (so that slabs
+  // could be multiplied as they land) the step measured slower (M = 4: 15.46
+  // -> 16.05 us; 40-layer stack 1226 -> 1254 us)
   TileRegs T;
   float hr[1][32];
   load_tile(tile, lane, T);
