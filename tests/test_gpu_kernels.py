@@ -283,6 +283,24 @@ def test_moe_block_dense_mfma(m, gpu, M, E, k, shared, resid, dense_min_rows):
     assert tol_ratio(out, ref) <= 1.0
 
 
+@pytest.mark.parametrize("M,E,k,shared", [(16, 8, 8, True), (13, 4, 2, False), (7, 3, 3, True),
+                                          (15, 16, 5, True)])
+def test_moe_block_valu_rows_small_m(m, gpu, M, E, k, shared):
+    """M <= 16, three launches with every slot on VALU (threshold above M):
+    slots of up to 16 rows through the one-row gate_up items and the down
+    kernel's two-row batches, odd counts included, every element."""
+    lay = moe_layer(seed=11 * M + E, wl=205, M=M, E_=E, H_=2048, I_=512, k=k, shared=shared)
+    residual = synth.normal_bf16(synth.key(5, 206, M), (M, 2048))
+    r, out = _run_block(m, gpu, lay, residual, schedule=2, dense_min_rows=M + 1)
+    ids, w = oracle.route_topk(lay.logits, k, lay.bias)
+    check_routing_exact(r, ids, w, E)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    assert counts.max() >= 3
+    ref = oracle.moe_block(lay.x, ids, w, lay.gate_up, lay.down, lay.shared_gate_up,
+                           lay.shared_down, residual)
+    assert tol_ratio(out, ref) <= 1.0
+
+
 @pytest.mark.parametrize("M", [9, 12, 24, 33, 48])
 def test_moe_block_default_threshold_zipf(m, gpu, M):
     """The library's default MFMA threshold, which depends on M (3 rows for
