@@ -210,8 +210,9 @@ int32_t launch_route(const float* logits, const float* bias, int64_t M, int64_t 
                        n_active);
     return launched("moe_route_topk");
   }
-  hipLaunchKernelGGL(route_rows_kernel, dim3(grid_for(M, kRouteWaves, 1 << 20)), dim3(1024), 0,
-                     stream, logits, bias, (int)M, (int)E, (int)k, ids, w);
+  hipLaunchKernelGGL(route_rows_kernel, dim3(grid_for(M, kRowWaves, 1 << 20)),
+                     dim3(kRowWaves * 64), 0, stream, logits, bias, (int)M, (int)E, (int)k, ids,
+                     w);
   const int32_t st = launched("moe_route_topk rows");
   if (st != NVFP4MOE_OK) return st;
   hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, ids, (int)M, (int)E, (int)k,
