@@ -739,9 +739,15 @@ constexpr int kTokenMajorMaxRows = 8;
 // extra bytes, and y never leaves the chip (no combine launch). h must be
 // FP32 words: every slot took the VALU gate_up path.
 // Slot q of row m (q = k: the shared expert), down tile t: its outputs to ys[q].
-template <int LIC>
+// What a slot's wave requests between its tile loads and its products.
+struct NoPrefetch {
+  __device__ void operator()() const {}
+};
+
+template <int LIC, typename Pre = NoPrefetch>
 __device__ __forceinline__ void token_down_slot(const MoeParams& p, int q, int m, int t, int L,
-                                                float (*ys)[LIC ? 512 / LIC : 512]) {
+                                                float (*ys)[LIC ? 512 / LIC : 512],
+                                                Pre pre = Pre()) {
   const int lane = threadIdx.x & 63;
   const bool sh = q == p.k;  // the shared expert's slot (only with has_shared)
   const int pair = sh ? p.M * p.k + m : m * p.k + q;
@@ -751,6 +757,7 @@ __device__ __forceinline__ void token_down_slot(const MoeParams& p, int q, int m
   const float g = sh ? p.sdn_g[0] : p.dn_g[e];
   if constexpr (LIC == 0) {
     if (p.QI > 1 || L < 8) {  // any row width, any number of panels
+      pre();
       float v[8];
       panels_dot_f32<0>(sh ? p.sdn : p.dn + (int64_t)e * p.dn_mat_bytes, t, p.QI, p.KpI, p.hp,
                         p.I, pair, lane, L, v);
@@ -766,6 +773,7 @@ __device__ __forceinline__ void token_down_slot(const MoeParams& p, int q, int m
   float hr[1][32];
   load_tile(tile, lane, T);
   load_h_f32(p.hp, p.I, pair, 32 * (lane % L), hr[0]);
+  pre();
   float part[1][8];
   tile_dot_f32<1>(T, hr, part);
   reduce_slabs_rt<LIC>(part[0], lane, L);
@@ -790,17 +798,45 @@ __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel
   // eight routed ones a wave takes two (q = wave, wave + waves), so that a
   // block of five waves leaves room for three blocks per CU where nine waves
   // left room for one (40-layer stack at M = 8: 1364 -> 1318 us)
+  const int nrows = min(rpt, p.H - t * rpt);
+  // wave 0's threads sum the first 64 output rows: their routing weights and
+  // residual are requested once the wave's tile loads are out, so that they
+  // are in by the barrier (before the tiles they delayed the tiles: M = 4
+  // 15.43 -> 15.75 us; after them, 40-layer stack 1224.3 -> 1204.1 us)
+  float wv[kMaxTopK], res = 0.0f;
+  auto pre = [&]() {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) wv[j] = j < p.k ? p.w[m * p.k + j] : 0.0f;
+    const int r = (int)threadIdx.x;
+    if (p.residual && r < nrows) res = bf16_to_f32(p.residual[(int64_t)m * p.H + t * rpt + r]);
+  };
   if constexpr (SPW == 1) {
-    token_down_slot<LIC>(p, wave, m, t, L, ys);
+    if (wave == 0)
+      token_down_slot<LIC>(p, wave, m, t, L, ys, pre);
+    else
+      token_down_slot<LIC>(p, wave, m, t, L, ys);
   } else {
     const int waves = (int)(blockDim.x >> 6);
-    token_down_slot<LIC>(p, wave, m, t, L, ys);
+    if (wave == 0)
+      token_down_slot<LIC>(p, wave, m, t, L, ys, pre);
+    else
+      token_down_slot<LIC>(p, wave, m, t, L, ys);
     if (wave + waves < p.k + p.has_shared) token_down_slot<LIC>(p, wave + waves, m, t, L, ys);
   }
   __syncthreads();
   // the tile's output rows (past H in a ragged last row block: none)
-  const int nrows = min(rpt, p.H - t * rpt);
-  for (int r = (int)threadIdx.x; r < nrows; r += (int)blockDim.x) {
+  if (wave == 0 && (int)threadIdx.x < nrows) {
+    const int r = (int)threadIdx.x;
+    const int64_t o = (int64_t)m * p.H + t * rpt + r;
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < p.k) acc += wv[j] * ys[j][r];
+    if (p.has_shared) acc += ys[p.k][r];
+    if (p.residual) acc += res;
+    p.out[o] = f32_to_bf16_rne(acc);
+  }
+  for (int r = 64 + (int)threadIdx.x; r < nrows; r += (int)blockDim.x) {
     const int64_t o = (int64_t)m * p.H + t * rpt + r;
     float acc = 0.0f;
 #pragma unroll

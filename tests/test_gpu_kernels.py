@@ -173,7 +173,9 @@ def test_moe_block_small(m, gpu, M, E, H, I, k, shared, resid, schedule):
     (1, 256, 2048, 512, 8, False, False, False), (4, 256, 2048, 512, 8, False, False, True),
     (8, 256, 2048, 512, 8, True, True, True), (3, 16, 256, 256, 4, True, False, False),
     (5, 8, 512, 512, 8, True, False, False), (2, 32, 1024, 256, 2, False, True, False),
-    (12, 64, 2048, 512, 8, True, False, True), (6, 4, 2048, 512, 1, True, True, False)])
+    (12, 64, 2048, 512, 8, True, False, True), (6, 4, 2048, 512, 1, True, True, False),
+    # down tiles of more than 64 output rows (I = 128: 128, I = 96: 512)
+    (4, 16, 512, 128, 4, False, True, True), (3, 8, 2048, 96, 2, True, True, False)])
 def test_moe_route_decode_fused(m, gpu, M, E, H, I, k, shared, resid, bias):
     """Routing inside the gate_up launch: ids and w bit-identical to the oracle's
     routing, the output within tolerance of the oracle and bit-identical to
