@@ -1,12 +1,16 @@
 // fused.hpp - routing folded into gate_up for few rows (two launches from the
 // logits to the output, with token_down_combine_kernel).
 //
-// One block per (item, gate tile j); items are the pairs m*k + jj (row m, slot
-// jj), then the shared expert's rows. Both waves of a routed item select the
-// top k of row m themselves (the same per-row routine as moe_route_topk, so
-// the same experts and weights bit for bit) while the row of x is already on
-// its way; wave 0 then streams gate tile j of expert ids[m][jj], wave 1 the up
-// tile, as in staged_gate_split_kernel. The items of tile 0 store ids and w
+// One block per (item, gate tile j); items go row by row: row m's k slots,
+// then (with a shared expert) its shared row. The launch's blocks are dealt to
+// the XCDs in consecutive ranges, so in this order every XCD gets the same mix
+// of routed and shared items; with the shared rows last, one XCD took nearly
+// all of them (tiles its L2 already held) and ran idle for the last 5 of the
+// launch's 17 us (40-layer stack 1207.6 -> 1194.5 us). Both waves of a routed
+// item select the top k of row m themselves (the same per-row routine as
+// moe_route_topk, so the same experts and weights bit for bit) while the row
+// of x is already on its way; wave 0 then streams gate tile j of expert
+// ids[m][jj], wave 1 the up tile, as in staged_gate_split_kernel. The items of tile 0 store ids and w
 // for the down launch. With few rows nearly every pair has its own expert, so
 // a tile per pair costs almost no extra bytes, and no grouping is needed.
 #pragma once
@@ -29,8 +33,10 @@ __global__ void __launch_bounds__(128, 4) fused_route_gate_kernel(MoeParams p,
   const int b = xcd_block((int)blockIdx.x, (int)gridDim.x);
   const int item = b / p.PG, j = b % p.PG;
   const int npairs = p.M * p.k;
-  const bool sh = item >= npairs;
-  const int m = sh ? item - npairs : item / p.k;
+  const int nq = p.k + p.has_shared;  // row m's items: its k slots, then its shared row
+  const int m = item / nq, q = item - m * nq;
+  const bool sh = q == p.k;
+  const int hrow = sh ? npairs + m : m * p.k + q;  // the pair's h row
   const int L = LHC ? LHC : p.LH;
   uint4 xr[1][4];
   load_x_bf16(p.x, p.H, m, 32 * (lane % L), xr[0]);
@@ -38,15 +44,15 @@ __global__ void __launch_bounds__(128, 4) fused_route_gate_kernel(MoeParams p,
   if (!sh) {
     int my_id;
     float my_w;
-    const int jj = item - m * p.k;
+    const int jj = q;
     // the items of tile 0 store ids and w (all k rounds, softmax); the others
     // need only the first jj + 1 experts
     route_row_core(logits, bias, p.E, p.k, m, lane, lp[wave], my_id, my_w,
                    j == 0 ? kRouteMaxK : jj + 1, j == 0);
     e = __builtin_amdgcn_readlane(my_id, jj);
     if (j == 0 && wave == 0 && lane == jj) {
-      ids[item] = my_id;
-      w[item] = my_w;
+      ids[hrow] = my_id;
+      w[hrow] = my_w;
     }
   }
   const uint8_t* mat = sh ? p.sgu : p.gu + (int64_t)e * p.gu_mat_bytes;
@@ -66,15 +72,15 @@ __global__ void __launch_bounds__(128, 4) fused_route_gate_kernel(MoeParams p,
   }
   const int nv = LHC ? 1 : reduced_values(L);
 #pragma unroll
-  for (int q = 0; q < NV; ++q)
-    if (wave == 1 && q < nv) up_lds[q][lane] = v[q];
+  for (int qv = 0; qv < NV; ++qv)
+    if (wave == 1 && qv < nv) up_lds[qv][lane] = v[qv];
   __syncthreads();
   if (wave == 0 && reduced_writer_rt(lane, L)) {
 #pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      if (q < nv) {
-        const int i = j * p.RH + reduced_row_v(lane, L, q);
-        p.hp[(int64_t)item * p.I + i] = silu(v[q] * g) * (up_lds[q][lane] * g);
+    for (int qv = 0; qv < NV; ++qv) {
+      if (qv < nv) {
+        const int i = j * p.RH + reduced_row_v(lane, L, qv);
+        p.hp[(int64_t)hrow * p.I + i] = silu(v[qv] * g) * (up_lds[qv][lane] * g);
       }
     }
   }
