@@ -103,16 +103,18 @@ struct GemmLaunch {
   }
 };
 
-// token_down_combine blocks: one wave per slot up to eight slots, else two
-// slots a wave (five waves for eight routed slots and the shared expert).
+// token_down_combine blocks: one wave per slot up to eight slots; eight waves
+// for eight routed slots and the shared expert, wave 0 taking two (k <= 8, so
+// nine slots means k = 8 with a shared expert).
 template <int LI>
 void launch_token_down(const MoeParams& p, hipStream_t s) {
   const int n = p.k + p.has_shared;
   const int grid = p.M * p.PD + p.proj_blocks;  // the projection's blocks first
   if (n <= 8)
-    hipLaunchKernelGGL((token_down_combine_kernel<LI, 1>), dim3(grid), dim3(n * 64), 0, s, p);
+    hipLaunchKernelGGL((token_down_combine_kernel<LI, false>), dim3(grid), dim3(n * 64), 0, s,
+                       p);
   else
-    hipLaunchKernelGGL((token_down_combine_kernel<LI, 2>), dim3(grid), dim3((n + 1) / 2 * 64), 0,
+    hipLaunchKernelGGL((token_down_combine_kernel<LI, true>), dim3(grid), dim3((n - 1) * 64), 0,
                        s, p);
 }
 

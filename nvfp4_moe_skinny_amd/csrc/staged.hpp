@@ -780,7 +780,7 @@ __device__ __forceinline__ void token_down_slot(const MoeParams& p, int q, int m
   if (reduced_writer_rt(lane, L)) ys[q][reduced_row(lane, L)] = part[0][0] * g;
 }
 
-template <int LIC, int SPW>
+template <int LIC, bool W0_SHARED>
 __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel(MoeParams p) {
   __shared__ float ys[kMaxTopK + 1][LIC ? 512 / LIC : 512];  // a down tile's rows per slot
   const int wave = threadIdx.x >> 6;
@@ -794,10 +794,13 @@ __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel
   const int m = b / p.PD, t = b % p.PD;
   const int L = LIC ? LIC : p.LI;
   const int rpt = p.RI;  // output rows of a down tile
-  // SPW slots per wave: one up to eight slots; with the shared expert beside
-  // eight routed ones a wave takes two (q = wave, wave + waves), so that a
-  // block of five waves leaves room for three blocks per CU where nine waves
-  // left room for one (40-layer stack at M = 8: 1364 -> 1318 us)
+  // One wave per slot, up to eight slots. With the shared expert beside eight
+  // routed ones (W0_SHARED) the block keeps eight waves and wave 0 takes the
+  // shared slot first, then routed slot 0: two such blocks fit a CU, where
+  // nine waves left room for one, and the shared expert's tile t, which every
+  // row reads, mostly comes from cache. (40-layer stack at M = 8: nine waves
+  // 1364 us; five waves of two slots each 1318 us, 1191 us after later
+  // changes; eight waves with routed slot 0 first 1183 us, shared first 1180.)
   const int nrows = min(rpt, p.H - t * rpt);
   // wave 0's threads sum the first 64 output rows: their routing weights and
   // residual are requested once the wave's tile loads are out, so that they
@@ -810,18 +813,15 @@ __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel
     const int r = (int)threadIdx.x;
     if (p.residual && r < nrows) res = bf16_to_f32(p.residual[(int64_t)m * p.H + t * rpt + r]);
   };
-  if constexpr (SPW == 1) {
-    if (wave == 0)
-      token_down_slot<LIC>(p, wave, m, t, L, ys, pre);
-    else
-      token_down_slot<LIC>(p, wave, m, t, L, ys);
+  if (wave == 0) {
+    if constexpr (W0_SHARED) {
+      token_down_slot<LIC>(p, p.k, m, t, L, ys, pre);
+      token_down_slot<LIC>(p, 0, m, t, L, ys);
+    } else {
+      token_down_slot<LIC>(p, 0, m, t, L, ys, pre);
+    }
   } else {
-    const int waves = (int)(blockDim.x >> 6);
-    if (wave == 0)
-      token_down_slot<LIC>(p, wave, m, t, L, ys, pre);
-    else
-      token_down_slot<LIC>(p, wave, m, t, L, ys);
-    if (wave + waves < p.k + p.has_shared) token_down_slot<LIC>(p, wave + waves, m, t, L, ys);
+    token_down_slot<LIC>(p, wave, m, t, L, ys);
   }
   __syncthreads();
   // the tile's output rows (past H in a ragged last row block: none)
