@@ -620,12 +620,18 @@ int32_t route_decode(const moe_nvfp4_args* a, const float* logits, const float* 
   const int grid = (int)((M * a->k + (p.has_shared ? M : 0)) * p.PG);
   int32_t* ids = const_cast<int32_t*>(a->ids);
   float* w = const_cast<float*>(a->w);
-  if (specialised)
-    hipLaunchKernelGGL(fused_route_gate_kernel<64>, dim3(grid), dim3(128), 0, stream, p, logits,
-                       bias, ids, w);
+  if (specialised && p.has_shared)
+    hipLaunchKernelGGL((fused_route_gate_kernel<64, true>), dim3(grid), dim3(128), 0, stream, p,
+                       logits, bias, ids, w);
+  else if (specialised)
+    hipLaunchKernelGGL((fused_route_gate_kernel<64, false>), dim3(grid), dim3(128), 0, stream, p,
+                       logits, bias, ids, w);
+  else if (p.has_shared)
+    hipLaunchKernelGGL((fused_route_gate_kernel<0, true>), dim3(grid), dim3(128), 0, stream, p,
+                       logits, bias, ids, w);
   else
-    hipLaunchKernelGGL(fused_route_gate_kernel<0>, dim3(grid), dim3(128), 0, stream, p, logits,
-                       bias, ids, w);
+    hipLaunchKernelGGL((fused_route_gate_kernel<0, false>), dim3(grid), dim3(128), 0, stream, p,
+                       logits, bias, ids, w);
   const int32_t st2 = launched("moe_nvfp4_route_decode gate_up");
   if (st2 != NVFP4MOE_OK) return st2;
   if (specialised)
