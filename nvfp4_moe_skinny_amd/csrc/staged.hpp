@@ -806,12 +806,17 @@ __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel
   // residual are requested once the wave's tile loads are out, so that they
   // are in by the barrier (before the tiles they delayed the tiles: M = 4
   // 15.43 -> 15.75 us; after them, 40-layer stack 1224.3 -> 1204.1 us)
-  float wv[kMaxTopK], res = 0.0f;
+  // (the residual load is unconditional, from x's same place without one and
+  // a clamped row: under a branch the compiler waited for every load in
+  // flight, the tile's included, right after it; stack 1185.3 -> 1184.4 us)
+  float wv[kMaxTopK];
+  uint16_t res_raw = 0;
   auto pre = [&]() {
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) wv[j] = j < p.k ? p.w[m * p.k + j] : 0.0f;
-    const int r = (int)threadIdx.x;
-    if (p.residual && r < nrows) res = bf16_to_f32(p.residual[(int64_t)m * p.H + t * rpt + r]);
+    const int r = min((int)threadIdx.x, nrows - 1);
+    const uint16_t* rsrc = p.residual ? p.residual : p.x;  // both [M][H]
+    res_raw = rsrc[(int64_t)m * p.H + t * rpt + r];
   };
   if (wave == 0) {
     if constexpr (W0_SHARED) {
@@ -833,7 +838,7 @@ __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel
     for (int j = 0; j < kMaxTopK; ++j)
       if (j < p.k) acc += wv[j] * ys[j][r];
     if (p.has_shared) acc += ys[p.k][r];
-    if (p.residual) acc += res;
+    if (p.residual) acc += bf16_to_f32(res_raw);
     p.out[o] = f32_to_bf16_rne(acc);
   }
   for (int r = 64 + (int)threadIdx.x; r < nrows; r += (int)blockDim.x) {
