@@ -64,7 +64,7 @@ __device__ __forceinline__ void gemm_first(const uint8_t* __restrict__ tile_ptr,
     else for (int j = 0; j < 4; ++j) xr[r][j] = make_uint4(0, 0, 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  load_tile(tile_ptr, lane, T);
+  load_tile_scales_first(tile_ptr, lane, T);
   __builtin_amdgcn_sched_barrier(0);
   float part[R][8];
   tile_dot_bf16<R>(T, xr, part);
