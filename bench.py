@@ -706,8 +706,9 @@ def bench_quant(args):
 
 
 def bench_dense(args):
-    """The single dense NVFP4 matrix: M = 1 BF16 row ~N(0,1) times W [512][2048]
-    (uniform codes, E4M3 scales 2^U[-4,4), g = 1.0), 594,948 bytes a call.
+    """The single dense NVFP4 matrix: M = 1 BF16 row ~N(0,1) (--rows: M rows)
+    times W [512][2048] (uniform codes, E4M3 scales 2^U[-4,4), g = 1.0),
+    594,948 bytes a call at M = 1.
     Calls cycle through >= 2048 distinct seeded matrices (1.2 GB, copy 0 is
     the canonical seed-0 matrix) so that each reads HBM, not the last-level
     cache. value = the amortised rate of the calls in a graph; beside it the
@@ -721,12 +722,12 @@ def bench_dense(args):
     from synth import workloads as W
 
     dev = torch.device("cuda:0")
-    M, K, N = 1, 2048, 512
+    M, K, N = args.rows or 1, 2048, 512
     copies = max(args.copies or 2048, 16)
     t0 = time.time()
     ws, xs, host = [], [], []
     for c in range(copies):
-        x, w = W.dense_skinny(seed=0, layer=c)
+        x, w = W.dense_skinny(seed=0, M=M, layer=c)
         ws.append(pack(w, dev, m))
         xs.append(to_dev_bf16(x, dev))
         if c < 64:
@@ -759,12 +760,15 @@ def bench_dense(args):
     step_b = w_bytes + M * K * 2 + M * N * 2
     gbs = step_b / (ms * 1e-3) / 1e9
     ceiling_us = None if args.no_ceiling else read_ceiling(step_b, m)
+    # the library's choice for K = 2048, N = 512 (4-16 rows: the split-K MFMA kernel)
+    gemm_kernel = "skinny_gemm_kernel<64>" if M < 4 else (
+        "skinny_gemm_splitk_kernel" if M <= 16 else "skinny_gemm_dense_kernel")
     record = {
-        "metric": "NVFP4 dense skinny GEMM achieved HBM GB/s (single 2048->512 matrix, M=1)",
+        "metric": f"NVFP4 dense skinny GEMM achieved HBM GB/s (single 2048->512 matrix, M={M})",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": n_steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "nvfp4_skinny_gemm_m1_k2048_n512", "M": M, "K": K, "N": N,
+        "config": {"workload": f"nvfp4_skinny_gemm_m{M}_k2048_n512", "M": M, "K": K, "N": N,
                    "g": 1.0, "distinct_matrices": copies,
                    "timing": "hip graph replay, events (amortised over the calls)"},
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_b,
@@ -773,7 +777,7 @@ def bench_dense(args):
                              "mean": round(float(lat.mean()), 3),
                              "min": round(float(lat.min()), 3), "calls": int(lat.size),
                              "timing": "eager, each call alone between two events"},
-        "roofline": {"bound": "hbm", "kernel": "skinny_gemm_kernel<64> (one launch a call)",
+        "roofline": {"bound": "hbm", "kernel": f"{gemm_kernel} (one launch a call)",
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_launch_us": round(ms * 1e3, 4), "bytes_per_launch": step_b,

@@ -290,16 +290,17 @@ __device__ __forceinline__ void splitk_block(const uint16_t* __restrict__ x, int
       d.c[qq] = tvalid ? c : make_uint4(0, 0, 0, 0);
       d.s[qq] = tvalid ? sc : 0u;
     }
-    // x row m, pieces 4 (4 q + grp) + e of 16 bytes (8 BF16), q in this wave's quarter
+    // x row m, pieces 4 (4 q + grp) + e of 16 bytes (8 BF16), q in this wave's
+    // quarter; a lane past the last row reads row M - 1 (its D column, the
+    // only one its operand reaches, is not written), so no load is behind a
+    // branch
     uint4 xv[4][4];
-    const uint4* xrow = reinterpret_cast<const uint4*>(x + (valid ? m : 0) * K);
+    const uint4* xrow = reinterpret_cast<const uint4*>(x + (valid ? m : M - 1) * K);
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint4 v = xrow[4 * (4 * (4 * wave + qq) + grp) + e];
-        xv[qq][e] = valid ? v : make_uint4(0, 0, 0, 0);
-      }
+      for (int e = 0; e < 4; ++e) xv[qq][e] = xrow[4 * (4 * (4 * wave + qq) + grp) + e];
+    __builtin_amdgcn_sched_barrier(0);  // every load out before the first product
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       bf16x8 a[4];
