@@ -66,12 +66,26 @@ __global__ void __launch_bounds__(kQuantThreads) quant_amax_kernel(const uint16_
   const int64_t gi = blockIdx.y;
   const uint4* xm = reinterpret_cast<const uint4*>(x) + gi * chunks * 2;  // 16 BF16 per chunk
   uint32_t m = 0;
-  for (int64_t c = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; c < chunks;
-       c += (int64_t)gridDim.x * kQuantThreads) {
-    const uint4 a = load_stream(xm + 2 * c), b = load_stream(xm + 2 * c + 1);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  // four chunks a thread in flight (one at a time: 191.4 us for the
+  // [256][1024][2048] pass, four: 181.7 us, eight: 185.2 us); past the end a
+  // thread reads its first chunk of the step again (a repeat leaves the
+  // maximum unchanged)
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+  for (int64_t c0 = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; c0 < chunks;
+       c0 += 4 * stride) {
+    uint4 a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    for (int u = 0; u < 4; ++u) {
+      const int64_t c = c0 + u * stride < chunks ? c0 + u * stride : c0;
+      a[u] = load_stream(xm + 2 * c);
+      b[u] = load_stream(xm + 2 * c + 1);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t w[8] = {a[u].x, a[u].y, a[u].z, a[u].w, b[u].x, b[u].y, b[u].z, b[u].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    }
   }
   __shared__ uint32_t red[kQuantThreads / 64];
   m = wave_max_u32(m << 16);
