@@ -427,8 +427,8 @@ int32_t nvfp4_quantize(const uint16_t* x, int64_t G, int64_t N, int64_t K, uint8
   hipLaunchKernelGGL(quant_amax_kernel, dim3((unsigned)bx, (unsigned)G), dim3(kQuantThreads), 0,
                      stream, x, per, amax);
   hipLaunchKernelGGL(quant_blocks_kernel,
-                     dim3((unsigned)((total + kQuantThreads - 1) / kQuantThreads)),
-                     dim3(kQuantThreads), 0, stream, x, per, G, amax, codes, scales);
+                     dim3((unsigned)((per + kQuantThreads - 1) / kQuantThreads), (unsigned)G),
+                     dim3(kQuantThreads), 0, stream, x, per, amax, codes, scales);
   hipLaunchKernelGGL(quant_finish_kernel, dim3((unsigned)((G + kQuantThreads - 1) / kQuantThreads)),
                      dim3(kQuantThreads), 0, stream, g, G);
   return launched("nvfp4_quantize");

@@ -121,15 +121,14 @@ __device__ __forceinline__ uint32_t quotients_to_e2m1(uint32_t codes, uint32_t w
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, r0, r1, 1.0f, SEL);
 }
 
-// One 16-element block (row n, block b) of matrix g per thread.
+// One 16-element block i (of matrix gi) per thread.
 __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int64_t i,
-                                            int64_t blocks_per_matrix,
-                                            const uint32_t* __restrict__ amax,
+                                            int64_t gi, const uint32_t* __restrict__ amax,
                                             uint8_t* __restrict__ codes,
                                             uint8_t* __restrict__ scales) {
-  const float gv = quant_g(amax[i / blocks_per_matrix]);
   const uint4* xp = reinterpret_cast<const uint4*>(x) + 2 * i;
   const uint4 a = load_stream(xp), b = load_stream(xp + 1);
+  const float gv = quant_g(amax[gi]);
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t mb = 0;
 #pragma unroll
@@ -175,11 +174,16 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int6
   scales[i] = (uint8_t)sc;
 }
 
+// Grid (blocks of the matrix / kQuantThreads, G): the matrix is the
+// workgroup's row, so no thread divides its block index (a 64-bit division
+// ahead of every load: 254.6 -> 236.8 us for [256][1024][2048]).
 __global__ void __launch_bounds__(kQuantThreads) quant_blocks_kernel(
-    const uint16_t* __restrict__ x, int64_t blocks_per_matrix, int64_t G,
+    const uint16_t* __restrict__ x, int64_t blocks_per_matrix,
     const uint32_t* __restrict__ amax, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
-  if (i < blocks_per_matrix * G) quant_block(x, i, blocks_per_matrix, amax, codes, scales);
+  const int64_t il = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  const int64_t gi = blockIdx.y;
+  if (il < blocks_per_matrix)
+    quant_block(x, gi * blocks_per_matrix + il, gi, amax, codes, scales);
 }
 
 // g[i] = amax / 2688 (1 if 0), in place over the maxima.
