@@ -97,8 +97,9 @@ struct GemmLaunch {
   static int32_t run(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w, int64_t N,
                      uint16_t* y, hipStream_t s) {
     const int64_t blocks = row_blocks(N, K);  // one wave each
+    const float* gp = reinterpret_cast<const float*>(w + gscale_offset(1, N, K));
     hipLaunchKernelGGL(skinny_gemm_kernel<L>, dim3(grid_for(blocks, 4, 1 << 30)), dim3(256), 0,
-                       s, x, M, K, w, N, y);
+                       s, x, M, K, w, N, y, blocks, K / (L * 32), gp);
     return launched("nvfp4_skinny_gemm");
   }
 };

@@ -98,17 +98,20 @@ __device__ __forceinline__ void gemm_rows_panels(const uint8_t* __restrict__ blk
   gemm_write<L, R>(acc, m0, rows, lane, blk, N, g, y);
 }
 
-// L = Kp / 32 of the matrix's panel width; K = Q Kp.
+// L = Kp / 32 of the matrix's panel width; K = Q Kp. The host passes the
+// row-block count nrb, Q and the tensor scale's address: computed here, their
+// 64-bit divisions by runtime values came before the first load.
 template <int L>
 __global__ void __launch_bounds__(256) skinny_gemm_kernel(const uint16_t* __restrict__ x,
                                                           int64_t M, int64_t K,
                                                           const uint8_t* __restrict__ w,
-                                                          int64_t N, uint16_t* __restrict__ y) {
+                                                          int64_t N, uint16_t* __restrict__ y,
+                                                          int64_t nrb, int64_t Q,
+                                                          const float* __restrict__ gp) {
   const int lane = threadIdx.x & 63;
   const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // row block of W
-  if (blk >= row_blocks(N, K)) return;
-  const float g = reinterpret_cast<const float*>(w + gscale_offset(1, N, K))[0];
-  const int64_t Q = K / (L * 32);
+  if (blk >= nrb) return;
+  const float g = gp[0];
   if (Q > 1) {
     const uint8_t* tiles = w + blk * Q * kTileBytes;
     const int col0 = 32 * (lane % L);
