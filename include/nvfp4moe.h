@@ -270,8 +270,11 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* args, hipStream_t stream);
  * not used; everything else is as for moe_nvfp4_decode, the output
  * bit-identical to moe_route_topk + moe_nvfp4_decode with schedule 3.
  * Reading a weight tile per pair rather than per expert suits small M (up to
- * about 8); NVFP4MOE_ERR_UNSUPPORTED when H = 2048, I = 512 and M >=
- * dense_min_rows. The workspace holds the h rows only: (M*k (+M)) * I * 4
+ * about 8; without a shared expert and with routing spread evenly over the
+ * experts it stays ahead of grouping at least to M = 24, with skewed routing
+ * or a shared expert grouping wins from about M = 12); NVFP4MOE_ERR_UNSUPPORTED
+ * when H = 2048, I = 512 and M >= dense_min_rows (pass a larger value beyond
+ * M = 15: this path never uses the MFMA products). The workspace holds the h rows only: (M*k (+M)) * I * 4
  * bytes rounded up to 256 suffice (moe_nvfp4_workspace_bytes is more). */
 int32_t moe_nvfp4_route_decode(const moe_nvfp4_args* args, const float* logits, const float* bias,
                                hipStream_t stream);
