@@ -175,7 +175,9 @@ def test_moe_block_small(m, gpu, M, E, H, I, k, shared, resid, schedule):
     (5, 8, 512, 512, 8, True, False, False), (2, 32, 1024, 256, 2, False, True, False),
     (12, 64, 2048, 512, 8, True, False, True), (6, 4, 2048, 512, 1, True, True, False),
     # down tiles of more than 64 output rows (I = 128: 128, I = 96: 512)
-    (4, 16, 512, 128, 4, False, True, True), (3, 8, 2048, 96, 2, True, True, False)])
+    (4, 16, 512, 128, 4, False, True, True), (3, 8, 2048, 96, 2, True, True, False),
+    # beyond M = 15 with dense_min_rows above M
+    (16, 64, 2048, 512, 8, False, False, False), (24, 32, 2048, 512, 4, True, True, True)])
 def test_moe_route_decode_fused(m, gpu, M, E, H, I, k, shared, resid, bias):
     """Routing inside the gate_up launch: ids and w bit-identical to the oracle's
     routing, the output within tolerance of the oracle and bit-identical to
@@ -184,7 +186,7 @@ def test_moe_route_decode_fused(m, gpu, M, E, H, I, k, shared, resid, bias):
     residual = synth.normal_bf16(synth.key(5, 206, M), (M, H)) if resid else None
     d = upload_layer(lay, gpu, m)
     res = None if residual is None else to_dev_bf16(residual, gpu)
-    dmr = 13 if M == 12 else 0
+    dmr = M + 1 if M >= 12 else 0
     ws = m.moe_workspace(M, E, k, H, I, shared, gpu)
     call = lambda: m.moe_nvfp4_route_decode(d["x"], d["logits"], k, d["gu"], d["dn"], d["bias"],
                                             d["sgu"], d["sdn"], residual=res, workspace=ws,
