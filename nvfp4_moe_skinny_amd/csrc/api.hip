@@ -218,8 +218,12 @@ int32_t launch_route(const float* logits, const float* bias, int64_t M, int64_t 
                      w);
   const int32_t st = launched("moe_route_topk rows");
   if (st != NVFP4MOE_OK) return st;
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, ids, (int)M, (int)E, (int)k,
-                     counts, offsets, pairs, active, active_offsets, n_active);
+  if (M <= kGroupMaskRows)
+    hipLaunchKernelGGL(group_rows_kernel, dim3(1), dim3(1024), 0, stream, ids, (int)M, (int)E,
+                       (int)k, counts, offsets, pairs, active, active_offsets, n_active);
+  else
+    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, ids, (int)M, (int)E, (int)k,
+                       counts, offsets, pairs, active, active_offsets, n_active);
   return launched("moe_route_topk group");
 }
 

@@ -10,9 +10,10 @@
 // item select the top k of row m themselves (the same per-row routine as
 // moe_route_topk, so the same experts and weights bit for bit) while the row
 // of x is already on its way; wave 0 then streams gate tile j of expert
-// ids[m][jj], wave 1 the up tile, as in staged_gate_split_kernel. The items of tile 0 store ids and w
-// for the down launch. With few rows nearly every pair has its own expert, so
-// a tile per pair costs almost no extra bytes, and no grouping is needed.
+// ids[m][jj], wave 1 the up tile, as in staged_gate_split_kernel. The items
+// of tile 0 store ids and w for the down launch. With few rows nearly every
+// pair has its own expert, so a tile per pair costs almost no extra bytes, and
+// no grouping is needed.
 // SHARED (a shared expert present) is a template argument: without it the
 // routing is not behind a per-item branch, which measured faster (M = 4:
 // 15.44 -> 15.28 us per step; folding the shared rows into the slot-0 items

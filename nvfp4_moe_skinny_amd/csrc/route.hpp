@@ -268,14 +268,81 @@ __global__ void __launch_bounds__(1024) route_group_kernel(
 // rows spread over the compute units (M = 256: 64 units instead of 16, 206.6
 // -> 205.9 us per step; one or two rows a block measured the same).
 constexpr int kRowWaves = 4;
-__global__ void __launch_bounds__(kRowWaves * 64) route_rows_kernel(const float* __restrict__ logits,
-                                                          const float* __restrict__ bias, int M,
-                                                          int E, int k, int32_t* __restrict__ ids,
-                                                          float* __restrict__ w) {
+__global__ void __launch_bounds__(kRowWaves * 64)
+route_rows_kernel(const float* __restrict__ logits, const float* __restrict__ bias, int M, int E,
+                  int k, int32_t* __restrict__ ids, float* __restrict__ w) {
   __shared__ float lp[kRowWaves][kRouteMaxE];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowWaves + wave;
   if (row < M) route_row(logits, bias, E, k, row, lane, lp[wave], ids, w);
+}
+
+// Larger M, second launch, up to kGroupMaskRows rows: the row masks of
+// route_group_kernel with kGroupMaskRows / 64 words per expert, one block.
+// Every thread takes up to eight pairs: it sets their rows' bits (LDS atomic
+// OR), a thread per expert turns the words' popcounts into the number of
+// earlier rows before each word, wave 0 writes the runs, and every thread
+// places its pairs. The same pairs, bit for bit, as the ballot sort below.
+constexpr int kGroupMaskRows = 1024;
+constexpr int kGroupMaskWords = kGroupMaskRows / 64;
+__global__ void __launch_bounds__(1024) group_rows_kernel(const int32_t* __restrict__ ids,
+                                                          int M, int E, int k,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ pairs,
+                                                          int32_t* __restrict__ active,
+                                                          int32_t* __restrict__ active_offsets,
+                                                          int32_t* __restrict__ n_active) {
+  __shared__ unsigned long long rows_lds[kRouteMaxE][kGroupMaskWords];  // bit: row chose e
+  __shared__ int below_lds[kRouteMaxE][kGroupMaskWords];  // rows of e in the words before
+  __shared__ int run_lds[kRouteMaxE];
+  __shared__ int cnt_lds[kRouteMaxE];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int P = M * k, W = (M + 63) / 64;
+  int my_e[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {  // the ids first (one round trip)
+    const int q = (int)threadIdx.x + u * 1024;
+    my_e[u] = q < P ? ids[q] : -1;
+  }
+  for (int i = (int)threadIdx.x; i < kRouteMaxE * kGroupMaskWords; i += 1024)
+    (&rows_lds[0][0])[i] = 0ull;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (my_e[u] >= 0) {
+      const int row = ((int)threadIdx.x + u * 1024) / k;
+      atomicOr(&rows_lds[my_e[u]][row >> 6], 1ull << (row & 63));
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kRouteMaxE) {
+    const int e = (int)threadIdx.x;
+    int run = 0;
+    for (int wd = 0; wd < W; ++wd) {
+      below_lds[e][wd] = run;
+      run += __popcll(rows_lds[e][wd]);
+    }
+    cnt_lds[e] = run;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = cnt_lds[4 * lane + j];
+    write_runs(c, E, lane, run_lds, counts, offsets, active, active_offsets, n_active);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = my_e[u];
+    if (e >= 0) {
+      const int q = (int)threadIdx.x + u * 1024;
+      const int row = q / k, wd = row >> 6;
+      const int before = below_lds[e][wd] + __popcll(rows_lds[e][wd] & lanes_below(row & 63));
+      pairs[run_lds[e] + before] = q;
+    }
+  }
 }
 
 // Larger M, second launch: group all pairs in one block (P <= kGroupMaxPairs)

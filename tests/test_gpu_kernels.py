@@ -94,6 +94,7 @@ def test_skinny_gemm(m, gpu, M, K, N, g):
                                         (256, 256, 8, False), (1024, 256, 8, False),
                                         (3, 5, 2, False), (7, 64, 1, True), (20, 8, 8, False),
                                         (64, 8, 8, False),  # every row takes every expert
+                                        (2048, 64, 4, True), (8192, 256, 1, False),  # > 1024 rows
                                         (33, 3, 3, True),
                                         (5, 1, 1, True)])  # one expert: every row, w = 1
 def test_route_bit_exact(m, gpu, M, E, k, bias):
