@@ -570,6 +570,9 @@ int32_t moe_nvfp4_decode(const moe_nvfp4_args* a, hipStream_t stream) {
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "the projection rides on moe_nvfp4_route_decode only");
   const int64_t M = a->M, H = a->H, I = a->I;
   const bool specialised = H == 2048 && I == 512;
+  // the specialised kernels take 64 gate and 64 down row blocks as constants
+  if (specialised && (p.PG != 64 || p.PD != 64))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "internal: row blocks %d / %d", p.PG, p.PD);
   // per-row down + combine needs FP32 h for every pair: no slot (the shared
   // one has M rows) may take the MFMA gate_up path
   const bool valu_h = M < p.dense_min_rows || !specialised;
@@ -598,6 +601,9 @@ int32_t route_decode(const moe_nvfp4_args* a, const float* logits, const float* 
   if (st != NVFP4MOE_OK) return st;
   const int64_t M = a->M, H = a->H, I = a->I;
   const bool specialised = H == 2048 && I == 512;
+  // the specialised kernels take 64 gate and 64 down row blocks as constants
+  if (specialised && (p.PG != 64 || p.PD != 64))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "internal: row blocks %d / %d", p.PG, p.PD);
   if (specialised && M >= p.dense_min_rows)
     return fail(NVFP4MOE_ERR_UNSUPPORTED,
                 "moe_nvfp4_route_decode needs M < dense_min_rows (FP32 h for every pair)");

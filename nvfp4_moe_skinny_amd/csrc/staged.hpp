@@ -791,7 +791,8 @@ __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel
     return;
   }
   const int b = xcd_block((int)blockIdx.x - p.proj_blocks, (int)gridDim.x - p.proj_blocks);
-  const int m = b / p.PD, t = b % p.PD;
+  const int PD = LIC == 16 ? 64 : p.PD;  // H = 2048, I = 512: 2048 / 32 down row blocks
+  const int m = b / PD, t = b % PD;
   const int L = LIC ? LIC : p.LI;
   const int rpt = p.RI;  // output rows of a down tile
   // One wave per slot, up to eight slots. With the shared expert beside eight
