@@ -40,9 +40,11 @@ fused_route_gate_kernel(MoeParams p, const float* __restrict__ logits,
   __shared__ float lp[2][kRouteMaxE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = xcd_block((int)blockIdx.x, (int)gridDim.x);
-  // H = 2048, I = 512: 512 / 8 gate row blocks, a constant (with p.PG the
-  // division here measured 0.11 us more per M = 4 step)
-  const int PG = LHC == 64 ? 64 : p.PG;
+  // H = 2048, I = 512: 512 / 8 gate row blocks, a constant without a shared
+  // expert (with p.PG the division here measured 0.11 us more per M = 4 step;
+  // with a shared expert the constant measured slower: 40-layer stack 1177.8
+  // -> 1188.6 us)
+  const int PG = (LHC == 64 && !SHARED) ? 64 : p.PG;
   const int item = b / PG, j = b % PG;
   const int npairs = p.M * p.k;
   const int nq = SHARED ? p.k + 1 : p.k;  // row m's items: its k slots, then its shared row

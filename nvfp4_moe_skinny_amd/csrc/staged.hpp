@@ -791,7 +791,9 @@ __global__ void __launch_bounds__((kMaxTopK + 1) * 64) token_down_combine_kernel
     return;
   }
   const int b = xcd_block((int)blockIdx.x - p.proj_blocks, (int)gridDim.x - p.proj_blocks);
-  const int PD = LIC == 16 ? 64 : p.PD;  // H = 2048, I = 512: 2048 / 32 down row blocks
+  // H = 2048, I = 512: 2048 / 32 down row blocks, a constant as in the
+  // gate_up launch (and likewise not with the shared expert's eight waves)
+  const int PD = (LIC == 16 && !W0_SHARED) ? 64 : p.PD;
   const int m = b / PD, t = b % PD;
   const int L = LIC ? LIC : p.LI;
   const int rpt = p.RI;  // output rows of a down tile
