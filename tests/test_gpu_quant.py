@@ -41,7 +41,8 @@ def _bf16(v):
 
 @pytest.mark.parametrize("G,N,K,std", [(1, 4, 32, 1.0), (3, 17, 256, 1.0), (2, 64, 2048, 0.02),
                                        (4, 5, 48, 1000.0), (2, 33, 512, 1e-30),
-                                       (1, 512, 1024, 1.0)])
+                                       (1, 512, 1024, 1.0),
+                                       (700, 2, 64, 1.0)])  # many matrices: the grid's rows
 def test_quantize_bit_exact(m, gpu, G, N, K, std):
     x = synth.normal_bf16(synth.key(G, 120, N, K), (G, N, K), 0.0, std)
     # outliers, an all-zero block and negative zeros
