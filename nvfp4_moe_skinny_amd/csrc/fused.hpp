@@ -8,9 +8,9 @@
 // all of them (tiles its L2 already held) and ran idle for the last 5 of the
 // launch's 17 us (40-layer stack 1207.6 -> 1194.5 us). Both waves of a routed
 // item select the top k of row m themselves (the same per-row routine as
-// moe_route_topk, so the same experts and weights bit for bit) while the row
-// of x is already on its way; wave 0 then streams gate tile j of expert
-// ids[m][jj], wave 1 the up tile, as in staged_gate_split_kernel. The items
+// moe_route_topk, so the same experts and weights bit for bit), then request
+// row m of x; wave 0 streams gate tile j of expert ids[m][jj], wave 1 the up
+// tile, as in staged_gate_split_kernel. The items
 // of tile 0 store ids and w for the down launch. With few rows nearly every
 // pair has its own expert, so a tile per pair costs almost no extra bytes, and
 // no grouping is needed.
@@ -38,6 +38,7 @@ fused_route_gate_kernel(MoeParams p, const float* __restrict__ logits,
   constexpr int NV = LHC ? 1 : 8;  // reduced values a lane may hold
   __shared__ float up_lds[NV][64];
   __shared__ float lp[2][kRouteMaxE];
+  __shared__ uint4 xls[2][LHC ? 4 * LHC : 1];  // each wave's row of x (LHC != 0)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = xcd_block((int)blockIdx.x, (int)gridDim.x);
   // H = 2048, I = 512: 512 / 8 gate row blocks, a constant without a shared
@@ -53,10 +54,15 @@ fused_route_gate_kernel(MoeParams p, const float* __restrict__ logits,
   const int hrow = sh ? npairs + m : m * p.k + q;  // the pair's h row
   const int L = LHC ? LHC : p.LH;
   uint4 xr[1][4];
-  // the activation row goes out before the routing with a shared expert, after
-  // its wait without one (M = 4: 15.025 -> 14.967 us; the 40-layer stack took
-  // the late order 1179.6 -> 1190.8 us)
-  if constexpr (SHARED) load_x_bf16(p.x, p.H, m, 32 * (lane % L), xr[0]);
+  // Row m of x. At H = 2048 (LHC = 64) the wave requests the 4 KB row in
+  // coalesced 1 KB pieces once its routing is done and reads its lane's 64
+  // bytes back from its LDS row when the tile's loads are out (against direct
+  // loads, before the routing with a shared expert: 40-layer stack 1147.5 ->
+  // 1138.3 us; without one, after it: M = 4 unchanged). The generic instance
+  // loads the lane's columns directly: before the routing with a shared
+  // expert, after its wait without one (with direct loads at H = 2048: M = 4
+  // 15.025 -> 14.967 us late; the 40-layer stack 1179.6 -> 1190.8 us late).
+  if constexpr (SHARED && LHC == 0) load_x_bf16(p.x, p.H, m, 32 * (lane % L), xr[0]);
   int e = 0;
   if (!sh) {
     int my_id;
@@ -81,7 +87,11 @@ fused_route_gate_kernel(MoeParams p, const float* __restrict__ logits,
       w[hrow] = my_w;
     }
   }
-  if constexpr (!SHARED) load_x_bf16(p.x, p.H, m, 32 * (lane % L), xr[0]);
+  uint4 xv[LHC ? LHC / 16 : 1];
+  if constexpr (LHC != 0)
+    load_coalesced(reinterpret_cast<const uint4*>(p.x + (int64_t)m * p.H), lane, xv);
+  else if constexpr (!SHARED)
+    load_x_bf16(p.x, p.H, m, 32 * (lane % L), xr[0]);
   const uint8_t* mat = sh ? p.sgu : p.gu + (int64_t)e * p.gu_mat_bytes;
   const float g = sh ? p.sgu_g[0] : p.gu_g[e];
   const int rb = wave == 0 ? j : j + PG;  // gate row block j, or the matching up one
@@ -89,6 +99,7 @@ fused_route_gate_kernel(MoeParams p, const float* __restrict__ logits,
   if (LHC != 0 || p.QH == 1) {
     TileRegs T;
     load_tile(mat + (int64_t)rb * kTileBytes, lane, T);
+    if constexpr (LHC != 0) restage_row(xls[wave], lane, lane % LHC, xv, xr[0]);
     float part[1][8];
     tile_dot_bf16<1>(T, xr, part);
 #pragma unroll

@@ -142,4 +142,29 @@ __device__ __forceinline__ void load_h_f32(const float* h, int64_t ld, int64_t r
   }
 }
 
+// A whole activation row through LDS. Loaded directly, neighbouring lanes'
+// 32 columns lie 64 B (BF16) or 128 B (FP32) apart, so each 16-byte load of a
+// wave touches 32 (BF16 row of 64 chunks) or 16 (FP32 row of 16 chunks)
+// cache lines; requested as coalesced 1 KB pieces (8 lines each), written to
+// the wave's own LDS row and read back by columns, the row costs a quarter or
+// half of the line requests. load_coalesced: v[i] = src[64 i + lane].
+template <int N>
+__device__ __forceinline__ void load_coalesced(const uint4* src, int lane, uint4 (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = src[i * 64 + lane];
+}
+
+// Writes the N pieces to the wave's LDS row, then reads back the W 16-byte
+// words of chunk c (W = 4: 32 BF16 columns; W = 8: 32 FP32 columns). Only the
+// calling wave touches `lds`.
+template <int N, int W>
+__device__ __forceinline__ void restage_row(uint4* lds, int lane, int c, const uint4 (&v)[N],
+                                            uint4 (&out)[W]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) lds[i * 64 + lane] = v[i];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < W; ++i) out[i] = lds[W * c + i];
+}
+
 }  // namespace nvfp4moe
