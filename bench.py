@@ -84,9 +84,9 @@ def tol_ratio(got, ref):
 
 def host_info():
     """The machine the line was measured on: GPU, its compute units, the HIP
-    runtime and compiler, and the host CPU the oracle baseline ran on."""
-    import subprocess
-
+    runtime, the compiler the library was built with (recorded by the build:
+    no child process is started here, so none runs under a profiler's
+    preloaded library) and the host CPU the oracle baseline ran on."""
     import torch
     props = torch.cuda.get_device_properties(0)
     info = {"gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
@@ -99,10 +99,9 @@ def host_info():
     except OSError:
         pass
     try:
-        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
-                             timeout=60).stdout.splitlines()
-        info["hipcc"] = "; ".join(l.strip() for l in out if "version" in l.lower())[:200]
-    except (OSError, subprocess.SubprocessError):
+        with open(os.path.join(ROOT, "nvfp4_moe_skinny_amd", "libnvfp4moe.compiler.txt")) as fh:
+            info["hipcc"] = fh.read().strip()[:200]
+    except OSError:
         pass
     info.update(cpu_info())
     return info

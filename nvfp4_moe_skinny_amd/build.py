@@ -6,6 +6,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4moe.so")
+# the compiler's version lines, recorded beside the library at build time (a
+# measurement reads them from here rather than running the compiler itself)
+COMPILER_INFO = os.path.join(HERE, "libnvfp4moe.compiler.txt")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -25,6 +28,9 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
     os.replace(LIB + ".tmp", LIB)
+    v = subprocess.run([hipcc, "--version"], capture_output=True, text=True)
+    with open(COMPILER_INFO, "w") as fh:
+        fh.write("; ".join(l.strip() for l in v.stdout.splitlines() if "version" in l.lower()))
     return LIB
 
 
