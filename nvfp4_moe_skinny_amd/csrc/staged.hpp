@@ -696,11 +696,14 @@ __global__ void __launch_bounds__(64, RMAX == 1 ? 3 : 2) staged_down_kernel(MoeP
 
 constexpr int kMaxTopK = 8;  // the library's bound on k (checked on the host)
 
-// One thread per output (m, n): routed slots in j order, then shared, then
+// One thread per output (m, n) (blocks of TPB threads, a compile-time
+// constant: blockDim.x would be read from the dispatch packet before the first
+// address): routed slots in j order, then shared, then
 // residual. Every term's loads are issued before the first add (the loop over
 // k is unrolled to its maximum), so a thread waits one round trip, not k.
-__global__ void __launch_bounds__(256) staged_combine_kernel(MoeParams p) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+template <int TPB>
+__global__ void __launch_bounds__(TPB) staged_combine_kernel(MoeParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * TPB + threadIdx.x;
   if (idx >= (int64_t)p.M * p.H) return;
   const int m = (int)(idx / p.H), n = (int)(idx % p.H);
   float yv[kMaxTopK], wv[kMaxTopK];
