@@ -145,9 +145,10 @@ __device__ __forceinline__ void load_h_f32(const float* h, int64_t ld, int64_t r
 // A whole activation row through LDS. Loaded directly, neighbouring lanes'
 // 32 columns lie 64 B (BF16) or 128 B (FP32) apart, so each 16-byte load of a
 // wave touches 32 (BF16 row of 64 chunks) or 16 (FP32 row of 16 chunks)
-// cache lines; requested as coalesced 1 KB pieces (8 lines each), written to
-// the wave's own LDS row and read back by columns, the row costs a quarter or
-// half of the line requests. load_coalesced: v[i] = src[64 i + lane].
+// cache lines: 128 line requests for the row either way (4 or 8 loads).
+// Requested as coalesced 1 KB pieces (8 lines each), written to the wave's own
+// LDS row and read back by columns, it takes 32 (4 KB BF16 row) or 16 (2 KB
+// FP32 row). load_coalesced: v[i] = src[64 i + lane].
 template <int N>
 __device__ __forceinline__ void load_coalesced(const uint4* src, int lane, uint4 (&v)[N]) {
 #pragma unroll
