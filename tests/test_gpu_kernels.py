@@ -175,6 +175,9 @@ def test_moe_block_small(m, gpu, M, E, H, I, k, shared, resid, schedule):
     (8, 256, 2048, 512, 8, True, True, True), (3, 16, 256, 256, 4, True, False, False),
     (5, 8, 512, 512, 8, True, False, False), (2, 32, 1024, 256, 2, False, True, False),
     (12, 64, 2048, 512, 8, True, False, True), (6, 4, 2048, 512, 1, True, True, False),
+    # three routed slots without a shared expert at H = 2048, I = 512: three-wave
+    # down blocks, each wave restaging its own x and h rows through LDS
+    (5, 64, 2048, 512, 3, False, True, True),
     # down tiles of more than 64 output rows (I = 128: 128, I = 96: 512)
     (4, 16, 512, 128, 4, False, True, True), (3, 8, 2048, 96, 2, True, True, False),
     # beyond M = 15 with dense_min_rows above M
