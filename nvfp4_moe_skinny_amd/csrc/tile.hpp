@@ -163,7 +163,7 @@ __device__ __forceinline__ void restage_row(uint4* lds, int lane, int c, const u
                                             uint4 (&out)[W]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) lds[i * 64 + lane] = v[i];
-  // other lanes' writes before this lane's reads: without the fences the
+  // other lanes' writes before this lane's reads: with no barrier here the
   // compiler may hoist a read above a write it proves is not this lane's own
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
