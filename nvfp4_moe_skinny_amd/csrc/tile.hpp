@@ -29,9 +29,10 @@ __device__ __forceinline__ void load_tile(const uint8_t* tile, int lane, TileReg
 // The same with the scale word requested first, so that slab i can be
 // multiplied once the loads up to it have landed (every slab needs its scale
 // bytes). Measured faster in the skinny GEMM's single-panel kernel (M = 1,
-// 2048 -> 512: 3.975 -> 3.915 us); in the MoE kernels, where the compiler
-// places the loads itself, it measured slower (M = 4 15.12 -> 15.22 us,
-// 40-layer stack 1178 -> 1184 us).
+// 2048 -> 512: 3.975 -> 3.915 us) and in the M = 4 gate_up kernel once its
+// activation row came in coalesced pieces ahead of the tile (14.705 -> 14.688
+// us); elsewhere in the MoE kernels it measured slower (40-layer stack 1178 ->
+// 1184 us).
 __device__ __forceinline__ void load_tile_scales_first(const uint8_t* tile, int lane,
                                                        TileRegs& t) {
   const uint4* c = reinterpret_cast<const uint4*>(tile);
